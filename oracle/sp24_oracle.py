@@ -1,0 +1,235 @@
+"""CPU oracle for the transposable 2:4 FFN path.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this module.  The HIP library never calls it, and it shares no
+code, table or helper with the HIP path: the pattern list below is enumerated
+here from its definition, independently of the GPU side's own table.
+
+Source: "Accelerating Transformer Pre-training with 2:4 Sparsity" (Hu, Zhao,
+Huang, Chen, Zhu; ICML 2024).  Cited as [HZ24 Alg.1] for Algorithm 1
+(transposable mask search) on the reproducibility page, [HZ24 abstract] for
+the abstract, and [HZ24 SW] for the page's "Software Dependencies" row, which
+names the CUTLASS 2:4 sparse matrix multiplications and the Triton mask-search
+and pruning kernels.
+
+What the method computes, and the readings taken where the pages are silent:
+
+1. Mask search [HZ24 Alg.1]: take |W|, correlate it with every mask pattern
+   m using a 4x4 window at stride 4 and no padding, and return the argmax over
+   patterns for each 4x4 block.
+   * The pattern set m is every 4x4 0/1 matrix with exactly two ones in each
+     row and each column.  These are the transposable 2:4 masks [HZ24
+     abstract]: the block keeps 2 of 4 along rows and along columns.  There
+     are 90 of them.
+   * Pattern order (silent on the pages): each row keeps one of six column
+     pairs, coded 0:{0,1} 1:{0,2} 2:{0,3} 3:{1,2} 4:{1,3} 5:{2,3}.  A pattern
+     is a tuple (a, b, c, d) of codes for rows 0..3.  The list is every valid
+     tuple in lexicographic order, a slowest.
+   * "argmax(out, dim=2)" is read as the argmax over the pattern axis.
+   * Score precision and order (silent): fp32, the kept magnitudes added one
+     at a time in row-major order, starting from +0.
+   * Tie-break (silent): the first maximum in pattern order (strict >).
+   * R and C must be multiples of 4.  The stride-4 correlation without padding
+     would drop a remainder, so the oracle refuses it instead.
+2. Pruning and compression [HZ24 SW] (the format is not on the pages):
+   * Row form: for row i and group g (columns 4g..4g+3) with kept in-group
+     positions i0 < i1, ``vals_row[i, 2g:2g+2] = W[i, 4g+i0], W[i, 4g+i1]``
+     (bit copies).  The nibble ``i0 | i1 << 2`` goes to bits 4*(g % 4) of the
+     uint16 ``meta_row[i, g // 4]``.
+   * Column form: the same applied to W transposed, so column j, group h (rows
+     4h..4h+3) fills ``vals_col[j, 2h:2h+2]`` and ``meta_col[j, h // 4]``.
+     Transposability [HZ24 abstract] makes every column group keep exactly 2.
+   * Compression needs R and C to be multiples of 16, since a meta word holds
+     four groups.
+3. Sparse GEMMs [HZ24 abstract, SW]: ``Y = X Ws^T`` (forward) and
+   ``dX = dY Ws`` (input gradient), with Ws the pruned weight.  The plain
+   definition is the dense product with the decoded pruned matrix, computed
+   here in float64.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+# Column pairs a row may keep, coded 0..5 in lexicographic order.
+ROW_PAIRS = ((0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3))
+
+
+def pattern_codes() -> list:
+    """The transposable patterns as row-pair code tuples, in index order.
+
+    Enumerates (a, b, c, d) over {0..5}^4 in lexicographic order and keeps a
+    tuple when every column of the resulting 4x4 mask holds exactly two ones.
+    """
+    out = []
+    for codes in itertools.product(range(6), repeat=4):
+        colcount = [0, 0, 0, 0]
+        for code in codes:
+            for c in ROW_PAIRS[code]:
+                colcount[c] += 1
+        if colcount == [2, 2, 2, 2]:
+            out.append(codes)
+    return out
+
+
+def pattern_masks() -> np.ndarray:
+    """uint8 [90, 4, 4]: mask p has a one at (r, c) when pattern p keeps it."""
+    codes = pattern_codes()
+    m = np.zeros((len(codes), 4, 4), dtype=np.uint8)
+    for p, tup in enumerate(codes):
+        for r, code in enumerate(tup):
+            for c in ROW_PAIRS[code]:
+                m[p, r, c] = 1
+    return m
+
+
+def _check_shape(W: np.ndarray, mult: int) -> tuple:
+    if W.ndim != 2:
+        raise ValueError("W must be 2-D")
+    R, C = W.shape
+    if R <= 0 or C <= 0 or R % mult or C % mult:
+        raise ValueError(f"W shape {W.shape} must be positive multiples of {mult}")
+    return R, C
+
+
+def _blocks(W: np.ndarray) -> np.ndarray:
+    """[R/4, C/4, 4, 4] view of a [R, C] array, block (bi, bj) at [bi, bj]."""
+    R, C = W.shape
+    return W.reshape(R // 4, 4, C // 4, 4).transpose(0, 2, 1, 3)
+
+
+def block_scores(W: np.ndarray) -> np.ndarray:
+    """float32 [R/4, C/4, 90]: the correlation ``out`` of [HZ24 Alg.1].
+
+    Step 1 takes |W| (fp16 -> fp32 is exact; the sign bit is cleared, so -0
+    becomes +0).  Step 2 scores block (bi, bj) against pattern p by adding the
+    kept magnitudes one at a time, in row-major order, in fp32.
+    """
+    W = np.asarray(W)
+    if W.dtype != np.float16:
+        raise TypeError("W must be float16")
+    _check_shape(W, 4)
+    A = _blocks(np.abs(W).astype(np.float32))
+    masks = pattern_masks()
+    out = np.empty(A.shape[:2] + (len(masks),), dtype=np.float32)
+    for p, m in enumerate(masks):
+        s = np.zeros(A.shape[:2], dtype=np.float32)
+        for r in range(4):
+            for c in range(4):
+                if m[r, c]:
+                    s = s + A[:, :, r, c]       # one fp32 add, round to nearest even
+        out[:, :, p] = s
+    return out
+
+
+def mask_search(W: np.ndarray) -> np.ndarray:
+    """uint8 [R/4, C/4] pattern index per 4x4 block [HZ24 Alg.1, step 3].
+
+    The argmax keeps the first maximum in pattern order: a later pattern
+    replaces the running best only when its score is strictly greater.
+    """
+    S = block_scores(W)
+    best = np.zeros(S.shape[:2], dtype=np.uint8)
+    best_s = S[:, :, 0].copy()
+    for p in range(1, S.shape[2]):
+        better = S[:, :, p] > best_s
+        best = np.where(better, np.uint8(p), best)
+        best_s = np.where(better, S[:, :, p], best_s)
+    return best
+
+
+def idx_to_mask(idx: np.ndarray) -> np.ndarray:
+    """bool [R, C] mask of kept entries from the per-block pattern indices."""
+    masks = pattern_masks().astype(bool)
+    nbr, nbc = idx.shape
+    return masks[idx].transpose(0, 2, 1, 3).reshape(4 * nbr, 4 * nbc)
+
+
+def _compress_groups(W: np.ndarray, M: np.ndarray):
+    """Compress along axis 1 in groups of 4: returns (vals [n, m/2], meta [n, m/16])."""
+    n, m = W.shape
+    G = m // 4
+    Wg = W.reshape(n, G, 4)
+    Mg = M.reshape(n, G, 4)
+    if not (Mg.sum(axis=2) == 2).all():
+        raise ValueError("every group of 4 must keep exactly 2")
+    i0 = np.argmax(Mg, axis=2)                   # first kept position
+    i1 = 3 - np.argmax(Mg[:, :, ::-1], axis=2)   # last kept position
+    v0 = np.take_along_axis(Wg, i0[:, :, None], axis=2)[:, :, 0]
+    v1 = np.take_along_axis(Wg, i1[:, :, None], axis=2)[:, :, 0]
+    vals = np.stack([v0, v1], axis=2).reshape(n, m // 2)
+    nib = (i0 | (i1 << 2)).astype(np.uint16).reshape(n, G // 4, 4)
+    meta = nib[:, :, 0] | (nib[:, :, 1] << 4) | (nib[:, :, 2] << 8) | (nib[:, :, 3] << 12)
+    return vals, meta.astype(np.uint16)
+
+
+def compress(W: np.ndarray, idx: np.ndarray) -> dict:
+    """Prune W with the searched masks and store both 2:4 forms.
+
+    Returns ``vals_row`` fp16 [R, C/2], ``meta_row`` uint16 [R, C/16],
+    ``vals_col`` fp16 [C, R/2] and ``meta_col`` uint16 [C, R/16].
+    """
+    W = np.asarray(W)
+    if W.dtype != np.float16:
+        raise TypeError("W must be float16")
+    R, C = _check_shape(W, 16)
+    if idx.shape != (R // 4, C // 4):
+        raise ValueError("idx shape does not match W")
+    if (idx >= 90).any():
+        raise ValueError("pattern index out of range")
+    M = idx_to_mask(idx)
+    vals_row, meta_row = _compress_groups(W, M)
+    vals_col, meta_col = _compress_groups(np.ascontiguousarray(W.T), np.ascontiguousarray(M.T))
+    return {"vals_row": vals_row, "meta_row": meta_row,
+            "vals_col": vals_col, "meta_col": meta_col}
+
+
+def _decode_groups(vals: np.ndarray, meta: np.ndarray, n: int, m: int) -> np.ndarray:
+    """Inverse of ``_compress_groups``: fp16 [n, m], +0 where nothing is kept."""
+    out = np.zeros((n, m // 4, 4), dtype=np.float16)
+    v = vals.reshape(n, m // 4, 2)
+    for g in range(m // 4):
+        nib = (meta[:, g // 4].astype(np.int64) >> (4 * (g % 4))) & 0xF
+        i0, i1 = nib & 3, nib >> 2
+        rows = np.arange(n)
+        out[rows, g, i0] = v[:, g, 0]
+        out[rows, g, i1] = v[:, g, 1]
+    return out.reshape(n, m)
+
+
+def decode_row_form(vals_row, meta_row, R: int, C: int) -> np.ndarray:
+    """Dense fp16 [R, C] pruned weight from the row form."""
+    return _decode_groups(vals_row, meta_row, R, C)
+
+
+def decode_col_form(vals_col, meta_col, R: int, C: int) -> np.ndarray:
+    """Dense fp16 [R, C] pruned weight from the column form."""
+    return _decode_groups(vals_col, meta_col, C, R).T
+
+
+def spmm_fwd(X: np.ndarray, vals_row, meta_row, R: int, C: int) -> np.ndarray:
+    """float64 [T, R]: Y = X Ws^T with Ws decoded from the row form."""
+    Ws = decode_row_form(vals_row, meta_row, R, C).astype(np.float64)
+    return np.asarray(X, dtype=np.float64) @ Ws.T
+
+
+def spmm_bwd_input(dY: np.ndarray, vals_col, meta_col, R: int, C: int) -> np.ndarray:
+    """float64 [T, C]: dX = dY Ws with Ws decoded from the column form."""
+    Ws = decode_col_form(vals_col, meta_col, R, C).astype(np.float64)
+    return np.asarray(dY, dtype=np.float64) @ Ws
+
+
+def gemm_errors(out: np.ndarray, ref: np.ndarray) -> tuple:
+    """(normwise max relative error, mean absolute error) of ``out`` vs ``ref``.
+
+    The relative error is max|out - ref| / max|ref|: an elementwise relative
+    error is unbounded where ref is near zero, for any finite-precision result.
+    """
+    o = np.asarray(out, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    diff = np.abs(o - r)
+    denom = np.abs(r).max() if r.size else 0.0
+    max_rel = float(diff.max() / denom) if r.size and denom > 0 else float(diff.max() if r.size else 0.0)
+    mean_abs = float(diff.mean()) if r.size else 0.0
+    return max_rel, mean_abs

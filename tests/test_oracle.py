@@ -1,0 +1,346 @@
+"""Pins for the CPU oracle, checked against mathematics rather than itself.
+
+Every test here runs on the CPU.  The oracle is pinned by:
+* brute-force enumeration of all 2^16 4x4 0/1 masks (the pattern set and its
+  known size, 90);
+* exact rational scoring (``fractions.Fraction``) of random blocks whose
+  sums are exact in fp32, compared with the oracle including the tie-break;
+* hand-worked blocks in ``tests/golden/handworked_blocks.txt``;
+* metamorphic properties (sign flips, power-of-two scaling, transposition,
+  separable blocks, planted patterns);
+* the literal form of Algorithm 1 ("Accelerating Transformer Pre-training
+  with 2:4 Sparsity"): a float64 ``conv2d`` with stride 4 and an ``argmax``
+  over the pattern axis, run with PyTorch's CPU library ops;
+* for the GEMMs, an explicit float64 loop over the compressed storage and
+  identity-matrix special cases.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import sp24_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "handworked_blocks.txt")
+
+
+# ----------------------------------------------------------------------------
+# brute-force reference for the pattern set (independent of the oracle's
+# row-pair enumeration): every 16-bit mask, bit 4r+c for entry (r, c)
+def _brute_patterns():
+    pats = []
+    for bits in range(1 << 16):
+        m = np.array([(bits >> k) & 1 for k in range(16)], dtype=np.uint8).reshape(4, 4)
+        if (m.sum(axis=0) == 2).all() and (m.sum(axis=1) == 2).all():
+            pats.append(m)
+    return pats
+
+
+def _msb_first_key(m):
+    """The 16-bit string of m read row by row, leftmost column first."""
+    return int("".join(str(int(v)) for v in m.reshape(-1)), 2)
+
+
+BRUTE = _brute_patterns()
+# Pattern order pin: lexicographic over row-pair codes equals descending order
+# of the row-major, leftmost-first bit string (code 0 = 1100 is the largest
+# row string, code 5 = 0011 the smallest).
+BRUTE_ORDERED = sorted(BRUTE, key=_msb_first_key, reverse=True)
+
+
+def test_pattern_count_is_90():
+    # The number of 4x4 0/1 matrices with all row and column sums 2 is 90.
+    assert len(BRUTE) == 90
+    assert len(O.pattern_codes()) == 90
+
+
+def test_pattern_set_and_order_match_brute_force():
+    masks = O.pattern_masks()
+    assert masks.shape == (90, 4, 4)
+    for p in range(90):
+        assert (masks[p] == BRUTE_ORDERED[p]).all(), p
+    # first and last patterns written out by hand
+    assert masks[0].tolist() == [[1, 1, 0, 0], [1, 1, 0, 0], [0, 0, 1, 1], [0, 0, 1, 1]]
+    assert masks[89].tolist() == [[0, 0, 1, 1], [0, 0, 1, 1], [1, 1, 0, 0], [1, 1, 0, 0]]
+    assert masks[23].tolist() == [[1, 0, 1, 0], [0, 1, 0, 1], [1, 0, 1, 0], [0, 1, 0, 1]]
+
+
+def test_pattern_set_closed_under_transpose():
+    keys = {m.tobytes() for m in O.pattern_masks()}
+    for m in O.pattern_masks():
+        assert np.ascontiguousarray(m.T).tobytes() in keys
+
+
+# ----------------------------------------------------------------------------
+# exact rational brute force of the mask search on one block
+def _brute_block(block16):
+    """(index, exact score) of the first maximum over BRUTE_ORDERED."""
+    a = [Fraction(float(abs(v))) for v in np.asarray(block16, dtype=np.float16).reshape(-1)]
+    best, best_s = None, None
+    for p, m in enumerate(BRUTE_ORDERED):
+        s = sum((a[k] for k in range(16) if m.reshape(-1)[k]), Fraction(0))
+        if best is None or s > best_s:
+            best, best_s = p, s
+    return best, best_s
+
+
+def _exact_regime(block16):
+    """True when every partial sum of up to 8 entries is exact in fp32."""
+    a = [Fraction(float(abs(v))) for v in np.asarray(block16, dtype=np.float16).reshape(-1)]
+    nz = [x for x in a if x != 0]
+    if not nz:
+        return True
+    # q = the finest power of two all entries are integer multiples of
+    q = Fraction(1, 1 << 24)
+    while all((x / (q * 2)).denominator == 1 for x in nz) and q < 2**20:
+        q *= 2
+    return 8 * max(a) < q * 2**24
+
+
+def _random_blocks(rng, n, kind):
+    if kind == "normal":
+        b = (rng.standard_normal((n, 16)) * 0.02).astype(np.float16)
+    elif kind == "ints":
+        b = (rng.integers(-3, 4, size=(n, 16)) / 8).astype(np.float16)
+    elif kind == "small-ints":
+        b = rng.integers(-2, 3, size=(n, 16)).astype(np.float16)
+    else:
+        raise ValueError(kind)
+    return b
+
+
+@pytest.mark.parametrize("kind", ["normal", "ints", "small-ints"])
+def test_mask_search_matches_exact_brute_force(kind):
+    rng = np.random.default_rng([7, len(kind)])
+    blocks = _random_blocks(rng, 300, kind)
+    # lay the blocks out as a [4, 4*n] matrix: block j at columns 4j..4j+3
+    W = blocks.reshape(-1, 4, 4).transpose(1, 0, 2).reshape(4, -1)
+    idx = O.mask_search(W)[0]
+    scores = O.block_scores(W)[0]
+    for j, b in enumerate(blocks):
+        assert _exact_regime(b)
+        p, s = _brute_block(b)
+        assert idx[j] == p, (j, b.reshape(4, 4))
+        assert Fraction(float(scores[j, p])) == s
+
+
+def _load_golden():
+    rows = []
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, vals, idx, score, _note = [t.strip() for t in line.split("|")]
+            v = [float.fromhex(t) if "0x" in t else float(t) for t in vals.split()]
+            rows.append((name, np.array(v, dtype=np.float16).reshape(4, 4), int(idx), float(score)))
+    return rows
+
+
+GOLDEN_ROWS = _load_golden()
+
+
+@pytest.mark.parametrize("name,block,idx,score", GOLDEN_ROWS, ids=[r[0] for r in GOLDEN_ROWS])
+def test_handworked_blocks(name, block, idx, score):
+    assert O.mask_search(block)[0, 0] == idx
+    assert float(O.block_scores(block)[0, 0, idx]) == score
+    if _exact_regime(block):
+        assert _brute_block(block)[0] == idx
+
+
+def test_b7_b8_outside_exact_regime():
+    g = {r[0]: r for r in GOLDEN_ROWS}
+    b7, b8 = g["B7"][1], g["B8"][1]
+    assert not _exact_regime(b7) and not _exact_regime(b8)
+    # B7: the exact scores of 63 and 65 tie, so exact arithmetic also gives 63
+    assert _brute_block(b7)[0] == 63
+    # B8: exact arithmetic picks 24, fp32 in row-major order picks 11
+    assert _brute_block(b8)[0] == 24
+    assert O.mask_search(b8)[0, 0] == 11
+    # B9: exact arithmetic picks 60, row-major fp32 picks 30
+    b9 = g["B9"][1]
+    assert not _exact_regime(b9)
+    assert _brute_block(b9)[0] == 60
+    assert O.mask_search(b9)[0, 0] == 30
+
+
+# ----------------------------------------------------------------------------
+# invariants and metamorphic properties on whole matrices
+def _w(seed, R, C, kind="normal"):
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        return (rng.standard_normal((R, C)) * 0.02).astype(np.float16)
+    return (rng.integers(-3, 4, size=(R, C)) / 8).astype(np.float16)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ints"])
+def test_mask_invariants(kind):
+    W = _w(11, 64, 96, kind)
+    idx = O.mask_search(W)
+    assert idx.shape == (16, 24) and idx.dtype == np.uint8 and (idx < 90).all()
+    M = O.idx_to_mask(idx)
+    blocks = M.reshape(16, 4, 24, 4)
+    assert (blocks.sum(axis=3) == 2).all()   # each block row keeps 2
+    assert (blocks.sum(axis=1) == 2).all()   # each block column keeps 2
+
+
+def test_sign_flips_do_not_change_mask():
+    W = _w(12, 32, 32, "ints")
+    rng = np.random.default_rng(5)
+    sign = np.where(rng.random(W.shape) < 0.5, -1, 1).astype(np.float16)
+    assert (O.mask_search(W) == O.mask_search(W * sign)).all()
+
+
+@pytest.mark.parametrize("k", [-6, -1, 1, 5])
+def test_power_of_two_scaling_does_not_change_mask(k):
+    W = _w(13, 32, 64, "ints")
+    W2 = (W.astype(np.float32) * np.float32(2.0 ** k)).astype(np.float16)
+    assert (W2.astype(np.float32) == W.astype(np.float32) * 2.0 ** k).all()
+    assert (O.mask_search(W) == O.mask_search(W2)).all()
+
+
+def test_transpose_keeps_best_score():
+    W = _w(14, 32, 32, "normal")
+    s = O.block_scores(W).max(axis=2)
+    st = O.block_scores(np.ascontiguousarray(W.T)).max(axis=2)
+    assert (s == st.T).all()
+
+
+def test_separable_blocks_tie_to_index_0():
+    rng = np.random.default_rng(15)
+    for _ in range(20):
+        r = rng.integers(0, 8, size=(4, 1))
+        c = rng.integers(0, 8, size=(1, 4))
+        b = (r + c).astype(np.float16)
+        assert O.mask_search(b)[0, 0] == 0
+
+
+def test_planted_pattern_wins():
+    masks = O.pattern_masks()
+    for p in range(90):
+        b = np.where(masks[p] == 1, 1.0, 0.25).astype(np.float16)
+        assert O.mask_search(b)[0, 0] == p
+
+
+def test_shape_rules():
+    with pytest.raises(ValueError):
+        O.mask_search(np.zeros((6, 8), np.float16))
+    with pytest.raises(ValueError):
+        O.compress(np.zeros((8, 8), np.float16), np.zeros((2, 2), np.uint8))
+    with pytest.raises(TypeError):
+        O.mask_search(np.zeros((8, 8), np.float32))
+
+
+# ----------------------------------------------------------------------------
+# the literal Algorithm 1: conv2d with stride 4 and argmax over patterns
+def test_literal_conv2d_argmax_formulation():
+    torch = pytest.importorskip("torch")
+    W = np.concatenate([_w(16, 32, 64, "normal"), _w(17, 32, 64, "ints")], axis=0)
+    Wabs = torch.from_numpy(np.abs(W).astype(np.float64))[None, None]     # step 1
+    m = torch.from_numpy(O.pattern_masks().astype(np.float64))[:, None]    # [90, 1, 4, 4]
+    out = torch.nn.functional.conv2d(Wabs, m, stride=4, padding=0)         # step 2: [1, 90, R/4, C/4]
+    out = out[0].permute(1, 2, 0)                                          # [R/4, C/4, 90]
+    index = torch.argmax(out, dim=2).numpy()                               # step 3: first maximum
+    assert (index == O.mask_search(W)).all()
+    # in this (exact) regime the fp32 row-major scores equal the float64 conv
+    assert (O.block_scores(W).astype(np.float64) == out.numpy()).all()
+
+
+# ----------------------------------------------------------------------------
+# compression
+def _decode_loop(vals, meta, n, m):
+    """Explicit per-entry decode of one compressed form (rows of length m)."""
+    out = np.zeros((n, m), dtype=np.float16)
+    for i in range(n):
+        for g in range(m // 4):
+            nib = (int(meta[i, g // 4]) >> (4 * (g % 4))) & 0xF
+            out[i, 4 * g + (nib & 3)] = vals[i, 2 * g]
+            out[i, 4 * g + (nib >> 2)] = vals[i, 2 * g + 1]
+    return out
+
+
+@pytest.mark.parametrize("kind", ["normal", "ints"])
+def test_compress_roundtrip(kind):
+    W = _w(18, 48, 32, kind)
+    W[0, 0] = np.float16(-0.0)
+    idx = O.mask_search(W)
+    c = O.compress(W, idx)
+    R, C = W.shape
+    assert c["vals_row"].shape == (R, C // 2) and c["meta_row"].shape == (R, C // 16)
+    assert c["vals_col"].shape == (C, R // 2) and c["meta_col"].shape == (C, R // 16)
+    M = O.idx_to_mask(idx)
+    pruned = np.where(M, W, np.float16(0))
+    d_row = O.decode_row_form(c["vals_row"], c["meta_row"], R, C)
+    d_col = O.decode_col_form(c["vals_col"], c["meta_col"], R, C)
+    assert (d_row.view(np.uint16) == pruned.view(np.uint16)).all()
+    assert (d_col.view(np.uint16) == pruned.view(np.uint16)).all()
+    assert (_decode_loop(c["vals_row"], c["meta_row"], R, C).view(np.uint16) == pruned.view(np.uint16)).all()
+    assert (_decode_loop(c["vals_col"], c["meta_col"], C, R).T.view(np.uint16) == pruned.view(np.uint16)).all()
+    legal = {0x4, 0x8, 0xC, 0x9, 0xD, 0xE}
+    for meta in (c["meta_row"], c["meta_col"]):
+        for sh in (0, 4, 8, 12):
+            assert set(np.unique((meta >> sh) & 0xF).tolist()) <= legal
+    # kept values are stored in increasing in-group position, sign and all
+    assert c["vals_row"].dtype == np.float16
+
+
+def test_compress_worked_example_b3():
+    # 16x16 tiling of the separable block 4r+c+1 -> every block picks pattern 0
+    b = (np.arange(16, dtype=np.float32) + 1).reshape(4, 4)
+    W = np.tile(b, (4, 4)).astype(np.float16)
+    idx = O.mask_search(W)
+    assert (idx == 0).all()
+    c = O.compress(W, idx)
+    # pattern 0 keeps columns {0,1} in rows 0,1 (nibble 0|1<<2 = 0x4) and
+    # columns {2,3} in rows 2,3 (nibble 2|3<<2 = 0xE); columns likewise.
+    assert c["meta_row"][0, 0] == 0x4444 and c["meta_row"][2, 0] == 0xEEEE
+    assert c["meta_col"][0, 0] == 0x4444 and c["meta_col"][3, 0] == 0xEEEE
+    assert c["vals_row"][0, :2].tolist() == [1, 2] and c["vals_row"][3, :2].tolist() == [15, 16]
+    assert c["vals_col"][0, :2].tolist() == [1, 5] and c["vals_col"][2, :2].tolist() == [11, 15]
+
+
+# ----------------------------------------------------------------------------
+# GEMMs
+def _spmm_loop(A, vals, meta, n_out, K):
+    """float64 A[T,K] times the compressed [n_out, K] matrix, transposed, by explicit loops."""
+    T = A.shape[0]
+    out = np.zeros((T, n_out))
+    for n in range(n_out):
+        for g in range(K // 4):
+            nib = (int(meta[n, g // 4]) >> (4 * (g % 4))) & 0xF
+            for slot, k in ((0, 4 * g + (nib & 3)), (1, 4 * g + (nib >> 2))):
+                w = float(vals[n, 2 * g + slot])
+                out[:, n] += A[:, k].astype(np.float64) * w
+    return out
+
+
+def test_gemm_oracle_matches_explicit_loop():
+    W = _w(19, 32, 48, "normal")
+    idx = O.mask_search(W)
+    c = O.compress(W, idx)
+    rng = np.random.default_rng(20)
+    X = rng.standard_normal((9, 48)).astype(np.float16)
+    dY = rng.standard_normal((9, 32)).astype(np.float16)
+    Y = O.spmm_fwd(X, c["vals_row"], c["meta_row"], 32, 48)
+    dX = O.spmm_bwd_input(dY, c["vals_col"], c["meta_col"], 32, 48)
+    np.testing.assert_allclose(Y, _spmm_loop(X, c["vals_row"], c["meta_row"], 32, 48), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dX, _spmm_loop(dY, c["vals_col"], c["meta_col"], 48, 32), rtol=1e-12, atol=1e-12)
+
+
+def test_gemm_identity_special_cases():
+    W = _w(21, 32, 16, "ints")
+    idx = O.mask_search(W)
+    c = O.compress(W, idx)
+    pruned = np.where(O.idx_to_mask(idx), W, np.float16(0)).astype(np.float64)
+    Y = O.spmm_fwd(np.eye(16, dtype=np.float16), c["vals_row"], c["meta_row"], 32, 16)
+    assert (Y == pruned.T).all()                 # X = I gives Ws^T
+    dX = O.spmm_bwd_input(np.eye(32, dtype=np.float16), c["vals_col"], c["meta_col"], 32, 16)
+    assert (dX == pruned).all()                  # dY = I gives Ws
+
+
+def test_gemm_error_metric():
+    ref = np.array([[1.0, -2.0], [0.5, 4.0]])
+    out = ref + np.array([[0.0, 0.04], [0.0, -0.02]])
+    mr, ma = O.gemm_errors(out, ref)
+    assert abs(mr - 0.01) < 1e-15 and abs(ma - 0.015) < 1e-15
