@@ -1,0 +1,157 @@
+/*
+ * sp24.h - C ABI of the transposable 2:4 sparse FFN kernels for MI355X (gfx950).
+ *
+ * Method: "Accelerating Transformer Pre-training with 2:4 Sparsity" (Hu, Zhao,
+ * Huang, Chen, Zhu; ICML 2024).  Citations below name the part of that paper's
+ * pages that defines each operation:
+ *   [Alg.1]    Algorithm 1, "transposable mask search" (reproducibility table,
+ *              "Pseudocode" row): |W|, a stride-4 correlation with the mask
+ *              patterns, argmax over patterns.
+ *   [Abstract] the abstract: transposable 2:4 masks computed by convolution,
+ *              2:4 sparse matrix multiplication for the FFN layers.
+ *   [SW]       reproducibility table, "Software Dependencies" row: separate
+ *              mask-search and pruning kernels, and 2:4 sparse MMs.
+ *
+ * Conventions shared by every entry point:
+ *   - W is the fp16 weight [R, C], row-major, PyTorch Linear layout [out, in].
+ *   - Every pointer argument except `stream` is a DEVICE pointer owned by the
+ *     caller.  The library allocates nothing, keeps no per-call state and never
+ *     frees caller memory.  Buffers are contiguous and row-major.
+ *   - Every device pointer must be 16-byte aligned (SP24_ERR_ALIGN otherwise).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls enqueue their kernels on that stream and return at once; nothing
+ *     is synchronised.  A fault inside a kernel surfaces at the caller's next
+ *     synchronisation of that stream.
+ *   - Arguments are checked on the host before any HIP call, so every
+ *     validation error is returned without touching the device.  A zero-sized
+ *     problem (R, C or T equal to 0) is valid, launches nothing and may pass
+ *     NULL for its buffers.
+ *   - Calls are reentrant and thread-safe.
+ *   - Inputs are expected to be finite.  +-Inf is handled deterministically
+ *     (Inf scores tie and the first such pattern wins); NaN inputs give
+ *     unspecified (but in-bounds) results.
+ *
+ * Pattern index: the 90 transposable 4x4 patterns (two kept entries in every
+ * row and every column of the block) are numbered by the tuple (a, b, c, d) of
+ * row-pair codes of rows 0..3, in lexicographic order, a slowest, with codes
+ * 0:{0,1} 1:{0,2} 2:{0,3} 3:{1,2} 4:{1,3} 5:{2,3}.
+ *
+ * Compressed 2:4 storage (the pages leave the format open; this is the
+ * library's fixed layout):
+ *   row form     vals_row fp16 [R, C/2], meta_row uint16 [R, C/16].  Row i,
+ *                group g (columns 4g..4g+3) keeps in-group positions i0 < i1:
+ *                vals_row[i][2g] = W[i][4g+i0], vals_row[i][2g+1] = W[i][4g+i1]
+ *                (bit copies), and the nibble (i0 | i1 << 2) sits at bits
+ *                4*(g%4) .. 4*(g%4)+3 of meta_row[i][g/4].
+ *   column form  vals_col fp16 [C, R/2], meta_col uint16 [C, R/16]: the same
+ *                layout applied to the transpose of the pruned W (groups of 4
+ *                along R).  It exists because the masks are transposable, so
+ *                every column group keeps exactly two entries [Abstract].
+ */
+#ifndef SP24_H
+#define SP24_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+  SP24_OK = 0,
+  SP24_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  SP24_ERR_SHAPE = 2,       /* negative size, or not a required multiple         */
+  SP24_ERR_ALIGN = 3,       /* a device pointer is not 16-byte aligned           */
+  SP24_ERR_LAUNCH = 4,      /* the HIP runtime rejected a kernel launch          */
+  SP24_ERR_UNSUPPORTED = 5, /* not available on this device / build              */
+  SP24_ERR_TOO_LARGE = 6    /* a size exceeds the kernels' index range           */
+};
+
+/*
+ * Transposable 2:4 mask search [Alg.1].
+ *
+ * For each 4x4 block (bi, bj) of |W| (rows 4bi..4bi+3, columns 4bj..4bj+3),
+ * scores every pattern p as the fp32 sum of the 8 kept magnitudes added in
+ * row-major order starting from +0, and writes the index of the first maximum
+ * (strict >) to idx[bi * (C/4) + bj].  fp16 subnormals are kept exactly.
+ *
+ *   W    in   fp16 [R, C]
+ *   R, C      R >= 0 and C >= 0, both multiples of 4 (a stride-4 window with
+ *             no padding would drop a remainder; the call refuses it instead)
+ *   idx  out  uint8 [R/4, C/4], values 0..89
+ * Errors: NULL, SHAPE, ALIGN, TOO_LARGE (R*C >= 2^40), LAUNCH.
+ */
+int sp24_mask_search(const void* W, int64_t R, int64_t C, uint8_t* idx, void* stream);
+
+/*
+ * Prune W with the given masks and store both compressed forms [SW, Abstract].
+ *
+ *   W         in   fp16 [R, C]
+ *   idx       in   uint8 [R/4, C/4] pattern indices (values >= 90 give
+ *                  unspecified but in-bounds output)
+ *   R, C           >= 0, both multiples of 16 (a meta word covers 4 groups)
+ *   vals_row  out  fp16 [R, C/2]     meta_row  out  uint16 [R, C/16]
+ *   vals_col  out  fp16 [C, R/2]     meta_col  out  uint16 [C, R/16]
+ * Either (vals, meta) pair may be NULL to skip that form, but not both, and
+ * not one pointer of a pair.
+ * Errors: NULL, SHAPE, ALIGN, TOO_LARGE, LAUNCH.
+ */
+int sp24_compress(const void* W, const uint8_t* idx, int64_t R, int64_t C,
+                  void* vals_row, uint16_t* meta_row,
+                  void* vals_col, uint16_t* meta_col, void* stream);
+
+/*
+ * Mask search and compression in one pass over W [Alg.1, SW]: the same
+ * results as sp24_mask_search followed by sp24_compress, with W read once.
+ * idx may be NULL (not written).  Either (vals, meta) pair may be NULL, as in
+ * sp24_compress.  R, C: >= 0, multiples of 16.
+ * Errors: NULL, SHAPE, ALIGN, TOO_LARGE, LAUNCH.
+ */
+int sp24_search_compress(const void* W, int64_t R, int64_t C, uint8_t* idx,
+                         void* vals_row, uint16_t* meta_row,
+                         void* vals_col, uint16_t* meta_col, void* stream);
+
+/*
+ * Forward 2:4 sparse GEMM  Y = X * Ws^T  [Abstract, SW].
+ *
+ *   X         in   fp16 [T, C] activations
+ *   vals_row, meta_row   in   row form of the pruned W [R, C]
+ *   T, R, C        T >= 0; R, C >= 0 and multiples of 16
+ *   Y         out  fp16 [T, R]; fp32 accumulation, rounded to nearest even
+ * No bias, no activation.  Errors: NULL, SHAPE, ALIGN, TOO_LARGE, LAUNCH.
+ */
+int sp24_spmm_fwd(const void* X, const void* vals_row, const uint16_t* meta_row,
+                  int64_t T, int64_t R, int64_t C, void* Y, void* stream);
+
+/*
+ * Input-gradient 2:4 sparse GEMM  dX = dY * Ws  [Abstract, SW].  Uses the
+ * column form, which exists because the mask is transposable.
+ *
+ *   dY        in   fp16 [T, R]
+ *   vals_col, meta_col   in   column form of the pruned W [R, C]
+ *   T, R, C        as for sp24_spmm_fwd
+ *   dX        out  fp16 [T, C]; fp32 accumulation, rounded to nearest even
+ * Errors: NULL, SHAPE, ALIGN, TOO_LARGE, LAUNCH.
+ */
+int sp24_spmm_bwd_input(const void* dY, const void* vals_col, const uint16_t* meta_col,
+                        int64_t T, int64_t R, int64_t C, void* dX, void* stream);
+
+/* Host only: a static, human-readable name for a status code. */
+const char* sp24_status_str(int status);
+
+/*
+ * Host only: writes the 90 patterns in index order to out[0..89] (host
+ * memory).  Bit 4r+c of out[p] is set when pattern p keeps entry (r, c) of
+ * the block.  Returns SP24_OK, or SP24_ERR_NULL for a NULL out.
+ */
+int sp24_pattern_table(uint16_t* out);
+
+/* Host only: the library's ABI version (1 for this header). */
+int sp24_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SP24_H */

@@ -1,0 +1,125 @@
+// C ABI of the transposable 2:4 FFN kernels (declared in include/sp24.h).
+//
+// Every entry point validates its arguments on the host before any HIP call,
+// then enqueues its kernels on the caller's stream and returns.  Nothing here
+// allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "sp24.h"
+#include "sp24_internal.hpp"
+#include "sp24_patterns.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;        // each dimension below 2^31
+constexpr int64_t kMaxElems = (int64_t)1 << 40;      // each matrix below 2^40 entries
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(int64_t a, int64_t b, int64_t mult) {
+  if (a < 0 || b < 0 || a % mult != 0 || b % mult != 0) return SP24_ERR_SHAPE;
+  if (a >= kMaxDim || b >= kMaxDim) return SP24_ERR_TOO_LARGE;
+  if (a != 0 && b >= kMaxElems / a) return SP24_ERR_TOO_LARGE;
+  return SP24_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? SP24_OK : SP24_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_pair(const void* vals, const void* meta, bool& present) {
+  present = vals != nullptr || meta != nullptr;
+  if (present && (vals == nullptr || meta == nullptr)) return SP24_ERR_NULL;
+  if (present && (!aligned16(vals) || !aligned16(meta))) return SP24_ERR_ALIGN;
+  return SP24_OK;
+}
+
+int compress_common(const void* W, const uint8_t* idx_in, uint8_t* idx_out, int64_t R, int64_t C, void* vals_row,
+                    uint16_t* meta_row, void* vals_col, uint16_t* meta_col, void* stream) {
+  int st = check_dims(R, C, 16);
+  if (st != SP24_OK) return st;
+  bool has_row = false, has_col = false;
+  if ((st = check_pair(vals_row, meta_row, has_row)) != SP24_OK) return st;
+  if ((st = check_pair(vals_col, meta_col, has_col)) != SP24_OK) return st;
+  if (!has_row && !has_col) return SP24_ERR_NULL;
+  if (R == 0 || C == 0) return SP24_OK;
+  if (W == nullptr) return SP24_ERR_NULL;
+  if (!aligned16(W) || (idx_in && !aligned16(idx_in)) || (idx_out && !aligned16(idx_out))) return SP24_ERR_ALIGN;
+  return launch_status(sp24::launch_search_compress(
+      static_cast<const uint16_t*>(W), R, C, idx_in, idx_out, static_cast<uint16_t*>(vals_row), meta_row,
+      static_cast<uint16_t*>(vals_col), meta_col, as_stream(stream)));
+}
+
+int spmm_common(const void* A, const void* vals, const uint16_t* meta, int64_t T, int64_t N, int64_t K, void* out,
+                void* stream) {
+  if (T < 0) return SP24_ERR_SHAPE;
+  int st = check_dims(N, K, 16);
+  if (st != SP24_OK) return st;
+  if (T >= kMaxDim) return SP24_ERR_TOO_LARGE;
+  if (T != 0 && (K >= kMaxElems / T || N >= kMaxElems / T)) return SP24_ERR_TOO_LARGE;
+  if (T == 0 || N == 0) return SP24_OK;
+  if (out == nullptr || (K != 0 && (A == nullptr || vals == nullptr || meta == nullptr))) return SP24_ERR_NULL;
+  if (!aligned16(out) || (K != 0 && (!aligned16(A) || !aligned16(vals) || !aligned16(meta)))) return SP24_ERR_ALIGN;
+  return launch_status(sp24::launch_spmm_nt(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(vals), meta,
+                                            T, N, K, static_cast<uint16_t*>(out), as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int sp24_mask_search(const void* W, int64_t R, int64_t C, uint8_t* idx, void* stream) {
+  int st = check_dims(R, C, 4);
+  if (st != SP24_OK) return st;
+  if (R == 0 || C == 0) return SP24_OK;
+  if (W == nullptr || idx == nullptr) return SP24_ERR_NULL;
+  if (!aligned16(W) || !aligned16(idx)) return SP24_ERR_ALIGN;
+  return launch_status(sp24::launch_mask_search(static_cast<const uint16_t*>(W), R, C, idx, as_stream(stream)));
+}
+
+int sp24_compress(const void* W, const uint8_t* idx, int64_t R, int64_t C, void* vals_row, uint16_t* meta_row,
+                  void* vals_col, uint16_t* meta_col, void* stream) {
+  if (idx == nullptr && R > 0 && C > 0 && R % 16 == 0 && C % 16 == 0) return SP24_ERR_NULL;
+  return compress_common(W, idx, nullptr, R, C, vals_row, meta_row, vals_col, meta_col, stream);
+}
+
+int sp24_search_compress(const void* W, int64_t R, int64_t C, uint8_t* idx, void* vals_row, uint16_t* meta_row,
+                         void* vals_col, uint16_t* meta_col, void* stream) {
+  return compress_common(W, nullptr, idx, R, C, vals_row, meta_row, vals_col, meta_col, stream);
+}
+
+int sp24_spmm_fwd(const void* X, const void* vals_row, const uint16_t* meta_row, int64_t T, int64_t R, int64_t C,
+                  void* Y, void* stream) {
+  // Y[T][R] = X[T][C] * Ws^T: output features R, reduction over C
+  return spmm_common(X, vals_row, meta_row, T, R, C, Y, stream);
+}
+
+int sp24_spmm_bwd_input(const void* dY, const void* vals_col, const uint16_t* meta_col, int64_t T, int64_t R,
+                        int64_t C, void* dX, void* stream) {
+  // dX[T][C] = dY[T][R] * Ws: output features C, reduction over R
+  return spmm_common(dY, vals_col, meta_col, T, C, R, dX, stream);
+}
+
+const char* sp24_status_str(int status) {
+  switch (status) {
+    case SP24_OK: return "ok";
+    case SP24_ERR_NULL: return "null pointer";
+    case SP24_ERR_SHAPE: return "bad shape (negative, or not a required multiple)";
+    case SP24_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case SP24_ERR_LAUNCH: return "kernel launch failed";
+    case SP24_ERR_UNSUPPORTED: return "unsupported";
+    case SP24_ERR_TOO_LARGE: return "size exceeds index range";
+    default: return "unknown status";
+  }
+}
+
+int sp24_pattern_table(uint16_t* out) {
+  if (out == nullptr) return SP24_ERR_NULL;
+  for (int p = 0; p < sp24::kNumPatterns; ++p) out[p] = sp24::kTables.mask[p];
+  return SP24_OK;
+}
+
+int sp24_abi_version(void) { return 1; }
+
+}  // extern "C"

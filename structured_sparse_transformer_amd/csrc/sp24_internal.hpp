@@ -1,0 +1,23 @@
+// Internal launch interface between the C ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace sp24 {
+
+// Mask search only: idx[R/4][C/4].  R, C multiples of 4.
+hipError_t launch_mask_search(const uint16_t* W, int64_t R, int64_t C, uint8_t* idx, hipStream_t s);
+
+// Compression with either the searched masks (idx_in == nullptr: search and,
+// if idx_out != nullptr, write idx) or given masks (idx_in != nullptr).
+// R, C multiples of 16.  Either (vals, meta) pair may be null.
+hipError_t launch_search_compress(const uint16_t* W, int64_t R, int64_t C, const uint8_t* idx_in,
+                                  uint8_t* idx_out, uint16_t* vals_row, uint16_t* meta_row,
+                                  uint16_t* vals_col, uint16_t* meta_col, hipStream_t s);
+
+// out[T][N] = A[T][K] * S[N][K]^T with S in 2:4 row form along K:
+// vals [N][K/2] fp16, meta [N][K/16].  N, K multiples of 16.
+hipError_t launch_spmm_nt(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T,
+                          int64_t N, int64_t K, uint16_t* out, hipStream_t s);
+
+}  // namespace sp24

@@ -1,0 +1,373 @@
+// Transposable 2:4 mask search and 2:4 compression kernels for gfx950.
+//
+// Method: "Accelerating Transformer Pre-training with 2:4 Sparsity",
+// Algorithm 1 (transposable mask search: |W|, a stride-4 correlation with the
+// 90 transposable patterns, argmax over patterns) and the pruning kernel of
+// the "Software Dependencies" row of its reproducibility table.  The pages
+// give the correlation as a conv2d; here it is a per-block search in
+// registers: the score tensor is never materialised.
+//
+// Score semantics (fixed by the library): a pattern's score is the fp32 sum of
+// the 8 kept magnitudes added in row-major order from +0, and the first
+// maximum in pattern order wins.  Two code paths compute exactly that:
+//
+//  * search_fast, for blocks whose sums are all exact in fp32.  With e the
+//    fp16 exponent field, a block is exact when emax - max(emin_nonzero, 1)
+//    <= 10: every entry is then an integer multiple of q = 2^(emin-25) below
+//    2^21 q, so every sum of up to 8 entries is an integer multiple of q below
+//    2^24 q and is exact in fp32 whatever the order of additions.  The sums are
+//    then formed as integers in units of q, shifted left by 7, with 127 - index
+//    in the low 7 bits, so an unsigned max returns the highest score and, among
+//    equal scores, the lowest index.  The score splits into rows 0-1 ("top")
+//    and rows 2-3 ("bottom"); the column counts of the top pair fix which
+//    bottom pairs complete it (19 deficit classes), so the best pattern is the
+//    max over classes of (best top key + best bottom key).
+//  * search_exact_order, for every other block (and Inf/NaN): the 90
+//    sequential fp32 sums in row-major order with a strict > scan.
+//
+// Compression layouts: see include/sp24.h.
+#include <hip/hip_runtime.h>
+#include <algorithm>
+#include <cstdint>
+
+#include "sp24_internal.hpp"
+#include "sp24_patterns.hpp"
+
+namespace sp24 {
+namespace {
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b)));
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b)));
+}
+__device__ __forceinline__ uint32_t pk_dec_u16(uint32_t a) {
+  // subtract 1 from each 16-bit half, wrapping (0 -> 0xFFFF)
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(us2, a) - us2{1, 1});
+}
+
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+}
+
+// m[r][h]: sign-cleared fp16 pairs of block row r; h = 0 holds columns 0 (low
+// half) and 1, h = 1 holds columns 2 and 3.
+struct BlockMag {
+  uint32_t m[4][2];
+};
+
+// Exponent range of the block: returns true (fast path usable) and the scale
+// exponent emin' when all partial sums are exact in fp32.
+__device__ __forceinline__ bool exact_regime(const BlockMag& b, int& emin_out) {
+  uint32_t mx = pk_max_u16(pk_max_u16(pk_max_u16(b.m[0][0], b.m[0][1]), pk_max_u16(b.m[1][0], b.m[1][1])),
+                           pk_max_u16(pk_max_u16(b.m[2][0], b.m[2][1]), pk_max_u16(b.m[3][0], b.m[3][1])));
+  uint32_t mn = pk_min_u16(pk_min_u16(pk_min_u16(pk_dec_u16(b.m[0][0]), pk_dec_u16(b.m[0][1])),
+                                      pk_min_u16(pk_dec_u16(b.m[1][0]), pk_dec_u16(b.m[1][1]))),
+                           pk_min_u16(pk_min_u16(pk_dec_u16(b.m[2][0]), pk_dec_u16(b.m[2][1])),
+                                      pk_min_u16(pk_dec_u16(b.m[3][0]), pk_dec_u16(b.m[3][1]))));
+  const uint32_t hmax = max(mx & 0xFFFFu, mx >> 16);
+  const uint32_t hmin_nz = min(mn & 0xFFFFu, mn >> 16) + 1u;  // 0x10000 when all entries are zero
+  const int emax = (int)(hmax >> 10);
+  const int emin = max((int)(hmin_nz >> 10), 1);                 // 64 when all entries are zero
+  emin_out = emin;
+  return emax < 31 && emax - emin <= 10;
+}
+
+__device__ __forceinline__ int search_fast(const BlockMag& b, int emin) {
+  constexpr const PatternTables& T = kTables;
+  // scale 2^(25 - emin): entries become integers below 2^21.  fma(x, s, 2^23)
+  // is exact and its bit pattern is 0x4B000000 + integer.
+  const float scale = __uint_as_float((uint32_t)(25 - emin + 127) << 23);
+  uint32_t q[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    q[r][0] = __float_as_uint(__builtin_fmaf(half_lo(b.m[r][0]), scale, 8388608.0f));
+    q[r][1] = __float_as_uint(__builtin_fmaf(half_hi(b.m[r][0]), scale, 8388608.0f));
+    q[r][2] = __float_as_uint(__builtin_fmaf(half_lo(b.m[r][1]), scale, 8388608.0f));
+    q[r][3] = __float_as_uint(__builtin_fmaf(half_hi(b.m[r][1]), scale, 8388608.0f));
+  }
+  // Pair sums shifted left by 7.  The two 0x4B000000 offsets sum to
+  // 0x96000000, which vanishes modulo 2^32 after the shift.
+  uint32_t P[4][6];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int k = 0; k < 6; ++k) P[r][k] = (q[r][kPairLo[k]] + q[r][kPairHi[k]]) << 7;
+  // best top and bottom key per deficit class
+  uint32_t top[kNumClasses], bot[kNumClasses];
+  bool top_set[kNumClasses] = {}, bot_set[kNumClasses] = {};
+#pragma unroll
+  for (int p = 0; p < 36; ++p) {
+    const int x = p / 6, y = p % 6;
+    const uint32_t tk = P[0][x] + P[1][y] + (uint32_t)(122 - T.top_base[p]);
+    const uint32_t bk = P[2][x] + P[3][y] + (uint32_t)(5 - T.bot_rank[p]);
+    const int tc = T.pair_class[p], bc = T.bot_class[p];
+    top[tc] = top_set[tc] ? max(top[tc], tk) : tk;
+    top_set[tc] = true;
+    bot[bc] = bot_set[bc] ? max(bot[bc], bk) : bk;
+    bot_set[bc] = true;
+  }
+  uint32_t best = top[0] + bot[0];
+#pragma unroll
+  for (int k = 1; k < kNumClasses; ++k) best = max(best, top[k] + bot[k]);
+  return 127 - (int)(best & 127u);
+}
+
+__device__ __noinline__ int search_exact_order(const BlockMag& b) {
+  constexpr const PatternTables& T = kTables;
+  float a[16];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    a[4 * r + 0] = half_lo(b.m[r][0]);
+    a[4 * r + 1] = half_hi(b.m[r][0]);
+    a[4 * r + 2] = half_lo(b.m[r][1]);
+    a[4 * r + 3] = half_hi(b.m[r][1]);
+  }
+  float best_s = 0.0f;
+  int best = 0;
+#pragma unroll
+  for (int p = 0; p < kNumPatterns; ++p) {
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (T.mask[p] & (1u << e)) s = s + a[e];
+    if (p == 0) {
+      best_s = s;
+    } else if (s > best_s) {
+      best_s = s;
+      best = p;
+    }
+  }
+  return best;
+}
+
+__device__ __forceinline__ int search_block(const BlockMag& b) {
+  int emin;
+  if (exact_regime(b, emin)) return search_fast(b, emin);
+  return search_exact_order(b);
+}
+
+__device__ __forceinline__ BlockMag load_block(const uint32_t (&w)[4][2]) {
+  BlockMag b;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    b.m[r][0] = w[r][0] & 0x7FFF7FFFu;
+    b.m[r][1] = w[r][1] & 0x7FFF7FFFu;
+  }
+  return b;
+}
+
+// ---------------------------------------------------------------------------
+// mask search only
+
+constexpr int kSearchThreads = 256;
+
+__global__ __launch_bounds__(kSearchThreads) void mask_search_kernel(const uint16_t* __restrict__ W, int64_t R,
+                                                                     int64_t C, uint8_t* __restrict__ idx) {
+  const int64_t nbc = C / 4;
+  const int64_t nblocks = (R / 4) * nbc;
+  for (int64_t blk = (int64_t)blockIdx.x * kSearchThreads + threadIdx.x; blk < nblocks;
+       blk += (int64_t)gridDim.x * kSearchThreads) {
+    const int64_t bi = blk / nbc, bj = blk - bi * nbc;
+    uint32_t w[4][2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint2 v = *reinterpret_cast<const uint2*>(W + (4 * bi + r) * C + 4 * bj);
+      w[r][0] = v.x;
+      w[r][1] = v.y;
+    }
+    idx[blk] = (uint8_t)search_block(load_block(w));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// search (or read idx) + compress, one 128x128 tile of W per workgroup
+
+constexpr int kTile = 128;            // rows and columns of W per workgroup
+constexpr int kTB = kTile / 4;        // blocks per tile side (32)
+constexpr int kCompressThreads = 256;
+constexpr int kBlocksPerThread = kTB * kTB / kCompressThreads;  // 4
+
+// byte selectors for v_perm_b32 that gather halves i0 and i1 of a 4-half group
+constexpr uint32_t pair_selector(int i0, int i1) {
+  return (uint32_t)(2 * i0) | (uint32_t)(2 * i0 + 1) << 8 | (uint32_t)(2 * i1) << 16 | (uint32_t)(2 * i1 + 1) << 24;
+}
+
+struct SelTable {
+  uint32_t row_sel[kNumPatterns][4];
+  uint32_t col_sel[kNumPatterns][4];
+  uint32_t nibs[kNumPatterns];  // row nibbles (bits 0..15) | column nibbles << 16
+};
+
+constexpr SelTable build_sel_table() {
+  SelTable s{};
+  for (int p = 0; p < kNumPatterns; ++p) {
+    for (int r = 0; r < 4; ++r) {
+      const int n = (kTables.row_nib[p] >> (4 * r)) & 0xF;
+      s.row_sel[p][r] = pair_selector(n & 3, n >> 2);
+      const int c = (kTables.col_nib[p] >> (4 * r)) & 0xF;
+      s.col_sel[p][r] = pair_selector(c & 3, c >> 2);
+    }
+    s.nibs[p] = (uint32_t)kTables.row_nib[p] | (uint32_t)kTables.col_nib[p] << 16;
+  }
+  return s;
+}
+
+__constant__ SelTable g_sel = build_sel_table();
+
+struct CompressSmem {
+  uint32_t row_sel[kNumPatterns][4];
+  uint32_t col_sel[kNumPatterns][4];
+  uint32_t nibs[kNumPatterns];
+  uint32_t vals_row[kTile][kTB + 1];     // [row][group]: kept pair as one dword
+  uint32_t vals_col[kTile][kTB + 1];     // [column][row group]
+  uint8_t nib_row[kTile][kTB + 4];       // [row][group]: nibble
+  uint8_t nib_col[kTile][kTB + 4];       // [column][row group]
+  uint8_t idx[kTB][kTB];
+};
+
+template <bool kSearch>
+__global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(
+    const uint16_t* __restrict__ W, int64_t R, int64_t C, const uint8_t* __restrict__ idx_in,
+    uint8_t* __restrict__ idx_out, uint16_t* __restrict__ vals_row, uint16_t* __restrict__ meta_row,
+    uint16_t* __restrict__ vals_col, uint16_t* __restrict__ meta_col, int64_t tiles_c, int64_t ntiles) {
+  __shared__ CompressSmem sm;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kNumPatterns * 4; i += kCompressThreads) {
+    (&sm.row_sel[0][0])[i] = (&g_sel.row_sel[0][0])[i];
+    (&sm.col_sel[0][0])[i] = (&g_sel.col_sel[0][0])[i];
+  }
+  for (int i = tid; i < kNumPatterns; i += kCompressThreads) sm.nibs[i] = g_sel.nibs[i];
+
+  // Consecutive workgroups are dealt round-robin to the 8 XCDs; remap so each
+  // XCD walks a contiguous run of tiles (neighbouring output lines then meet
+  // in the same L2).
+  const int64_t per_xcd = (ntiles + 7) / 8;
+  const int64_t lin = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (lin >= ntiles) return;
+  const int64_t ti = lin / tiles_c, tj = lin - ti * tiles_c;
+  const int64_t r0 = ti * kTile, c0 = tj * kTile;
+  const int rows = (int)min<int64_t>(kTile, R - r0), cols = (int)min<int64_t>(kTile, C - c0);
+  const int nbc_t = cols / 4, nbr_t = rows / 4;
+  __syncthreads();
+
+  const int bj = tid % kTB;
+#pragma unroll
+  for (int q = 0; q < kBlocksPerThread; ++q) {
+    const int bi = tid / kTB + q * (kCompressThreads / kTB);
+    if (bi >= nbr_t || bj >= nbc_t) continue;
+    uint32_t w[4][2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint2 v = *reinterpret_cast<const uint2*>(W + (r0 + 4 * bi + r) * C + c0 + 4 * bj);
+      w[r][0] = v.x;
+      w[r][1] = v.y;
+    }
+    int p;
+    if constexpr (kSearch) {
+      p = search_block(load_block(w));
+    } else {
+      p = idx_in[(r0 / 4 + bi) * (C / 4) + c0 / 4 + bj];
+      p = p < kNumPatterns ? p : 0;
+    }
+    sm.idx[bi][bj] = (uint8_t)p;
+    const uint32_t nibs = sm.nibs[p];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sm.vals_row[4 * bi + r][bj] = __builtin_amdgcn_perm(w[r][1], w[r][0], sm.row_sel[p][r]);
+      sm.nib_row[4 * bi + r][bj] = (uint8_t)((nibs >> (4 * r)) & 0xF);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t hsel = (c & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t top = __builtin_amdgcn_perm(w[1][c >> 1], w[0][c >> 1], hsel);  // rows 0,1 of column c
+      const uint32_t bot = __builtin_amdgcn_perm(w[3][c >> 1], w[2][c >> 1], hsel);  // rows 2,3
+      sm.vals_col[4 * bj + c][bi] = __builtin_amdgcn_perm(bot, top, sm.col_sel[p][c]);
+      sm.nib_col[4 * bj + c][bi] = (uint8_t)((nibs >> (16 + 4 * c)) & 0xF);
+    }
+  }
+  __syncthreads();
+
+  // idx: rows of nbc_t bytes, written one dword (4 blocks) at a time
+  if (idx_out) {
+    for (int i = tid; i < nbr_t * (nbc_t / 4); i += kCompressThreads) {
+      const int bi = i / (nbc_t / 4), b4 = i - bi * (nbc_t / 4);
+      const uint32_t v = (uint32_t)sm.idx[bi][4 * b4] | (uint32_t)sm.idx[bi][4 * b4 + 1] << 8 |
+                         (uint32_t)sm.idx[bi][4 * b4 + 2] << 16 | (uint32_t)sm.idx[bi][4 * b4 + 3] << 24;
+      *reinterpret_cast<uint32_t*>(idx_out + (r0 / 4 + bi) * (C / 4) + c0 / 4 + 4 * b4) = v;
+    }
+  }
+  // row form: vals_row[r][c/2], 4 groups (16 bytes) per store
+  if (vals_row) {
+    const int q4 = nbc_t / 4;
+    for (int i = tid; i < rows * q4; i += kCompressThreads) {
+      const int r = i / q4, g4 = i - r * q4;
+      uint4 v;
+      v.x = sm.vals_row[r][4 * g4 + 0];
+      v.y = sm.vals_row[r][4 * g4 + 1];
+      v.z = sm.vals_row[r][4 * g4 + 2];
+      v.w = sm.vals_row[r][4 * g4 + 3];
+      *reinterpret_cast<uint4*>(vals_row + (r0 + r) * (C / 2) + c0 / 2 + 8 * g4) = v;
+    }
+    for (int i = tid; i < rows * q4; i += kCompressThreads) {
+      const int r = i / q4, g4 = i - r * q4;
+      const uint8_t* n = &sm.nib_row[r][4 * g4];
+      meta_row[(r0 + r) * (C / 16) + c0 / 16 + g4] =
+          (uint16_t)(n[0] | n[1] << 4 | n[2] << 8 | n[3] << 12);
+    }
+  }
+  // column form: vals_col[c][r/2]
+  if (vals_col) {
+    const int q4 = nbr_t / 4;
+    for (int i = tid; i < cols * q4; i += kCompressThreads) {
+      const int c = i / q4, g4 = i - c * q4;
+      uint4 v;
+      v.x = sm.vals_col[c][4 * g4 + 0];
+      v.y = sm.vals_col[c][4 * g4 + 1];
+      v.z = sm.vals_col[c][4 * g4 + 2];
+      v.w = sm.vals_col[c][4 * g4 + 3];
+      *reinterpret_cast<uint4*>(vals_col + (c0 + c) * (R / 2) + r0 / 2 + 8 * g4) = v;
+    }
+    for (int i = tid; i < cols * q4; i += kCompressThreads) {
+      const int c = i / q4, g4 = i - c * q4;
+      const uint8_t* n = &sm.nib_col[c][4 * g4];
+      meta_col[(c0 + c) * (R / 16) + r0 / 16 + g4] =
+          (uint16_t)(n[0] | n[1] << 4 | n[2] << 8 | n[3] << 12);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mask_search(const uint16_t* W, int64_t R, int64_t C, uint8_t* idx, hipStream_t s) {
+  const int64_t nblocks = (R / 4) * (C / 4);
+  if (nblocks == 0) return hipSuccess;
+  const int64_t want = (nblocks + kSearchThreads - 1) / kSearchThreads;
+  const int64_t grid = want < (1 << 20) ? want : (1 << 20);
+  hipLaunchKernelGGL(mask_search_kernel, dim3((unsigned)grid), dim3(kSearchThreads), 0, s, W, R, C, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_search_compress(const uint16_t* W, int64_t R, int64_t C, const uint8_t* idx_in,
+                                  uint8_t* idx_out, uint16_t* vals_row, uint16_t* meta_row,
+                                  uint16_t* vals_col, uint16_t* meta_col, hipStream_t s) {
+  if (R == 0 || C == 0) return hipSuccess;
+  const int64_t tiles_r = (R + kTile - 1) / kTile, tiles_c = (C + kTile - 1) / kTile;
+  const int64_t ntiles = tiles_r * tiles_c;
+  const int64_t grid = ((ntiles + 7) / 8) * 8;
+  if (idx_in)
+    hipLaunchKernelGGL(search_compress_kernel<false>, dim3((unsigned)grid), dim3(kCompressThreads), 0, s, W, R,
+                       C, idx_in, nullptr, vals_row, meta_row, vals_col, meta_col, tiles_c, ntiles);
+  else
+    hipLaunchKernelGGL(search_compress_kernel<true>, dim3((unsigned)grid), dim3(kCompressThreads), 0, s, W, R, C,
+                       nullptr, idx_out, vals_row, meta_row, vals_col, meta_col, tiles_c, ntiles);
+  return hipGetLastError();
+}
+
+}  // namespace sp24

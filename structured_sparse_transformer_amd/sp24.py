@@ -1,0 +1,169 @@
+"""ctypes binding of libsp24.so (argument marshalling only).
+
+Each function takes and returns torch tensors on the current HIP device; the
+C library does all of the computing, on the caller's current torch stream.
+Output tensors are allocated with torch when not supplied.  Errors from the
+library raise :class:`Sp24Error`.  There is no fallback: without the built
+library every call raises.
+
+Shapes and layouts follow ``include/sp24.h``: W is fp16 [R, C]; idx uint8
+[R/4, C/4]; the row form is (vals_row fp16 [R, C/2], meta_row int16 [R, C/16])
+and the column form (vals_col fp16 [C, R/2], meta_col int16 [C, R/16]).  torch
+has no uint16, so meta words travel as int16 tensors with the same bits.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsp24.so")
+
+SP24_OK = 0
+STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_LAUNCH",
+                5: "ERR_UNSUPPORTED", 6: "ERR_TOO_LARGE"}
+EXPORTS = ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_spmm_fwd",
+           "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table", "sp24_abi_version")
+
+
+class Sp24Error(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(status, status)} ({text})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libsp24.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m structured_sparse_transformer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        sig = {
+            "sp24_mask_search": [p, i64, i64, p, p],
+            "sp24_compress": [p, p, i64, i64, p, p, p, p, p],
+            "sp24_search_compress": [p, i64, i64, p, p, p, p, p, p],
+            "sp24_spmm_fwd": [p, p, p, i64, i64, i64, p, p],
+            "sp24_spmm_bwd_input": [p, p, p, i64, i64, i64, p, p],
+            "sp24_status_str": [i32],
+            "sp24_pattern_table": [p],
+            "sp24_abi_version": [],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_char_p if name == "sp24_status_str" else i32
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != SP24_OK:
+        raise Sp24Error(fn, status, lib().sp24_status_str(status).decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _out(t, shape, dtype, device):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"output must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    return t
+
+
+def _w(W):
+    if W.dtype != torch.float16 or W.dim() != 2:
+        raise ValueError("W must be a 2-D float16 tensor")
+    return W.shape
+
+
+def sp24_mask_search(W, idx=None, stream=None):
+    """idx[R/4, C/4] (uint8) of the transposable pattern kept by each 4x4 block."""
+    R, C = _w(W)
+    idx = _out(idx, (R // 4, C // 4), torch.uint8, W.device)
+    _check("sp24_mask_search", lib().sp24_mask_search(_ptr(W), R, C, _ptr(idx), _stream(stream)))
+    return idx
+
+
+def _forms(R, C, device, row, col, out):
+    out = dict(out or {})
+    if row:
+        out["vals_row"] = _out(out.get("vals_row"), (R, C // 2), torch.float16, device)
+        out["meta_row"] = _out(out.get("meta_row"), (R, C // 16), torch.int16, device)
+    if col:
+        out["vals_col"] = _out(out.get("vals_col"), (C, R // 2), torch.float16, device)
+        out["meta_col"] = _out(out.get("meta_col"), (C, R // 16), torch.int16, device)
+    return out
+
+
+def sp24_compress(W, idx, row=True, col=True, out=None, stream=None):
+    """Row and/or column 2:4 forms of W pruned by the masks ``idx``."""
+    R, C = _w(W)
+    if idx.dtype != torch.uint8:
+        raise ValueError("idx must be uint8")
+    o = _forms(R, C, W.device, row, col, out)
+    _check("sp24_compress", lib().sp24_compress(
+        _ptr(W), _ptr(idx), R, C, _ptr(o.get("vals_row")), _ptr(o.get("meta_row")),
+        _ptr(o.get("vals_col")), _ptr(o.get("meta_col")), _stream(stream)))
+    return o
+
+
+def sp24_search_compress(W, want_idx=True, row=True, col=True, out=None, stream=None):
+    """Mask search and compression in one pass over W."""
+    R, C = _w(W)
+    o = _forms(R, C, W.device, row, col, out)
+    if want_idx:
+        o["idx"] = _out(o.get("idx"), (R // 4, C // 4), torch.uint8, W.device)
+    _check("sp24_search_compress", lib().sp24_search_compress(
+        _ptr(W), R, C, _ptr(o.get("idx")), _ptr(o.get("vals_row")), _ptr(o.get("meta_row")),
+        _ptr(o.get("vals_col")), _ptr(o.get("meta_col")), _stream(stream)))
+    return o
+
+
+def sp24_spmm_fwd(X, vals_row, meta_row, R, C, Y=None, stream=None):
+    """Y[T, R] = X[T, C] * Ws^T."""
+    T = X.shape[0]
+    if X.dtype != torch.float16 or tuple(X.shape) != (T, C):
+        raise ValueError("X must be float16 [T, C]")
+    Y = _out(Y, (T, R), torch.float16, X.device)
+    _check("sp24_spmm_fwd", lib().sp24_spmm_fwd(_ptr(X), _ptr(vals_row), _ptr(meta_row), T, R, C,
+                                                _ptr(Y), _stream(stream)))
+    return Y
+
+
+def sp24_spmm_bwd_input(dY, vals_col, meta_col, R, C, dX=None, stream=None):
+    """dX[T, C] = dY[T, R] * Ws."""
+    T = dY.shape[0]
+    if dY.dtype != torch.float16 or tuple(dY.shape) != (T, R):
+        raise ValueError("dY must be float16 [T, R]")
+    dX = _out(dX, (T, C), torch.float16, dY.device)
+    _check("sp24_spmm_bwd_input", lib().sp24_spmm_bwd_input(_ptr(dY), _ptr(vals_col), _ptr(meta_col), T, R, C,
+                                                            _ptr(dX), _stream(stream)))
+    return dX
+
+
+def sp24_pattern_table():
+    """The 90 patterns as 16-bit masks (bit 4r+c for kept entry (r, c))."""
+    buf = (ctypes.c_uint16 * 90)()
+    _check("sp24_pattern_table", lib().sp24_pattern_table(ctypes.cast(buf, ctypes.c_void_p)))
+    return list(buf)

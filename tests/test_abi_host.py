@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI library: no GPU and no kernel launch needed.
+
+* libsp24.so loads and exports every function that include/sp24.h declares;
+* the pattern table compiled into the library equals the oracle's
+  independently enumerated list;
+* every argument error is reported before any HIP call (the pointers passed
+  here are fake and would fault if the library ever used them);
+* zero-sized problems succeed without touching the device.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import sp24_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sp24.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from structured_sparse_transformer_amd import sp24
+    if not os.path.exists(sp24.LIB_PATH):
+        from structured_sparse_transformer_amd import build
+        build.build()
+    return sp24.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sp24_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_spmm_fwd",
+              "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table", "sp24_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def test_pattern_table_matches_oracle(L):
+    from structured_sparse_transformer_amd import sp24
+    got = sp24.sp24_pattern_table()
+    masks = O.pattern_masks()
+    want = [int(sum(int(masks[p, r, c]) << (4 * r + c) for r in range(4) for c in range(4))) for p in range(90)]
+    assert got == want
+    assert got[0] == 0xCC33 and got[89] == 0x33CC
+
+
+def test_version_and_status_strings(L):
+    assert L.sp24_abi_version() == 1
+    for s in range(7):
+        assert L.sp24_status_str(s)
+    assert L.sp24_status_str(99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)       # aligned, never dereferenced
+MIS = ctypes.c_void_p(0x1008)        # 8-byte aligned only
+NUL = None
+
+
+def test_mask_search_validation(L):
+    f = L.sp24_mask_search
+    assert f(FAKE, 6, 8, FAKE, NUL) == 2          # R not a multiple of 4
+    assert f(FAKE, 8, 10, FAKE, NUL) == 2
+    assert f(FAKE, -4, 8, FAKE, NUL) == 2
+    assert f(NUL, 8, 8, FAKE, NUL) == 1
+    assert f(FAKE, 8, 8, NUL, NUL) == 1
+    assert f(MIS, 8, 8, FAKE, NUL) == 3
+    assert f(FAKE, 8, 8, MIS, NUL) == 3
+    assert f(FAKE, 1 << 31, 8, FAKE, NUL) == 6
+    assert f(FAKE, 1 << 24, 1 << 20, FAKE, NUL) == 6
+    assert f(NUL, 0, 8, NUL, NUL) == 0            # empty: nothing to do
+    assert f(NUL, 8, 0, NUL, NUL) == 0
+
+
+def test_compress_validation(L):
+    f = L.sp24_compress
+    assert f(FAKE, FAKE, 8, 16, FAKE, FAKE, FAKE, FAKE, NUL) == 2       # R % 16
+    assert f(FAKE, FAKE, 16, 20, FAKE, FAKE, FAKE, FAKE, NUL) == 2
+    assert f(FAKE, NUL, 16, 16, FAKE, FAKE, FAKE, FAKE, NUL) == 1       # idx required
+    assert f(FAKE, FAKE, 16, 16, NUL, NUL, NUL, NUL, NUL) == 1          # no output at all
+    assert f(FAKE, FAKE, 16, 16, FAKE, NUL, NUL, NUL, NUL) == 1         # half a pair
+    assert f(FAKE, FAKE, 16, 16, NUL, NUL, NUL, FAKE, NUL) == 1
+    assert f(NUL, FAKE, 16, 16, FAKE, FAKE, NUL, NUL, NUL) == 1
+    assert f(MIS, FAKE, 16, 16, FAKE, FAKE, NUL, NUL, NUL) == 3
+    assert f(FAKE, FAKE, 16, 16, FAKE, MIS, NUL, NUL, NUL) == 3
+    assert f(NUL, NUL, 0, 16, FAKE, FAKE, NUL, NUL, NUL) == 0
+
+
+def test_search_compress_validation(L):
+    f = L.sp24_search_compress
+    assert f(FAKE, 16, 24, FAKE, FAKE, FAKE, FAKE, FAKE, NUL) == 2
+    assert f(FAKE, 16, 16, FAKE, NUL, NUL, NUL, NUL, NUL) == 1
+    assert f(FAKE, 16, 16, MIS, FAKE, FAKE, NUL, NUL, NUL) == 3
+    assert f(NUL, 0, 0, NUL, FAKE, FAKE, NUL, NUL, NUL) == 0
+
+
+@pytest.mark.parametrize("name", ["sp24_spmm_fwd", "sp24_spmm_bwd_input"])
+def test_spmm_validation(L, name):
+    f = getattr(L, name)
+    assert f(FAKE, FAKE, FAKE, 8, 16, 20, FAKE, NUL) == 2      # C % 16
+    assert f(FAKE, FAKE, FAKE, 8, 20, 16, FAKE, NUL) == 2      # R % 16
+    assert f(FAKE, FAKE, FAKE, -1, 16, 16, FAKE, NUL) == 2
+    assert f(NUL, FAKE, FAKE, 8, 16, 16, FAKE, NUL) == 1
+    assert f(FAKE, NUL, FAKE, 8, 16, 16, FAKE, NUL) == 1
+    assert f(FAKE, FAKE, NUL, 8, 16, 16, FAKE, NUL) == 1
+    assert f(FAKE, FAKE, FAKE, 8, 16, 16, NUL, NUL) == 1
+    assert f(FAKE, FAKE, FAKE, 8, 16, 16, MIS, NUL) == 3
+    assert f(MIS, FAKE, FAKE, 8, 16, 16, FAKE, NUL) == 3
+    assert f(FAKE, FAKE, FAKE, 1 << 31, 16, 16, FAKE, NUL) == 6
+    assert f(NUL, NUL, NUL, 0, 16, 16, NUL, NUL) == 0          # no tokens
+    assert f(NUL, NUL, NUL, 8, 0, 0, NUL, NUL) == 0
+
+
+def test_binding_refuses_cpu_tensors(L):
+    torch = pytest.importorskip("torch")
+    from structured_sparse_transformer_amd import sp24
+    with pytest.raises(ValueError):
+        sp24.sp24_mask_search(torch.zeros(8, 8, dtype=torch.float16))
