@@ -1,0 +1,268 @@
+"""Benchmark of the transposable 2:4 FFN hot path on one MI355X.
+
+Workload: one GPT-2-1.5B-shaped FFN layer (d = 1600, 4d = 6400, 16384
+tokens) run as the noisy re-search loop: at step s the weights are
+W_s = fp16(f32(W_{s-1}) + N(0, 1e-3)) (precomputed and resident in HBM before
+timing), and each step runs
+
+    search+compress(W1_s), search+compress(W2_s)        (sp24_search_compress)
+    Y1  = X   W1s^T,  dX1 = dY1 W1s                     (sp24_spmm_fwd / _bwd_input)
+    Y2  = H   W2s^T,  dX2 = dY2 W2s
+
+Prints one JSON line.  ``value`` is dense-equivalent GEMM TFLOP/s over the
+whole step (2*T*N*K summed over the four GEMMs, divided by the wall time of
+the step including both search+compress calls).  The line also carries the
+search+compress GB/s (4.3125 algorithmic bytes per weight element), the GEMM
+kernel's roofline fraction and the CPU oracle baseline.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from structured_sparse_transformer_amd import workloads as WL  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+FP16_MFMA_PEAK_TFLOPS = 2500.0      # dense fp16 matrix-core peak of MI355X
+SC_BYTES_PER_ELEM = 4.3125          # read W 2, idx 1/16, two 2:4 forms 2 x (1 + 1/8)
+COUNTERS = os.path.join(ROOT, "profiles", "spmm_nt_gpt2-1.5b_counters.json")
+GEMM_SRC = os.path.join(ROOT, "structured_sparse_transformer_amd", "csrc", "sp24_spmm.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def src_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_counters():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    or None when the summary is missing or the kernel source changed since."""
+    try:
+        c = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha256_16") != src_hash(GEMM_SRC):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, sample_tokens: int):
+    """The CPU oracle on a bounded sample of one step, scaled to TFLOP/s."""
+    from oracle import sp24_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    forms = []
+    for W in (inp.w1, inp.w2):
+        idx = O.mask_search(W)
+        forms.append(O.compress(W, idx))
+    t_sc = time.perf_counter() - t0
+    Ts = sample_tokens
+    t0 = time.perf_counter()
+    (f1, f2) = forms
+    d, f = cfg.d, cfg.dff
+    O.spmm_fwd(inp.x[:Ts], f1["vals_row"], f1["meta_row"], f, d)
+    O.spmm_bwd_input(inp.dy1[:Ts], f1["vals_col"], f1["meta_col"], f, d)
+    O.spmm_fwd(inp.h[:Ts], f2["vals_row"], f2["meta_row"], d, f)
+    O.spmm_bwd_input(inp.dy2[:Ts], f2["vals_col"], f2["meta_col"], d, f)
+    t_gemm = time.perf_counter() - t0
+    step_s = t_sc + t_gemm * cfg.tokens / Ts
+    return {
+        "value": round(cfg.dense_equiv_flops() / step_s / 1e12, 4),
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"mask search + compress of W1 and W2 in full (NumPy, single thread, {t_sc:.1f} s) and the "
+                   f"four float64 GEMMs on the first {Ts} of {cfg.tokens} tokens (BLAS, {blas_threads} threads, "
+                   f"{t_gemm:.1f} s), GEMM time scaled linearly to all tokens; one step of the 1.5B loop"),
+        "search_compress_GBps": round(SC_BYTES_PER_ELEM * (inp.w1.size + inp.w2.size) / t_sc / 1e9, 4),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy context numbers")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the transposable 2:4 hot path here has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from structured_sparse_transformer_amd import sp24
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a HIP device")
+    sp24.lib()
+    dev = torch.device("cuda:0")
+    cfg = WL.GPT2_1P5B
+    d, f, T = cfg.d, cfg.dff, cfg.tokens
+    nsteps = args.warmup + args.steps
+
+    t0 = time.perf_counter()
+    inp = WL.ffn_inputs(cfg)
+    to = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    X, H, dY1, dY2 = to(inp.x), to(inp.h), to(inp.dy1), to(inp.dy2)
+    W1s = [to(w) for _, w in WL.noisy_weights(cfg, inp.w1, 1, nsteps)]
+    W2s = [to(w) for _, w in WL.noisy_weights(cfg, inp.w2, 2, nsteps)]
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    def forms(R, C):
+        return {"idx": torch.empty(R // 4, C // 4, dtype=torch.uint8, device=dev),
+                "vals_row": torch.empty(R, C // 2, dtype=torch.float16, device=dev),
+                "meta_row": torch.empty(R, C // 16, dtype=torch.int16, device=dev),
+                "vals_col": torch.empty(C, R // 2, dtype=torch.float16, device=dev),
+                "meta_col": torch.empty(C, R // 16, dtype=torch.int16, device=dev)}
+    F1, F2 = forms(f, d), forms(d, f)
+    Y1 = torch.empty(T, f, dtype=torch.float16, device=dev)
+    dX1 = torch.empty(T, d, dtype=torch.float16, device=dev)
+    Y2 = torch.empty(T, d, dtype=torch.float16, device=dev)
+    dX2 = torch.empty(T, f, dtype=torch.float16, device=dev)
+
+    def step(s, ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        sp24.sp24_search_compress(W1s[s], out=F1)
+        sp24.sp24_search_compress(W2s[s], out=F2)
+        mark(1)
+        sp24.sp24_spmm_fwd(X, F1["vals_row"], F1["meta_row"], f, d, Y=Y1)
+        mark(2)
+        sp24.sp24_spmm_bwd_input(dY1, F1["vals_col"], F1["meta_col"], f, d, dX=dX1)
+        mark(3)
+        sp24.sp24_spmm_fwd(H, F2["vals_row"], F2["meta_row"], d, f, Y=Y2)
+        mark(4)
+        sp24.sp24_spmm_bwd_input(dY2, F2["vals_col"], F2["meta_col"], d, f, dX=dX2)
+        mark(5)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+
+    # timed region: exactly --steps steps, synchronised on both sides
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record()
+    for s in range(args.warmup, nsteps):
+        step(s)
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+    log(f"timed {args.steps} steps: {ms_total:.3f} ms on events, {wall_ms:.3f} ms wall")
+
+    # per-kernel breakdown: the same steps again with events between the calls
+    seg = np.zeros(5)
+    for s in range(args.warmup, nsteps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        step(s, ev)
+        torch.cuda.synchronize()
+        seg += [ev[i].elapsed_time(ev[i + 1]) for i in range(5)]
+    seg /= args.steps
+    sc_ms, gemm_ms = seg[0], seg[1:]
+    gemm_shapes = cfg.gemm_shapes()
+    sc_bytes = SC_BYTES_PER_ELEM * 2 * d * f
+    sc_gbps = sc_bytes / (sc_ms * 1e-3) / 1e9
+    gemm_dense_tflops = [2 * Tt * N * K / (ms * 1e-3) / 1e12 for (_, Tt, N, K), ms in zip(gemm_shapes, gemm_ms)]
+    # roofline of the GEMM kernel: executed (non-zero) flops T*N*K per launch
+    launch_flops = [Tt * N * K for (_, Tt, N, K) in gemm_shapes]
+    avg_launch_ms = float(np.mean(gemm_ms))
+    achieved = float(np.mean(launch_flops)) / (avg_launch_ms * 1e-3) / 1e12
+    traffic = traffic_from_counters()
+
+    flops_step = cfg.dense_equiv_flops()
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    context = None
+    if not args.no_context:
+        context = {}
+        # dense fp16 library GEMM of the same shapes (hipBLASLt through torch) and a copy
+        Wd1 = W1s[0]
+        for _ in range(2):
+            torch.matmul(X, Wd1.t())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch.matmul(X, Wd1.t())
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        context["dense_torch_matmul_fp16_TFLOPs"] = round(2 * T * f * d / (ms * 1e-3) / 1e12, 1)
+        context["dense_torch_matmul_ms"] = round(ms, 4)
+        src = torch.empty(512 * 1024 * 1024 // 2, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        context["copy_512MiB_GBps"] = round(2 * src.numel() * 2 / (ms * 1e-3) / 1e9, 1)
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline ...")
+        cpu = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
+
+    line = {
+        "metric": "mask-search+compress GB/s; 2:4 FFN GEMM TFLOP/s (dense-equiv), GPT-2 shapes",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": "gpt2-1.5b-ffn noisy 20-step loop: search+compress W1,W2 then 4 sparse GEMMs per step",
+                   "d": d, "d_ff": f, "tokens": T, "weights": [[f, d], [d, f]], "seed": cfg.seed},
+        "value_definition": "dense-equivalent GEMM flops per step (sum of 2*T*N*K) / step wall time incl. search+compress",
+        "search_compress_GBps": round(sc_gbps, 1),
+        "search_compress_frac_hbm": round(sc_gbps / HBM_PEAK_GBPS, 4),
+        "search_compress_us_both_weights": round(sc_ms * 1e3, 2),
+        "gemm_TFLOPs_dense_equiv": {n: round(v, 1) for (n, *_), v in zip(gemm_shapes, gemm_dense_tflops)},
+        "gemm_us": {n: round(ms * 1e3, 1) for (n, *_), ms in zip(gemm_shapes, gemm_ms)},
+        "roofline": {"kernel": "spmm_nt_kernel", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": traffic,
+                     "note": "executed non-zero flops T*N*K per launch (half the dense-equivalent 2*T*N*K) over the "
+                             "dense fp16 MFMA peak; equal to dense-equivalent flops over the 2:4 sparse peak"},
+        "cpu_baseline": cpu,
+        "context": context,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -236,11 +236,277 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* vals, const uint16_t* m
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Fast path (K a multiple of 64, every operand below 2 GiB).
+//
+// Workgroup tile BM features x BN tokens, 4 waves in a 2 x 2 grid, each
+// wave WM x WN.  A 3-stage LDS ring is filled by direct global->LDS buffer
+// loads (no VGPR round trip), two stages ahead of the one being computed, so
+// HBM/L2 latency hides behind two stages of MFMA work.  Rows past N or T read
+// as zero (buffer bounds); they only feed outputs that are not stored.
+//
+// LDS layouts (per stage), both XOR-swizzled so that ds_read_b128 is free of
+// bank conflicts for 8- and 16-lane groups:
+//   S  [BM rows][4 chunks of 16 B]: chunk c of row r at slot c ^ fS(r)
+//   B  [BN rows][8 chunks of 16 B]: chunk c of row r at slot c ^ fB(r)
+//   meta [BM rows][2 dwords]
+// A direct load writes 64 consecutive 16-byte LDS slots, one per lane, so each
+// lane fetches the global chunk whose swizzled slot is its own lane index.
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, gfx9 family
+
+// Raw buffer descriptor over [base, base + bytes), kept in scalar registers.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = (int)kRsrcWord3;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+
+// Direct global->LDS loads: lane l's bytes land at LDS address m0 + l * size.
+// Written as asm so that the compiler's wait-count pass does not make every
+// later LDS read wait for all outstanding loads (it cannot tell the stage
+// buffers apart); completion is tracked with explicit vmcnt waits instead.
+// The asm has no register outputs.  s_nop 0 covers the M0 write hazard.
+__device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t lds, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(i32x4 rsrc, uint32_t lds, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ int swz_s(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int swz_b(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int BM, int BN, int WM, int WN>
+struct FastCfg {
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int S_BYTES = BM * 64, B_BYTES = BN * 128, M_BYTES = BM * 8;
+  static constexpr int S_LOADS = S_BYTES / 1024 / WAVES;   // 16-byte direct loads per wave per stage
+  static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
+  static constexpr int M_LOADS = M_BYTES / 256 / WAVES;    // 4-byte direct loads
+  static constexpr int LOADS = S_LOADS + B_LOADS + M_LOADS;
+  static_assert(S_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0 && M_BYTES % (256 * WAVES) == 0,
+                "tile does not split evenly into direct loads");
+  static_assert(LOADS <= 63, "vmcnt range");
+};
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ vals, const uint16_t* __restrict__ meta,
+    int64_t T, int64_t N, int64_t K, uint16_t* __restrict__ out, int tiles_m, int tiles_n) {
+  using Cfg = FastCfg<BM, BN, WM, WN>;
+  __shared__ __align__(1024) unsigned char s_st0[Cfg::S_BYTES], s_st1[Cfg::S_BYTES], s_st2[Cfg::S_BYTES];
+  __shared__ __align__(1024) unsigned char b_st0[Cfg::B_BYTES], b_st1[Cfg::B_BYTES], b_st2[Cfg::B_BYTES];
+  __shared__ __align__(256) unsigned char m_st0[Cfg::M_BYTES], m_st1[Cfg::M_BYTES], m_st2[Cfg::M_BYTES];
+
+  // tile order: groups of kGroupM feature tiles, token tiles within a group,
+  // features fastest; each XCD (workgroups are dealt round-robin to 8 XCDs)
+  // takes a contiguous run of that order so concurrent tiles share operands in
+  // its L2
+  constexpr int kGroupM = 8;
+  const int ntiles = tiles_m * tiles_n;
+  const int per_xcd = (ntiles + 7) / 8;
+  const int lin = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (lin >= ntiles) return;
+  const int group = lin / (kGroupM * tiles_n);
+  const int gm0 = group * kGroupM;
+  const int gsize = min(kGroupM, tiles_m - gm0);
+  const int in_group = lin - group * kGroupM * tiles_n;
+  // the tile indices are uniform; readfirstlane keeps them (and the buffer
+  // descriptors built from them) in scalar registers
+  const int tn = __builtin_amdgcn_readfirstlane(in_group / gsize);
+  const int tm = __builtin_amdgcn_readfirstlane(gm0 + in_group % gsize);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  const int tid = threadIdx.x;
+  // the wave index is uniform across the wave; say so, since the direct
+  // loads take their LDS destination from a scalar register
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % Cfg::WAVES_M, wn = wave / Cfg::WAVES_M;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int Kh = (int)(K / 2), Km = (int)(K / 16);
+  const int nk = (int)(K / 64);
+
+  // buffer resources based at this tile's first row; bytes past the matrix
+  // end are out of range and load as zero
+  const i32x4 rs = make_rsrc(vals + m0 * Kh, (uint32_t)((N - m0) * Kh * 2));
+  const i32x4 rb = make_rsrc(A + n0 * K, (uint32_t)((T - n0) * K * 2));
+  const i32x4 rm = make_rsrc(meta + m0 * Km, (uint32_t)((N - m0) * Km * 2));
+
+  // per-lane global byte offsets of this wave's direct loads (stage 0)
+  int off_s[Cfg::S_LOADS], off_b[Cfg::B_LOADS], off_m[Cfg::M_LOADS];
+#pragma unroll
+  for (int i = 0; i < Cfg::S_LOADS; ++i) {
+    const int q = wave * Cfg::S_LOADS + i;          // 1 KiB block: rows 16q .. 16q+15
+    const int r = 16 * q + lane / 4, p = lane % 4;
+    off_s[i] = r * Kh * 2 + ((p ^ swz_s(r)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < Cfg::B_LOADS; ++i) {
+    const int q = wave * Cfg::B_LOADS + i;          // rows 8q .. 8q+7
+    const int r = 8 * q + lane / 8, p = lane % 8;
+    off_b[i] = r * K * 2 + ((p ^ swz_b(r)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < Cfg::M_LOADS; ++i) {
+    const int q = wave * Cfg::M_LOADS + i;          // rows 32q .. 32q+31
+    const int r = 32 * q + lane / 2;
+    off_m[i] = r * Km * 2 + (lane % 2) * 4;
+  }
+
+  auto issue = [&](int kt, unsigned char* sb, unsigned char* bb, unsigned char* mb) {
+    const int ds = kt * 64, db = kt * 128, dm = kt * 8;
+#pragma unroll
+    for (int i = 0; i < Cfg::S_LOADS; ++i)
+      dma_b128(rs, lds_addr(sb) + (wave * Cfg::S_LOADS + i) * 1024, off_s[i] + ds);
+#pragma unroll
+    for (int i = 0; i < Cfg::B_LOADS; ++i)
+      dma_b128(rb, lds_addr(bb) + (wave * Cfg::B_LOADS + i) * 1024, off_b[i] + db);
+#pragma unroll
+    for (int i = 0; i < Cfg::M_LOADS; ++i)
+      dma_b32(rm, lds_addr(mb) + (wave * Cfg::M_LOADS + i) * 256, off_m[i] + dm);
+  };
+
+  // LDS read offsets of this lane (bytes), independent of the stage
+  const int fs = swz_s(l32), fb = swz_b(l32);
+  const int rd_s0 = (wm * WM + l32) * 64 + (((0 + g) ^ fs) * 16);   // K32 step 0: chunk g
+  const int rd_s1 = (wm * WM + l32) * 64 + (((2 + g) ^ fs) * 16);   // step 1: chunk 2 + g
+  int rd_b[2][2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) rd_b[st][h] = (wn * WN + l32) * 128 + (((4 * st + 2 * h + g) ^ fb) * 16);
+  const int rd_m = (wm * WM + l32) * 8;
+
+  f16v acc[Cfg::TM][Cfg::TN];
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  auto compute = [&](const unsigned char* sb, const unsigned char* bb, const unsigned char* mb) {
+    uint32_t idx[Cfg::TM][2];
+#pragma unroll
+    for (int mt = 0; mt < Cfg::TM; ++mt) {
+      const uint2 mw = *reinterpret_cast<const uint2*>(mb + rd_m + mt * 32 * 8);
+      idx[mt][0] = g ? (mw.x >> 16) : mw.x;
+      idx[mt][1] = g ? (mw.y >> 16) : mw.y;
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      h8 af[Cfg::TM];
+      h16 bf[Cfg::TN];
+#pragma unroll
+      for (int mt = 0; mt < Cfg::TM; ++mt)
+        af[mt] = *reinterpret_cast<const h8*>(sb + (st ? rd_s1 : rd_s0) + mt * 32 * 64);
+#pragma unroll
+      for (int nt = 0; nt < Cfg::TN; ++nt) {
+        const h8 lo = *reinterpret_cast<const h8*>(bb + rd_b[st][0] + nt * 32 * 128);
+        const h8 hi = *reinterpret_cast<const h8*>(bb + rd_b[st][1] + nt * 32 * 128);
+        bf[nt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      }
+#pragma unroll
+      for (int mt = 0; mt < Cfg::TM; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < Cfg::TN; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(af[mt], bf[nt], acc[mt][nt], (int)idx[mt][st], 0, 0);
+    }
+  };
+
+  // vmcnt wait: allow `n` of this wave's direct loads to stay in flight
+  auto wait_loads = [&](bool next_in_flight) {
+    if (next_in_flight) {
+      // vmcnt = LOADS (bits 3:0 and 15:14), expcnt 7 and lgkmcnt 15 = no wait
+      constexpr int n = Cfg::LOADS;
+      __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+    } else {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    }
+  };
+
+  auto stage = [&](int kt, const unsigned char* sc, const unsigned char* bc, const unsigned char* mc,
+                   unsigned char* sn, unsigned char* bn, unsigned char* mn) {
+    // Own loads of stage kt done (vmcnt), then a bare barrier: every wave's
+    // loads of stage kt have landed and every wave has finished reading the
+    // buffer the next issue overwrites.  A __syncthreads() fence would also
+    // wait for the loads of stage kt+1 and serialise the pipeline.
+    wait_loads(kt + 1 < nk);
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < nk) issue(kt + 2, sn, bn, mn);
+    compute(sc, bc, mc);
+  };
+
+  issue(0, s_st0, b_st0, m_st0);
+  if (nk > 1) issue(1, s_st1, b_st1, m_st1);
+  for (int kt = 0; kt < nk; kt += 3) {
+    stage(kt, s_st0, b_st0, m_st0, s_st2, b_st2, m_st2);
+    if (kt + 1 < nk) stage(kt + 1, s_st1, b_st1, m_st1, s_st0, b_st0, m_st0);
+    if (kt + 2 < nk) stage(kt + 2, s_st2, b_st2, m_st2, s_st1, b_st1, m_st1);
+  }
+
+  // epilogue: fp32 -> fp16 (round to nearest even), 4 features per 8-byte store
+#pragma unroll
+  for (int mt = 0; mt < Cfg::TM; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < Cfg::TN; ++nt) {
+      const int64_t n = n0 + wn * WN + nt * 32 + l32;
+      if (n >= T) continue;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int64_t m = m0 + wm * WM + mt * 32 + 8 * i4 + 4 * g;
+        if (m >= N) continue;
+        const f16v& a = acc[mt][nt];
+        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a[4 * i4 + 0]) |
+                            (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a[4 * i4 + 1]) << 16;
+        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a[4 * i4 + 2]) |
+                            (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a[4 * i4 + 3]) << 16;
+        *reinterpret_cast<uint2*>(out + n * N + m) = make_uint2(lo, hi);
+      }
+    }
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_fast(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T, int64_t N,
+                       int64_t K, uint16_t* out, hipStream_t s) {
+  using Cfg = FastCfg<BM, BN, WM, WN>;
+  const int tiles_m = (int)((N + BM - 1) / BM), tiles_n = (int)((T + BN - 1) / BN);
+  const int ntiles = tiles_m * tiles_n;
+  const int grid = ((ntiles + 7) / 8) * 8;
+  hipLaunchKernelGGL((spmm_nt_fast_kernel<BM, BN, WM, WN>), dim3(grid), dim3(Cfg::THREADS), 0, s, A, vals, meta, T, N,
+                     K, out, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_spmm_nt(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T, int64_t N,
                           int64_t K, uint16_t* out, hipStream_t s) {
   if (T == 0 || N == 0) return hipSuccess;
+  constexpr int64_t kMaxBuf = (int64_t)1 << 31;   // buffer offsets are 32-bit
+  const bool fast = K % 64 == 0 && K > 0 && T * K * 2 < kMaxBuf && N * K < kMaxBuf && T * N * 2 < ((int64_t)1 << 40);
+  if (fast) return launch_fast<256, 256, 128, 128>(A, vals, meta, T, N, K, out, s);
   return launch_cfg<256, 128, 128, 64>(A, vals, meta, T, N, K, out, s);
 }
 
