@@ -96,6 +96,35 @@ def cpu_baseline(cfg, inp, sample_tokens: int):
     }
 
 
+def profile_only(args, sp24, torch, dev, cfg, F1, F2, W1s, W2s, X, dY1, H, dY2, Y1, dX1, Y2, dX2):
+    """Runs one kernel family alone so that counter passes see only it."""
+    d, f = cfg.d, cfg.dff
+    n = args.steps
+    if args.profile_kernel == "copy":
+        # plain copy of a known size: calibrates FETCH_SIZE / WRITE_SIZE
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.float16, device=dev)      # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(n):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy: {n} x 512 MiB")
+        return
+    for s in range(len(W1s)):
+        sp24.sp24_search_compress(W1s[s], out=F1)
+        sp24.sp24_search_compress(W2s[s], out=F2)
+        if args.profile_kernel == "search_compress" and s + 1 >= n:
+            break
+    torch.cuda.synchronize()
+    if args.profile_kernel == "gemm":
+        for _ in range(n):
+            sp24.sp24_spmm_fwd(X, F1["vals_row"], F1["meta_row"], f, d, Y=Y1)
+            sp24.sp24_spmm_bwd_input(dY1, F1["vals_col"], F1["meta_col"], f, d, dX=dX1)
+            sp24.sp24_spmm_fwd(H, F2["vals_row"], F2["meta_row"], d, f, Y=Y2)
+            sp24.sp24_spmm_bwd_input(dY2, F2["vals_col"], F2["meta_col"], d, f, dX=dX2)
+        torch.cuda.synchronize()
+    log(f"{args.profile_kernel}: {n} rounds")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +133,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy context numbers")
+    ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "copy"],
+                    help="run only this kernel --steps times (for rocprofv3 counter passes); prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the transposable 2:4 hot path here has no multi-GPU mode "
@@ -156,6 +187,10 @@ def main():
         mark(4)
         sp24.sp24_spmm_bwd_input(dY2, F2["vals_col"], F2["meta_col"], d, f, dX=dX2)
         mark(5)
+
+    if args.profile_kernel:
+        profile_only(args, sp24, torch, dev, cfg, F1, F2, W1s, W2s, X, dY1, H, dY2, Y1, dX1, Y2, dX2)
+        return
 
     for s in range(args.warmup):
         step(s)

@@ -273,22 +273,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_u8*)p;
 }
 
-// Direct global->LDS loads: lane l's bytes land at LDS address m0 + l * size.
+// Direct global->LDS loads: lane l's bytes land at LDS address M0 + l * size.
 // Written as asm so that the compiler's wait-count pass does not make every
 // later LDS read wait for all outstanding loads (it cannot tell the stage
 // buffers apart); completion is tracked with explicit vmcnt waits instead.
-// The asm has no register outputs.  s_nop 0 covers the M0 write hazard.
+// The LDS address is an input bound to M0, so the compiler sets M0; the asm
+// has no register outputs, and its s_nop 0 covers the M0-write hazard.
 __device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t lds, int voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voffset), "s"(rsrc)
-               : "memory", "m0");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voffset), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void dma_b32(i32x4 rsrc, uint32_t lds, int voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voffset), "s"(rsrc)
-               : "memory", "m0");
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" : : "v"(voffset), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ int swz_s(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
@@ -315,9 +310,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ vals, const uint16_t* __restrict__ meta,
     int64_t T, int64_t N, int64_t K, uint16_t* __restrict__ out, int tiles_m, int tiles_n) {
   using Cfg = FastCfg<BM, BN, WM, WN>;
-  __shared__ __align__(1024) unsigned char s_st0[Cfg::S_BYTES], s_st1[Cfg::S_BYTES], s_st2[Cfg::S_BYTES];
-  __shared__ __align__(1024) unsigned char b_st0[Cfg::B_BYTES], b_st1[Cfg::B_BYTES], b_st2[Cfg::B_BYTES];
-  __shared__ __align__(256) unsigned char m_st0[Cfg::M_BYTES], m_st1[Cfg::M_BYTES], m_st2[Cfg::M_BYTES];
+  // one LDS block: 3 S slots, 3 B slots, 3 meta slots (the epilogue reuses
+  // the start of it to stage the output tile)
+  __shared__ __align__(1024) unsigned char smem[3 * (Cfg::S_BYTES + Cfg::B_BYTES + Cfg::M_BYTES)];
 
   // tile order: groups of kGroupM feature tiles, token tiles within a group,
   // features fastest; each XCD (workgroups are dealt round-robin to 8 XCDs)
@@ -389,8 +384,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
 
   // LDS read offsets of this lane (bytes), independent of the stage
   const int fs = swz_s(l32), fb = swz_b(l32);
-  const int rd_s0 = (wm * WM + l32) * 64 + (((0 + g) ^ fs) * 16);   // K32 step 0: chunk g
-  const int rd_s1 = (wm * WM + l32) * 64 + (((2 + g) ^ fs) * 16);   // step 1: chunk 2 + g
+  int rd_s[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) rd_s[st] = (wm * WM + l32) * 64 + (((2 * st + g) ^ fs) * 16);
   int rd_b[2][2];
 #pragma unroll
   for (int st = 0; st < 2; ++st)
@@ -406,39 +402,44 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  auto compute = [&](const unsigned char* sb, const unsigned char* bb, const unsigned char* mb) {
-    uint32_t idx[Cfg::TM][2];
+  // register fragments of one K32 step
+  struct Frags {
+    h8 a[Cfg::TM];
+    h16 b[Cfg::TN];
+  };
+  auto load_frags = [&](const unsigned char* sb, const unsigned char* bb, int st, Frags& f) {
+#pragma unroll
+    for (int mt = 0; mt < Cfg::TM; ++mt) f.a[mt] = *reinterpret_cast<const h8*>(sb + rd_s[st] + mt * 32 * 64);
+#pragma unroll
+    for (int nt = 0; nt < Cfg::TN; ++nt) {
+      const h8 lo = *reinterpret_cast<const h8*>(bb + rd_b[st][0] + nt * 32 * 128);
+      const h8 hi = *reinterpret_cast<const h8*>(bb + rd_b[st][1] + nt * 32 * 128);
+      f.b[nt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    }
+  };
+  // meta words of this lane's rows for both K32 steps of a stage
+  auto load_meta = [&](const unsigned char* mb, uint2 (&mw)[Cfg::TM]) {
+#pragma unroll
+    for (int mt = 0; mt < Cfg::TM; ++mt) mw[mt] = *reinterpret_cast<const uint2*>(mb + rd_m + mt * 32 * 8);
+  };
+  auto mfmas = [&](const Frags& f, const uint2 (&mw)[Cfg::TM], int st) {
 #pragma unroll
     for (int mt = 0; mt < Cfg::TM; ++mt) {
-      const uint2 mw = *reinterpret_cast<const uint2*>(mb + rd_m + mt * 32 * 8);
-      idx[mt][0] = g ? (mw.x >> 16) : mw.x;
-      idx[mt][1] = g ? (mw.y >> 16) : mw.y;
-    }
+      const uint32_t w = st ? mw[mt].y : mw[mt].x;
+      const int idx = (int)(g ? (w >> 16) : w);
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      h8 af[Cfg::TM];
-      h16 bf[Cfg::TN];
-#pragma unroll
-      for (int mt = 0; mt < Cfg::TM; ++mt)
-        af[mt] = *reinterpret_cast<const h8*>(sb + (st ? rd_s1 : rd_s0) + mt * 32 * 64);
-#pragma unroll
-      for (int nt = 0; nt < Cfg::TN; ++nt) {
-        const h8 lo = *reinterpret_cast<const h8*>(bb + rd_b[st][0] + nt * 32 * 128);
-        const h8 hi = *reinterpret_cast<const h8*>(bb + rd_b[st][1] + nt * 32 * 128);
-        bf[nt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-      }
-#pragma unroll
-      for (int mt = 0; mt < Cfg::TM; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < Cfg::TN; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(af[mt], bf[nt], acc[mt][nt], (int)idx[mt][st], 0, 0);
+      for (int nt = 0; nt < Cfg::TN; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(f.a[mt], f.b[nt], acc[mt][nt], idx, 0, 0);
     }
   };
 
-  // vmcnt wait: allow `n` of this wave's direct loads to stay in flight
-  auto wait_loads = [&](bool next_in_flight) {
-    if (next_in_flight) {
-      // vmcnt = LOADS (bits 3:0 and 15:14), expcnt 7 and lgkmcnt 15 = no wait
+  // vmcnt wait: allow `stages` stages of this wave's direct loads in flight
+  auto wait_loads = [&](int stages) {
+    // vmcnt in bits 3:0 and 15:14; expcnt 7 and lgkmcnt 15 mean no wait
+    if (stages >= 2) {
+      constexpr int n = 2 * Cfg::LOADS;
+      __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+    } else if (stages == 1) {
       constexpr int n = Cfg::LOADS;
       __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
     } else {
@@ -446,45 +447,89 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
     }
   };
 
-  auto stage = [&](int kt, const unsigned char* sc, const unsigned char* bc, const unsigned char* mc,
-                   unsigned char* sn, unsigned char* bn, unsigned char* mn) {
-    // Own loads of stage kt done (vmcnt), then a bare barrier: every wave's
-    // loads of stage kt have landed and every wave has finished reading the
-    // buffer the next issue overwrites.  A __syncthreads() fence would also
-    // wait for the loads of stage kt+1 and serialise the pipeline.
-    wait_loads(kt + 1 < nk);
-    __builtin_amdgcn_s_barrier();
-    if (kt + 2 < nk) issue(kt + 2, sn, bn, mn);
-    compute(sc, bc, mc);
-  };
+  unsigned char* const s_buf[3] = {smem, smem + Cfg::S_BYTES, smem + 2 * Cfg::S_BYTES};
+  unsigned char* const b_buf[3] = {smem + 3 * Cfg::S_BYTES, smem + 3 * Cfg::S_BYTES + Cfg::B_BYTES,
+                                   smem + 3 * Cfg::S_BYTES + 2 * Cfg::B_BYTES};
+  unsigned char* const m_buf[3] = {smem + 3 * (Cfg::S_BYTES + Cfg::B_BYTES),
+                                   smem + 3 * (Cfg::S_BYTES + Cfg::B_BYTES) + Cfg::M_BYTES,
+                                   smem + 3 * (Cfg::S_BYTES + Cfg::B_BYTES) + 2 * Cfg::M_BYTES};
 
-  issue(0, s_st0, b_st0, m_st0);
-  if (nk > 1) issue(1, s_st1, b_st1, m_st1);
+  // Pipeline.  Stage s (64 of K) is loaded into ring slot s % 3 three stages
+  // ahead.  Within stage kt: the fragments of its second K32 step are read
+  // while the first step's MFMAs run; then, mid-stage, the wave waits for
+  // stage kt+1 to land, all waves meet at a barrier (after which nobody reads
+  // slot kt % 3 again), stage kt+3 is issued into that slot, and the first
+  // fragments of stage kt+1 are read while the second step's MFMAs run.
+  for (int s = 0; s < 3; ++s)
+    if (s < nk) issue(s, s_buf[s], b_buf[s], m_buf[s]);
+  wait_loads(min(nk, 3) - 1);
+  __builtin_amdgcn_s_barrier();
+  Frags f0, f1;
+  uint2 mw[Cfg::TM], mw_next[Cfg::TM];
+  load_meta(m_buf[0], mw);
+  load_frags(s_buf[0], b_buf[0], 0, f0);
+
+  auto stage = [&](int kt, int cur, int nxt) {
+    load_frags(s_buf[cur], b_buf[cur], 1, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f0, mw, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_loads(kt + 2 < nk ? 1 : 0);
+    // lgkmcnt(0): this wave's reads of slot kt % 3 are complete before the
+    // barrier lets stage kt+3 overwrite it (vmcnt 63, expcnt 7 = no wait)
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
+    __builtin_amdgcn_s_barrier();
+    if (kt + 3 < nk) issue(kt + 3, s_buf[cur], b_buf[cur], m_buf[cur]);
+    if (kt + 1 < nk) {
+      load_meta(m_buf[nxt], mw_next);
+      load_frags(s_buf[nxt], b_buf[nxt], 0, f0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1, mw, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < Cfg::TM; ++mt) mw[mt] = mw_next[mt];
+  };
   for (int kt = 0; kt < nk; kt += 3) {
-    stage(kt, s_st0, b_st0, m_st0, s_st2, b_st2, m_st2);
-    if (kt + 1 < nk) stage(kt + 1, s_st1, b_st1, m_st1, s_st0, b_st0, m_st0);
-    if (kt + 2 < nk) stage(kt + 2, s_st2, b_st2, m_st2, s_st1, b_st1, m_st1);
+    stage(kt, 0, 1);
+    if (kt + 1 < nk) stage(kt + 1, 1, 2);
+    if (kt + 2 < nk) stage(kt + 2, 2, 0);
   }
 
-  // epilogue: fp32 -> fp16 (round to nearest even), 4 features per 8-byte store
+  // Epilogue: fp32 -> fp16 (round to nearest even).  Each wave stages its
+  // WN tokens x WM features in LDS (token-major, 16-byte chunks XOR-swizzled
+  // by token) and writes whole contiguous token rows, so every store fills
+  // complete cache lines.  The ring is idle now: all loads were waited for,
+  // and the barrier makes sure no wave still reads its last fragments.
+  static_assert(Cfg::WAVES * WN * WM * 2 <= 3 * (Cfg::S_BYTES + Cfg::B_BYTES), "staging does not fit");
+  static_assert(WM == 128, "epilogue assumes 16 chunks of 8 features per token row");
+  __builtin_amdgcn_s_barrier();
+  unsigned char* stage_base = smem + (size_t)wave * WN * WM * 2;
 #pragma unroll
   for (int mt = 0; mt < Cfg::TM; ++mt)
 #pragma unroll
     for (int nt = 0; nt < Cfg::TN; ++nt) {
-      const int64_t n = n0 + wn * WN + nt * 32 + l32;
-      if (n >= T) continue;
+      const int t = nt * 32 + l32;                     // token within the wave tile
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int64_t m = m0 + wm * WM + mt * 32 + 8 * i4 + 4 * g;
-        if (m >= N) continue;
         const f16v& a = acc[mt][nt];
         const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a[4 * i4 + 0]) |
                             (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a[4 * i4 + 1]) << 16;
         const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a[4 * i4 + 2]) |
                             (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a[4 * i4 + 3]) << 16;
-        *reinterpret_cast<uint2*>(out + n * N + m) = make_uint2(lo, hi);
+        const int chunk = mt * 4 + i4;                 // 8 features per chunk: mt*32 + 8*i4 + 4g
+        *reinterpret_cast<uint2*>(stage_base + t * 256 + ((chunk ^ (t & 15)) * 16) + 8 * g) = make_uint2(lo, hi);
       }
     }
+  // the wave reads back only what it wrote, in order, so no barrier is needed
+#pragma unroll 4
+  for (int it = 0; it < WN * 16 / 64; ++it) {
+    const int t = it * 4 + lane / 16, c = lane % 16;
+    const uint4 v = *reinterpret_cast<const uint4*>(stage_base + t * 256 + ((c ^ (t & 15)) * 16));
+    const int64_t n = n0 + wn * WN + t;
+    const int64_t m = m0 + wm * WM + c * 8;
+    if (n < T && m < N) *reinterpret_cast<uint4*>(out + n * N + m) = v;
+  }
 }
 
 template <int BM, int BN, int WM, int WN>
