@@ -239,8 +239,8 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* vals, const uint16_t* m
 // ---------------------------------------------------------------------------
 // Fast path (K a multiple of 64, every operand below 2 GiB).
 //
-// Workgroup tile BM features x BN tokens, 4 waves in a 2 x 2 grid, each
-// wave WM x WN.  A 3-stage LDS ring is filled by direct global->LDS buffer
+// Workgroup tile BM features x BN tokens in waves of WM x WN (launched as
+// 256 x 256 with 8 waves of 128 x 64, two waves per SIMD).  A 3-stage LDS ring is filled by direct global->LDS buffer
 // loads (no VGPR round trip), two stages ahead of the one being computed, so
 // HBM/L2 latency hides behind two stages of MFMA work.  Rows past N or T read
 // as zero (buffer bounds); they only feed outputs that are not stored.
@@ -422,7 +422,11 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
 #pragma unroll
     for (int mt = 0; mt < Cfg::TM; ++mt) mw[mt] = *reinterpret_cast<const uint2*>(mb + rd_m + mt * 32 * 8);
   };
+  // Two waves share each SIMD; raising the priority of the wave that is in
+  // its MFMA block lets it issue back to back while the other wave issues its
+  // LDS reads and direct loads in between.
   auto mfmas = [&](const Frags& f, const uint2 (&mw)[Cfg::TM], int st) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mt = 0; mt < Cfg::TM; ++mt) {
       const uint32_t w = st ? mw[mt].y : mw[mt].x;
@@ -431,6 +435,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
       for (int nt = 0; nt < Cfg::TN; ++nt)
         acc[mt][nt] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(f.a[mt], f.b[nt], acc[mt][nt], idx, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // vmcnt wait: allow `stages` stages of this wave's direct loads in flight
@@ -551,7 +556,8 @@ hipError_t launch_spmm_nt(const uint16_t* A, const uint16_t* vals, const uint16_
   if (T == 0 || N == 0) return hipSuccess;
   constexpr int64_t kMaxBuf = (int64_t)1 << 31;   // buffer offsets are 32-bit
   const bool fast = K % 64 == 0 && K > 0 && T * K * 2 < kMaxBuf && N * K < kMaxBuf && T * N * 2 < ((int64_t)1 << 40);
-  if (fast) return launch_fast<256, 256, 128, 128>(A, vals, meta, T, N, K, out, s);
+  // 256 x 256 tiles, 8 waves (two per SIMD) of 128 features x 64 tokens
+  if (fast) return launch_fast<256, 256, 128, 64>(A, vals, meta, T, N, K, out, s);
   return launch_cfg<256, 128, 128, 64>(A, vals, meta, T, N, K, out, s);
 }
 
