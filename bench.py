@@ -5,7 +5,7 @@ tokens) run as the noisy re-search loop: at step s the weights are
 W_s = fp16(f32(W_{s-1}) + N(0, 1e-3)) (precomputed and resident in HBM before
 timing), and each step runs
 
-    search+compress(W1_s), search+compress(W2_s)        (sp24_search_compress)
+    search+compress(W1_s and W2_s, one launch)         (sp24_search_compress_batch)
     Y1  = X   W1s^T,  dX1 = dY1 W1s                     (sp24_spmm_fwd / _bwd_input)
     Y2  = H   W2s^T,  dX2 = dY2 W2s
 
@@ -110,8 +110,7 @@ def profile_only(args, sp24, torch, dev, cfg, F1, F2, W1s, W2s, X, dY1, H, dY2, 
         log(f"copy: {n} x 512 MiB")
         return
     for s in range(len(W1s)):
-        sp24.sp24_search_compress(W1s[s], out=F1)
-        sp24.sp24_search_compress(W2s[s], out=F2)
+        sp24.sp24_search_compress_batch([W1s[s], W2s[s]], outs=[F1, F2])
         if args.profile_kernel == "search_compress" and s + 1 >= n:
             break
     torch.cuda.synchronize()
@@ -176,8 +175,7 @@ def main():
             if ev is not None:
                 ev[i].record()
         mark(0)
-        sp24.sp24_search_compress(W1s[s], out=F1)
-        sp24.sp24_search_compress(W2s[s], out=F2)
+        sp24.sp24_search_compress_batch([W1s[s], W2s[s]], outs=[F1, F2])
         mark(1)
         sp24.sp24_spmm_fwd(X, F1["vals_row"], F1["meta_row"], f, d, Y=Y1)
         mark(2)
@@ -210,12 +208,17 @@ def main():
     ms_per_step = ms_total / args.steps
     log(f"timed {args.steps} steps: {ms_total:.3f} ms on events, {wall_ms:.3f} ms wall")
 
-    # per-kernel breakdown: the same steps again with events between the calls
-    seg = np.zeros(5)
+    # per-kernel breakdown: the same steps again with events between the
+    # calls, all enqueued before a single synchronisation so that host-side
+    # call overhead never sits between two events of an idle GPU
+    evs = []
     for s in range(args.warmup, nsteps):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         step(s, ev)
-        torch.cuda.synchronize()
+        evs.append(ev)
+    torch.cuda.synchronize()
+    seg = np.zeros(5)
+    for ev in evs:
         seg += [ev[i].elapsed_time(ev[i + 1]) for i in range(5)]
     seg /= args.steps
     sc_ms, gemm_ms = seg[0], seg[1:]

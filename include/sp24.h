@@ -113,6 +113,36 @@ int sp24_search_compress(const void* W, int64_t R, int64_t C, uint8_t* idx,
                          void* vals_col, uint16_t* meta_col, void* stream);
 
 /*
+ * One weight of a batched search + compression call.  The fields mean what
+ * the arguments of sp24_search_compress mean; idx and either (vals, meta)
+ * pair may be NULL, as there.
+ */
+typedef struct sp24_sc_job {
+  const void* W;
+  int64_t R;
+  int64_t C;
+  uint8_t* idx;
+  void* vals_row;
+  uint16_t* meta_row;
+  void* vals_col;
+  uint16_t* meta_col;
+} sp24_sc_job;
+
+#define SP24_MAX_BATCH 8
+
+/*
+ * sp24_search_compress for `count` weights (1..SP24_MAX_BATCH) in a single
+ * kernel launch [Alg.1, SW]: an FFN layer re-searches both of its weights
+ * every step, and one launch keeps the whole GPU streaming both.  `jobs` is a
+ * HOST array, read during the call only.  Every job is validated first; on
+ * any error nothing is launched and the first failing job's status is
+ * returned.  Results are identical to separate sp24_search_compress calls.
+ * Errors: NULL (jobs NULL, or a job as in sp24_search_compress), SHAPE (also
+ * count outside 1..SP24_MAX_BATCH), ALIGN, TOO_LARGE, LAUNCH.
+ */
+int sp24_search_compress_batch(const sp24_sc_job* jobs, int count, void* stream);
+
+/*
  * Forward 2:4 sparse GEMM  Y = X * Ws^T  [Abstract, SW].
  *
  *   X         in   fp16 [T, C] activations

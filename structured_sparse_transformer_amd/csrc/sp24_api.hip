@@ -35,8 +35,9 @@ int check_pair(const void* vals, const void* meta, bool& present) {
   return SP24_OK;
 }
 
-int compress_common(const void* W, const uint8_t* idx_in, uint8_t* idx_out, int64_t R, int64_t C, void* vals_row,
-                    uint16_t* meta_row, void* vals_col, uint16_t* meta_col, void* stream) {
+// Validates one search/compress job (shared by the single and batched calls).
+int check_compress(const void* W, const uint8_t* idx_in, uint8_t* idx_out, int64_t R, int64_t C, void* vals_row,
+                   uint16_t* meta_row, void* vals_col, uint16_t* meta_col) {
   int st = check_dims(R, C, 16);
   if (st != SP24_OK) return st;
   bool has_row = false, has_col = false;
@@ -46,6 +47,13 @@ int compress_common(const void* W, const uint8_t* idx_in, uint8_t* idx_out, int6
   if (R == 0 || C == 0) return SP24_OK;
   if (W == nullptr) return SP24_ERR_NULL;
   if (!aligned16(W) || (idx_in && !aligned16(idx_in)) || (idx_out && !aligned16(idx_out))) return SP24_ERR_ALIGN;
+  return SP24_OK;
+}
+
+int compress_common(const void* W, const uint8_t* idx_in, uint8_t* idx_out, int64_t R, int64_t C, void* vals_row,
+                    uint16_t* meta_row, void* vals_col, uint16_t* meta_col, void* stream) {
+  const int st = check_compress(W, idx_in, idx_out, R, C, vals_row, meta_row, vals_col, meta_col);
+  if (st != SP24_OK || R == 0 || C == 0) return st;
   return launch_status(sp24::launch_search_compress(
       static_cast<const uint16_t*>(W), R, C, idx_in, idx_out, static_cast<uint16_t*>(vals_row), meta_row,
       static_cast<uint16_t*>(vals_col), meta_col, as_stream(stream)));
@@ -87,6 +95,23 @@ int sp24_compress(const void* W, const uint8_t* idx, int64_t R, int64_t C, void*
 int sp24_search_compress(const void* W, int64_t R, int64_t C, uint8_t* idx, void* vals_row, uint16_t* meta_row,
                          void* vals_col, uint16_t* meta_col, void* stream) {
   return compress_common(W, nullptr, idx, R, C, vals_row, meta_row, vals_col, meta_col, stream);
+}
+
+int sp24_search_compress_batch(const sp24_sc_job* jobs, int count, void* stream) {
+  if (jobs == nullptr) return SP24_ERR_NULL;
+  if (count < 1 || count > SP24_MAX_BATCH || count > sp24::kMaxScJobs) return SP24_ERR_SHAPE;
+  sp24::ScJobs batch{};
+  for (int k = 0; k < count; ++k) {
+    const sp24_sc_job& j = jobs[k];
+    const int st = check_compress(j.W, nullptr, j.idx, j.R, j.C, j.vals_row, j.meta_row, j.vals_col, j.meta_col);
+    if (st != SP24_OK) return st;
+    if (j.R == 0 || j.C == 0) continue;
+    batch.j[batch.count++] = sp24::ScJob{static_cast<const uint16_t*>(j.W), j.R, j.C, nullptr, j.idx,
+                                         static_cast<uint16_t*>(j.vals_row), j.meta_row,
+                                         static_cast<uint16_t*>(j.vals_col), j.meta_col, 0, 0};
+  }
+  if (batch.count == 0) return SP24_OK;
+  return launch_status(sp24::launch_search_compress_jobs(batch, true, as_stream(stream)));
 }
 
 int sp24_spmm_fwd(const void* X, const void* vals_row, const uint16_t* meta_row, int64_t T, int64_t R, int64_t C,

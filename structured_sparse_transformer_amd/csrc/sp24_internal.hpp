@@ -8,6 +8,29 @@ namespace sp24 {
 // Mask search only: idx[R/4][C/4].  R, C multiples of 4.
 hipError_t launch_mask_search(const uint16_t* W, int64_t R, int64_t C, uint8_t* idx, hipStream_t s);
 
+// One weight of a (batched) search+compress launch.
+struct ScJob {
+  const uint16_t* W;
+  int64_t R, C;
+  const uint8_t* idx_in;     // given masks (compress only), or nullptr to search
+  uint8_t* idx_out;          // may be nullptr
+  uint16_t* vals_row;        // (vals_row, meta_row) may both be nullptr
+  uint16_t* meta_row;
+  uint16_t* vals_col;        // (vals_col, meta_col) may both be nullptr
+  uint16_t* meta_col;
+  int64_t tiles_c;           // filled in by the launcher
+  int64_t tile_begin;        // filled in by the launcher
+};
+constexpr int kMaxScJobs = 8;
+struct ScJobs {
+  ScJob j[kMaxScJobs];
+  int count;
+  int64_t total_tiles;
+};
+// Search (all jobs without idx_in) or compress with given masks (all jobs
+// with idx_in); R, C multiples of 16.
+hipError_t launch_search_compress_jobs(ScJobs jobs, bool search, hipStream_t s);
+
 // Compression with either the searched masks (idx_in == nullptr: search and,
 // if idx_out != nullptr, write idx) or given masks (idx_in != nullptr).
 // R, C multiples of 16.  Either (vals, meta) pair may be null.

@@ -187,7 +187,8 @@ __global__ __launch_bounds__(kSearchThreads) void mask_search_kernel(const uint1
 }
 
 // ---------------------------------------------------------------------------
-// search (or read idx) + compress, one 128x128 tile of W per workgroup
+// search (or read idx) + compress, one 128x128 tile of one weight per
+// workgroup; one launch may cover several weights (a job table)
 
 constexpr int kTile = 128;            // rows and columns of W per workgroup
 constexpr int kTB = kTile / 4;        // blocks per tile side (32)
@@ -222,9 +223,7 @@ constexpr SelTable build_sel_table() {
 __constant__ SelTable g_sel = build_sel_table();
 
 struct CompressSmem {
-  uint32_t row_sel[kNumPatterns][4];
-  uint32_t col_sel[kNumPatterns][4];
-  uint32_t nibs[kNumPatterns];
+  SelTable sel;
   uint32_t vals_row[kTile][kTB + 1];     // [row][group]: kept pair as one dword
   uint32_t vals_col[kTile][kTB + 1];     // [column][row group]
   uint8_t nib_row[kTile][kTB + 4];       // [row][group]: nibble
@@ -232,55 +231,76 @@ struct CompressSmem {
   uint8_t idx[kTB][kTB];
 };
 
-template <bool kSearch>
-__global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(
-    const uint16_t* __restrict__ W, int64_t R, int64_t C, const uint8_t* __restrict__ idx_in,
-    uint8_t* __restrict__ idx_out, uint16_t* __restrict__ vals_row, uint16_t* __restrict__ meta_row,
-    uint16_t* __restrict__ vals_col, uint16_t* __restrict__ meta_col, int64_t tiles_c, int64_t ntiles) {
-  __shared__ CompressSmem sm;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < kNumPatterns * 4; i += kCompressThreads) {
-    (&sm.row_sel[0][0])[i] = (&g_sel.row_sel[0][0])[i];
-    (&sm.col_sel[0][0])[i] = (&g_sel.col_sel[0][0])[i];
-  }
-  for (int i = tid; i < kNumPatterns; i += kCompressThreads) sm.nibs[i] = g_sel.nibs[i];
+// Tile geometry of one workgroup-tile of one job.  The job is copied by
+// value (selected with static indices), so the kernel-argument table never
+// needs an address and stays in scalar registers.
+struct TileRef {
+  ScJob jb;
+  int64_t r0, c0;
+  int rows, cols;
+};
 
-  // Consecutive workgroups are dealt round-robin to the 8 XCDs; remap so each
-  // XCD walks a contiguous run of tiles (neighbouring output lines then meet
-  // in the same L2).
-  const int64_t per_xcd = (ntiles + 7) / 8;
-  const int64_t lin = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (lin >= ntiles) return;
-  const int64_t ti = lin / tiles_c, tj = lin - ti * tiles_c;
-  const int64_t r0 = ti * kTile, c0 = tj * kTile;
-  const int rows = (int)min<int64_t>(kTile, R - r0), cols = (int)min<int64_t>(kTile, C - c0);
-  const int nbc_t = cols / 4, nbr_t = rows / 4;
-  __syncthreads();
+__device__ __forceinline__ TileRef tile_ref(const ScJobs& jobs, int64_t t) {
+  ScJob jb = jobs.j[0];
+#pragma unroll
+  for (int k = 1; k < kMaxScJobs; ++k)
+    if (k < jobs.count && t >= jobs.j[k].tile_begin) jb = jobs.j[k];
+  const int64_t u = t - jb.tile_begin;
+  const int64_t ti = u / jb.tiles_c, tj = u - ti * jb.tiles_c;
+  TileRef tr;
+  tr.jb = jb;
+  tr.r0 = ti * kTile;
+  tr.c0 = tj * kTile;
+  tr.rows = (int)min<int64_t>(kTile, jb.R - tr.r0);
+  tr.cols = (int)min<int64_t>(kTile, jb.C - tr.c0);
+  return tr;
+}
 
+// This thread's four blocks of one tile: rows 4*bi .. 4*bi+3 of block row
+// bi = tid/32 + 8q, columns 4*bj .. 4*bj+3.
+struct TileData {
+  uint32_t w[kBlocksPerThread][4][2];
+};
+
+__device__ __forceinline__ void load_tile(const TileRef& tr, int tid, TileData& d) {
   const int bj = tid % kTB;
 #pragma unroll
   for (int q = 0; q < kBlocksPerThread; ++q) {
     const int bi = tid / kTB + q * (kCompressThreads / kTB);
-    if (bi >= nbr_t || bj >= nbc_t) continue;
-    uint32_t w[4][2];
+    if (bi >= tr.rows / 4 || bj >= tr.cols / 4) continue;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint2 v = *reinterpret_cast<const uint2*>(W + (r0 + 4 * bi + r) * C + c0 + 4 * bj);
-      w[r][0] = v.x;
-      w[r][1] = v.y;
+      const uint2 v = *reinterpret_cast<const uint2*>(tr.jb.W + (tr.r0 + 4 * bi + r) * tr.jb.C + tr.c0 + 4 * bj);
+      d.w[q][r][0] = v.x;
+      d.w[q][r][1] = v.y;
     }
+  }
+}
+
+// Search (or read the given masks), then stage both compressed forms of the
+// tile in LDS.
+template <bool kSearch>
+__device__ __forceinline__ void stage_tile(const TileRef& tr, int tid, const TileData& d, CompressSmem& sm) {
+  const ScJob& jb = tr.jb;
+  const int bj = tid % kTB;
+  const int nbc_t = tr.cols / 4, nbr_t = tr.rows / 4;
+#pragma unroll
+  for (int q = 0; q < kBlocksPerThread; ++q) {
+    const int bi = tid / kTB + q * (kCompressThreads / kTB);
+    if (bi >= nbr_t || bj >= nbc_t) continue;
+    const uint32_t(&w)[4][2] = d.w[q];
     int p;
     if constexpr (kSearch) {
       p = search_block(load_block(w));
     } else {
-      p = idx_in[(r0 / 4 + bi) * (C / 4) + c0 / 4 + bj];
+      p = jb.idx_in[(tr.r0 / 4 + bi) * (jb.C / 4) + tr.c0 / 4 + bj];
       p = p < kNumPatterns ? p : 0;
     }
     sm.idx[bi][bj] = (uint8_t)p;
-    const uint32_t nibs = sm.nibs[p];
+    const uint32_t nibs = sm.sel.nibs[p];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sm.vals_row[4 * bi + r][bj] = __builtin_amdgcn_perm(w[r][1], w[r][0], sm.row_sel[p][r]);
+      sm.vals_row[4 * bi + r][bj] = __builtin_amdgcn_perm(w[r][1], w[r][0], sm.sel.row_sel[p][r]);
       sm.nib_row[4 * bi + r][bj] = (uint8_t)((nibs >> (4 * r)) & 0xF);
     }
 #pragma unroll
@@ -288,58 +308,89 @@ __global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(
       const uint32_t hsel = (c & 1) ? 0x07060302u : 0x05040100u;
       const uint32_t top = __builtin_amdgcn_perm(w[1][c >> 1], w[0][c >> 1], hsel);  // rows 0,1 of column c
       const uint32_t bot = __builtin_amdgcn_perm(w[3][c >> 1], w[2][c >> 1], hsel);  // rows 2,3
-      sm.vals_col[4 * bj + c][bi] = __builtin_amdgcn_perm(bot, top, sm.col_sel[p][c]);
+      sm.vals_col[4 * bj + c][bi] = __builtin_amdgcn_perm(bot, top, sm.sel.col_sel[p][c]);
       sm.nib_col[4 * bj + c][bi] = (uint8_t)((nibs >> (16 + 4 * c)) & 0xF);
     }
   }
-  __syncthreads();
+}
 
-  // idx: rows of nbc_t bytes, written one dword (4 blocks) at a time
-  if (idx_out) {
+// Coalesced stores of a staged tile: 16-byte row and column segments.
+__device__ __forceinline__ void write_tile(const TileRef& tr, int tid, const CompressSmem& sm) {
+  const ScJob& jb = tr.jb;
+  const int64_t R = jb.R, C = jb.C, r0 = tr.r0, c0 = tr.c0;
+  const int rows = tr.rows, cols = tr.cols, nbc_t = cols / 4, nbr_t = rows / 4;
+  if (jb.idx_out) {
     for (int i = tid; i < nbr_t * (nbc_t / 4); i += kCompressThreads) {
       const int bi = i / (nbc_t / 4), b4 = i - bi * (nbc_t / 4);
       const uint32_t v = (uint32_t)sm.idx[bi][4 * b4] | (uint32_t)sm.idx[bi][4 * b4 + 1] << 8 |
                          (uint32_t)sm.idx[bi][4 * b4 + 2] << 16 | (uint32_t)sm.idx[bi][4 * b4 + 3] << 24;
-      *reinterpret_cast<uint32_t*>(idx_out + (r0 / 4 + bi) * (C / 4) + c0 / 4 + 4 * b4) = v;
+      *reinterpret_cast<uint32_t*>(jb.idx_out + (r0 / 4 + bi) * (C / 4) + c0 / 4 + 4 * b4) = v;
     }
   }
-  // row form: vals_row[r][c/2], 4 groups (16 bytes) per store
-  if (vals_row) {
+  if (jb.vals_row) {
     const int q4 = nbc_t / 4;
     for (int i = tid; i < rows * q4; i += kCompressThreads) {
       const int r = i / q4, g4 = i - r * q4;
-      uint4 v;
-      v.x = sm.vals_row[r][4 * g4 + 0];
-      v.y = sm.vals_row[r][4 * g4 + 1];
-      v.z = sm.vals_row[r][4 * g4 + 2];
-      v.w = sm.vals_row[r][4 * g4 + 3];
-      *reinterpret_cast<uint4*>(vals_row + (r0 + r) * (C / 2) + c0 / 2 + 8 * g4) = v;
-    }
-    for (int i = tid; i < rows * q4; i += kCompressThreads) {
-      const int r = i / q4, g4 = i - r * q4;
+      const uint4 v = make_uint4(sm.vals_row[r][4 * g4 + 0], sm.vals_row[r][4 * g4 + 1], sm.vals_row[r][4 * g4 + 2],
+                                 sm.vals_row[r][4 * g4 + 3]);
+      *reinterpret_cast<uint4*>(jb.vals_row + (r0 + r) * (C / 2) + c0 / 2 + 8 * g4) = v;
       const uint8_t* n = &sm.nib_row[r][4 * g4];
-      meta_row[(r0 + r) * (C / 16) + c0 / 16 + g4] =
-          (uint16_t)(n[0] | n[1] << 4 | n[2] << 8 | n[3] << 12);
+      jb.meta_row[(r0 + r) * (C / 16) + c0 / 16 + g4] = (uint16_t)(n[0] | n[1] << 4 | n[2] << 8 | n[3] << 12);
     }
   }
-  // column form: vals_col[c][r/2]
-  if (vals_col) {
+  if (jb.vals_col) {
     const int q4 = nbr_t / 4;
     for (int i = tid; i < cols * q4; i += kCompressThreads) {
       const int c = i / q4, g4 = i - c * q4;
-      uint4 v;
-      v.x = sm.vals_col[c][4 * g4 + 0];
-      v.y = sm.vals_col[c][4 * g4 + 1];
-      v.z = sm.vals_col[c][4 * g4 + 2];
-      v.w = sm.vals_col[c][4 * g4 + 3];
-      *reinterpret_cast<uint4*>(vals_col + (c0 + c) * (R / 2) + r0 / 2 + 8 * g4) = v;
-    }
-    for (int i = tid; i < cols * q4; i += kCompressThreads) {
-      const int c = i / q4, g4 = i - c * q4;
+      const uint4 v = make_uint4(sm.vals_col[c][4 * g4 + 0], sm.vals_col[c][4 * g4 + 1], sm.vals_col[c][4 * g4 + 2],
+                                 sm.vals_col[c][4 * g4 + 3]);
+      *reinterpret_cast<uint4*>(jb.vals_col + (c0 + c) * (R / 2) + r0 / 2 + 8 * g4) = v;
       const uint8_t* n = &sm.nib_col[c][4 * g4];
-      meta_col[(c0 + c) * (R / 16) + r0 / 16 + g4] =
-          (uint16_t)(n[0] | n[1] << 4 | n[2] << 8 | n[3] << 12);
+      jb.meta_col[(c0 + c) * (R / 16) + r0 / 16 + g4] = (uint16_t)(n[0] | n[1] << 4 | n[2] << 8 | n[3] << 12);
     }
+  }
+}
+
+// Each workgroup handles kTilesPerWg tiles.  All of their loads are issued
+// first; tile k+1 is searched while the global stores of tile k drain, so
+// loading, searching and storing overlap within the workgroup instead of
+// running as three GPU-wide phases.
+constexpr int kTilesPerWg = 2;
+
+template <bool kSearch>
+__global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(ScJobs jobs) {
+  __shared__ CompressSmem sm;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < (int)(sizeof(SelTable) / 4); i += kCompressThreads)
+    reinterpret_cast<uint32_t*>(&sm.sel)[i] = reinterpret_cast<const uint32_t*>(&g_sel)[i];
+
+  // Workgroups are dealt round-robin to the 8 XCDs; remap so each XCD walks a
+  // contiguous run of tiles (neighbouring output lines then meet in its L2).
+  const int64_t ngroups = (jobs.total_tiles + kTilesPerWg - 1) / kTilesPerWg;
+  const int64_t per_xcd = (ngroups + 7) / 8;
+  const int64_t grp = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (grp >= ngroups) return;
+
+  TileRef tr[kTilesPerWg];
+  TileData td[kTilesPerWg];
+  bool have[kTilesPerWg];
+#pragma unroll
+  for (int k = 0; k < kTilesPerWg; ++k) {
+    const int64_t t = grp * kTilesPerWg + k;
+    have[k] = t < jobs.total_tiles;
+    if (have[k]) {
+      tr[k] = tile_ref(jobs, t);
+      load_tile(tr[k], tid, td[k]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kTilesPerWg; ++k) {
+    if (!have[k]) continue;
+    stage_tile<kSearch>(tr[k], tid, td[k], sm);
+    __syncthreads();
+    write_tile(tr[k], tid, sm);
+    __syncthreads();    // the staging buffer is read out before the next tile overwrites it
   }
 }
 
@@ -354,20 +405,33 @@ hipError_t launch_mask_search(const uint16_t* W, int64_t R, int64_t C, uint8_t* 
   return hipGetLastError();
 }
 
+hipError_t launch_search_compress_jobs(ScJobs jobs, bool search, hipStream_t s) {
+  int64_t total = 0;
+  for (int k = 0; k < jobs.count; ++k) {
+    ScJob& jb = jobs.j[k];
+    jb.tiles_c = (jb.C + kTile - 1) / kTile;
+    jb.tile_begin = total;
+    total += ((jb.R + kTile - 1) / kTile) * jb.tiles_c;
+  }
+  jobs.total_tiles = total;
+  if (total == 0) return hipSuccess;
+  const int64_t groups = (total + kTilesPerWg - 1) / kTilesPerWg;
+  const int64_t grid = ((groups + 7) / 8) * 8;
+  if (search)
+    hipLaunchKernelGGL(search_compress_kernel<true>, dim3((unsigned)grid), dim3(kCompressThreads), 0, s, jobs);
+  else
+    hipLaunchKernelGGL(search_compress_kernel<false>, dim3((unsigned)grid), dim3(kCompressThreads), 0, s, jobs);
+  return hipGetLastError();
+}
+
 hipError_t launch_search_compress(const uint16_t* W, int64_t R, int64_t C, const uint8_t* idx_in,
                                   uint8_t* idx_out, uint16_t* vals_row, uint16_t* meta_row,
                                   uint16_t* vals_col, uint16_t* meta_col, hipStream_t s) {
   if (R == 0 || C == 0) return hipSuccess;
-  const int64_t tiles_r = (R + kTile - 1) / kTile, tiles_c = (C + kTile - 1) / kTile;
-  const int64_t ntiles = tiles_r * tiles_c;
-  const int64_t grid = ((ntiles + 7) / 8) * 8;
-  if (idx_in)
-    hipLaunchKernelGGL(search_compress_kernel<false>, dim3((unsigned)grid), dim3(kCompressThreads), 0, s, W, R,
-                       C, idx_in, nullptr, vals_row, meta_row, vals_col, meta_col, tiles_c, ntiles);
-  else
-    hipLaunchKernelGGL(search_compress_kernel<true>, dim3((unsigned)grid), dim3(kCompressThreads), 0, s, W, R, C,
-                       nullptr, idx_out, vals_row, meta_row, vals_col, meta_col, tiles_c, ntiles);
-  return hipGetLastError();
+  ScJobs jobs{};
+  jobs.count = 1;
+  jobs.j[0] = ScJob{W, R, C, idx_in, idx_out, vals_row, meta_row, vals_col, meta_col, 0, 0};
+  return launch_search_compress_jobs(jobs, idx_in == nullptr, s);
 }
 
 }  // namespace sp24

@@ -369,6 +369,18 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
     off_m[i] = r * Km * 2 + (lane % 2) * 4;
   }
 
+  // one of this wave's LOADS direct loads of stage kt (j in [0, LOADS))
+  auto issue_one = [&](int j, int kt, unsigned char* sb, unsigned char* bb, unsigned char* mb) {
+    if (j < Cfg::S_LOADS) {
+      dma_b128(rs, lds_addr(sb) + (wave * Cfg::S_LOADS + j) * 1024, off_s[j] + kt * 64);
+    } else if (j < Cfg::S_LOADS + Cfg::B_LOADS) {
+      const int i = j - Cfg::S_LOADS;
+      dma_b128(rb, lds_addr(bb) + (wave * Cfg::B_LOADS + i) * 1024, off_b[i] + kt * 128);
+    } else {
+      const int i = j - Cfg::S_LOADS - Cfg::B_LOADS;
+      dma_b32(rm, lds_addr(mb) + (wave * Cfg::M_LOADS + i) * 256, off_m[i] + kt * 8);
+    }
+  };
   auto issue = [&](int kt, unsigned char* sb, unsigned char* bb, unsigned char* mb) {
     const int ds = kt * 64, db = kt * 128, dm = kt * 8;
 #pragma unroll
@@ -422,19 +434,30 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
 #pragma unroll
     for (int mt = 0; mt < Cfg::TM; ++mt) mw[mt] = *reinterpret_cast<const uint2*>(mb + rd_m + mt * 32 * 8);
   };
-  // Two waves share each SIMD; raising the priority of the wave that is in
-  // its MFMA block lets it issue back to back while the other wave issues its
-  // LDS reads and direct loads in between.
-  auto mfmas = [&](const Frags& f, const uint2 (&mw)[Cfg::TM], int st) {
+  // The SMFMACs of one K32 step.  Two waves share each SIMD; raising the
+  // priority of the wave in its MFMA block lets it issue back to back while
+  // the other wave issues its LDS reads and direct loads in between.  When
+  // kt_load >= 0, this wave's direct loads of stage kt_load go out one after
+  // each SMFMAC rather than in a burst, so the texture unit drains steadily
+  // and no wave stalls long on its in-order vector-memory issue.
+  auto mfmas = [&](const Frags& f, const uint2 (&mw)[Cfg::TM], int st, int kt_load, unsigned char* sb,
+                   unsigned char* bb, unsigned char* mb) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mt = 0; mt < Cfg::TM; ++mt) {
       const uint32_t w = st ? mw[mt].y : mw[mt].x;
       const int idx = (int)(g ? (w >> 16) : w);
 #pragma unroll
-      for (int nt = 0; nt < Cfg::TN; ++nt)
+      for (int nt = 0; nt < Cfg::TN; ++nt) {
         acc[mt][nt] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(f.a[mt], f.b[nt], acc[mt][nt], idx, 0, 0);
+        const int j = mt * Cfg::TN + nt;
+        if (j < Cfg::LOADS && kt_load >= 0) issue_one(j, kt_load, sb, bb, mb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+#pragma unroll
+    for (int j = Cfg::TM * Cfg::TN; j < Cfg::LOADS; ++j)
+      if (kt_load >= 0) issue_one(j, kt_load, sb, bb, mb);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -477,20 +500,20 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
   auto stage = [&](int kt, int cur, int nxt) {
     load_frags(s_buf[cur], b_buf[cur], 1, f1);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(f0, mw, 0);
+    mfmas(f0, mw, 0, -1, nullptr, nullptr, nullptr);
     __builtin_amdgcn_sched_barrier(0);
     wait_loads(kt + 2 < nk ? 1 : 0);
     // lgkmcnt(0): this wave's reads of slot kt % 3 are complete before the
     // barrier lets stage kt+3 overwrite it (vmcnt 63, expcnt 7 = no wait)
     __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
     __builtin_amdgcn_s_barrier();
-    if (kt + 3 < nk) issue(kt + 3, s_buf[cur], b_buf[cur], m_buf[cur]);
     if (kt + 1 < nk) {
       load_meta(m_buf[nxt], mw_next);
       load_frags(s_buf[nxt], b_buf[nxt], 0, f0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(f1, mw, 1);
+    // stage kt+3 goes into slot kt % 3, free since the barrier
+    mfmas(f1, mw, 1, kt + 3 < nk ? kt + 3 : -1, s_buf[cur], b_buf[cur], m_buf[cur]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mt = 0; mt < Cfg::TM; ++mt) mw[mt] = mw_next[mt];

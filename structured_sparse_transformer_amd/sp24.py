@@ -24,8 +24,16 @@ LIB_PATH = os.path.join(_HERE, "libsp24.so")
 SP24_OK = 0
 STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_LAUNCH",
                 5: "ERR_UNSUPPORTED", 6: "ERR_TOO_LARGE"}
-EXPORTS = ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_spmm_fwd",
-           "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table", "sp24_abi_version")
+EXPORTS = ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
+           "sp24_spmm_fwd", "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table", "sp24_abi_version")
+MAX_BATCH = 8
+
+
+class ScJob(ctypes.Structure):
+    """Mirror of sp24_sc_job (include/sp24.h)."""
+    _fields_ = [("W", ctypes.c_void_p), ("R", ctypes.c_int64), ("C", ctypes.c_int64), ("idx", ctypes.c_void_p),
+                ("vals_row", ctypes.c_void_p), ("meta_row", ctypes.c_void_p),
+                ("vals_col", ctypes.c_void_p), ("meta_col", ctypes.c_void_p)]
 
 
 class Sp24Error(RuntimeError):
@@ -49,6 +57,7 @@ def lib() -> ctypes.CDLL:
             "sp24_mask_search": [p, i64, i64, p, p],
             "sp24_compress": [p, p, i64, i64, p, p, p, p, p],
             "sp24_search_compress": [p, i64, i64, p, p, p, p, p, p],
+            "sp24_search_compress_batch": [p, i32, p],
             "sp24_spmm_fwd": [p, p, p, i64, i64, i64, p, p],
             "sp24_spmm_bwd_input": [p, p, p, i64, i64, i64, p, p],
             "sp24_status_str": [i32],
@@ -138,6 +147,26 @@ def sp24_search_compress(W, want_idx=True, row=True, col=True, out=None, stream=
         _ptr(W), R, C, _ptr(o.get("idx")), _ptr(o.get("vals_row")), _ptr(o.get("meta_row")),
         _ptr(o.get("vals_col")), _ptr(o.get("meta_col")), _stream(stream)))
     return o
+
+
+def sp24_search_compress_batch(Ws, outs=None, want_idx=True, row=True, col=True, stream=None):
+    """sp24_search_compress for several weights in one launch; returns one dict per weight."""
+    if not 1 <= len(Ws) <= MAX_BATCH:
+        raise ValueError(f"between 1 and {MAX_BATCH} weights per batch")
+    outs = list(outs) if outs is not None else [None] * len(Ws)
+    res, jobs = [], (ScJob * len(Ws))()
+    for k, W in enumerate(Ws):
+        R, C = _w(W)
+        o = _forms(R, C, W.device, row, col, outs[k])
+        if want_idx:
+            o["idx"] = _out(o.get("idx"), (R // 4, C // 4), torch.uint8, W.device)
+        ptr = lambda t: _ptr(t).value if t is not None and t.numel() else None  # noqa: E731
+        jobs[k] = ScJob(ptr(W), R, C, ptr(o.get("idx")), ptr(o.get("vals_row")), ptr(o.get("meta_row")),
+                        ptr(o.get("vals_col")), ptr(o.get("meta_col")))
+        res.append(o)
+    _check("sp24_search_compress_batch",
+           lib().sp24_search_compress_batch(ctypes.cast(jobs, ctypes.c_void_p), len(Ws), _stream(stream)))
+    return res
 
 
 def sp24_spmm_fwd(X, vals_row, meta_row, R, C, Y=None, stream=None):

@@ -127,3 +127,23 @@ def test_binding_refuses_cpu_tensors(L):
     from structured_sparse_transformer_amd import sp24
     with pytest.raises(ValueError):
         sp24.sp24_mask_search(torch.zeros(8, 8, dtype=torch.float16))
+
+
+def test_search_compress_batch_validation(L):
+    from structured_sparse_transformer_amd.sp24 import ScJob
+    f = L.sp24_search_compress_batch
+    ok = ScJob(0x1000, 16, 16, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000)
+    arr = (ScJob * 9)(*([ok] * 9))
+    p = ctypes.cast(arr, ctypes.c_void_p)
+    assert f(None, 1, NUL) == 1
+    assert f(p, 0, NUL) == 2
+    assert f(p, 9, NUL) == 2
+    bad_shape = (ScJob * 2)(ok, ScJob(0x1000, 16, 20, None, 0x3000, 0x4000, None, None))
+    assert f(ctypes.cast(bad_shape, ctypes.c_void_p), 2, NUL) == 2      # second job checked before launching
+    half = (ScJob * 1)(ScJob(0x1000, 16, 16, None, 0x3000, None, None, None))
+    assert f(ctypes.cast(half, ctypes.c_void_p), 1, NUL) == 1
+    mis = (ScJob * 1)(ScJob(0x1008, 16, 16, None, 0x3000, 0x4000, None, None))
+    assert f(ctypes.cast(mis, ctypes.c_void_p), 1, NUL) == 3
+    empty = (ScJob * 2)(ScJob(None, 0, 16, None, 0x3000, 0x4000, None, None),
+                        ScJob(None, 16, 0, None, 0x3000, 0x4000, None, None))
+    assert f(ctypes.cast(empty, ctypes.c_void_p), 2, NUL) == 0         # all empty: nothing launched

@@ -176,6 +176,27 @@ def test_compress_given_idx(sp, shape):
     assert_forms_equal(o, want)
 
 
+def test_search_compress_batch(sp):
+    # several weights, mixed shapes (with row and column tails), one launch
+    shapes = [(144, 272), (272, 144), (16, 16), (512, 128), (64, 1040)]
+    Ws = [(np.random.default_rng(40 + k).standard_normal(sh) * 0.02).astype(np.float16) for k, sh in enumerate(shapes)]
+    Ws[1] = wide_range_matrix(45, 272, 144)            # exact-order path inside a batch
+    outs = sp.sp24_search_compress_batch([dev(W) for W in Ws])
+    for W, o in zip(Ws, outs):
+        idx = O.mask_search(W)
+        assert_idx_equal(o["idx"], idx)
+        assert_forms_equal(o, O.compress(W, idx))
+
+
+def test_search_compress_batch_ffn_pair(sp):
+    w1, w2 = WL.ffn_weights(WL.GPT2_1P5B)
+    o1, o2 = sp.sp24_search_compress_batch([dev(w1), dev(w2)])
+    for W, o in ((w1, o1), (w2, o2)):
+        idx = O.mask_search(W)
+        assert_idx_equal(o["idx"], idx)
+        assert_forms_equal(o, O.compress(W, idx))
+
+
 def test_compress_random_indices(sp):
     # any index 0..89 per block, not only searched ones
     W = WL.normal_f16(77, 1, (64, 96), 1.0)
