@@ -308,7 +308,7 @@ struct FastCfg {
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ vals, const uint16_t* __restrict__ meta,
-    int64_t T, int64_t N, int64_t K, uint16_t* __restrict__ out, int tiles_m, int tiles_n) {
+    int64_t T, int64_t N, int64_t K, uint16_t* __restrict__ out, int64_t ldo, int tiles_m, int tiles_n) {
   using Cfg = FastCfg<BM, BN, WM, WN>;
   // one LDS block: 3 S slots, 3 B slots, 3 meta slots (the epilogue reuses
   // the start of it to stage the output tile)
@@ -556,20 +556,33 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
     const uint4 v = *reinterpret_cast<const uint4*>(stage_base + t * 256 + ((c ^ (t & 15)) * 16));
     const int64_t n = n0 + wn * WN + t;
     const int64_t m = m0 + wm * WM + c * 8;
-    if (n < T && m < N) *reinterpret_cast<uint4*>(out + n * N + m) = v;
+    if (n < T && m < N) *reinterpret_cast<uint4*>(out + n * ldo + m) = v;
   }
 }
 
+// out[T][ldo] columns [0, N) = A * S^T for the N feature rows of S given.
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_fast(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T, int64_t N,
-                       int64_t K, uint16_t* out, hipStream_t s) {
+                       int64_t K, uint16_t* out, int64_t ldo, hipStream_t s) {
   using Cfg = FastCfg<BM, BN, WM, WN>;
   const int tiles_m = (int)((N + BM - 1) / BM), tiles_n = (int)((T + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
   const int grid = ((ntiles + 7) / 8) * 8;
   hipLaunchKernelGGL((spmm_nt_fast_kernel<BM, BN, WM, WN>), dim3(grid), dim3(Cfg::THREADS), 0, s, A, vals, meta, T, N,
-                     K, out, tiles_m, tiles_n);
+                     K, out, ldo, tiles_m, tiles_n);
   return hipGetLastError();
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -579,8 +592,23 @@ hipError_t launch_spmm_nt(const uint16_t* A, const uint16_t* vals, const uint16_
   if (T == 0 || N == 0) return hipSuccess;
   constexpr int64_t kMaxBuf = (int64_t)1 << 31;   // buffer offsets are 32-bit
   const bool fast = K % 64 == 0 && K > 0 && T * K * 2 < kMaxBuf && N * K < kMaxBuf && T * N * 2 < ((int64_t)1 << 40);
-  // 256 x 256 tiles, 8 waves (two per SIMD) of 128 features x 64 tokens
-  if (fast) return launch_fast<256, 256, 128, 64>(A, vals, meta, T, N, K, out, s);
+  if (fast) {
+    // 256 x 256 tiles, 8 waves (two per SIMD) of 128 features x 64 tokens.
+    // When the tile count leaves a last, partly filled round of workgroups,
+    // the leading feature tiles that fill whole rounds run first and the last
+    // 256-feature strip runs as 256 x 64 tiles, four times as many and a
+    // quarter of the work each, so the tail takes a fraction of a round.
+    const int64_t cus = device_cu_count();
+    const int64_t tiles_n = (T + 255) / 256, tiles_m = (N + 255) / 256;
+    if (tiles_m > 1 && (tiles_m * tiles_n) % cus != 0 && ((tiles_m - 1) * tiles_n) % cus == 0 &&
+        (T + 63) / 64 <= cus) {
+      const int64_t n1 = (tiles_m - 1) * 256;
+      hipError_t e = launch_fast<256, 256, 128, 64>(A, vals, meta, T, n1, K, out, N, s);
+      if (e != hipSuccess) return e;
+      return launch_fast<256, 64, 128, 32>(A, vals + n1 * (K / 2), meta + n1 * (K / 16), T, N - n1, K, out + n1, N, s);
+    }
+    return launch_fast<256, 256, 128, 64>(A, vals, meta, T, N, K, out, N, s);
+  }
   return launch_cfg<256, 128, 128, 64>(A, vals, meta, T, N, K, out, s);
 }
 
