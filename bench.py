@@ -291,7 +291,7 @@ def main():
         "search_compress_us_both_weights": round(sc_ms * 1e3, 2),
         "gemm_TFLOPs_dense_equiv": {n: round(v, 1) for (n, *_), v in zip(gemm_shapes, gemm_dense_tflops)},
         "gemm_us": {n: round(ms * 1e3, 1) for (n, *_), ms in zip(gemm_shapes, gemm_ms)},
-        "roofline": {"kernel": "spmm_nt_kernel", "bound": "mfma", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "spmm_nt (one sp24_spmm_* call)", "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic,
                      "note": "executed non-zero flops T*N*K per launch (half the dense-equivalent 2*T*N*K) over the "
