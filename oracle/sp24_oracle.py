@@ -45,6 +45,9 @@ What the method computes, and the readings taken where the pages are silent:
    ``dX = dY Ws`` (input gradient), with Ws the pruned weight.  The plain
    definition is the dense product with the decoded pruned matrix, computed
    here in float64.
+4. Flip rate [HZ24 abstract] (no formula on the pages): the number of mask
+   entries whose kept/pruned state differs between two consecutive masks,
+   over the number of entries.
 """
 from __future__ import annotations
 
@@ -218,6 +221,27 @@ def spmm_bwd_input(dY: np.ndarray, vals_col, meta_col, R: int, C: int) -> np.nda
     """float64 [T, C]: dX = dY Ws with Ws decoded from the column form."""
     Ws = decode_col_form(vals_col, meta_col, R, C).astype(np.float64)
     return np.asarray(dY, dtype=np.float64) @ Ws
+
+
+def flip_count(idx_prev: np.ndarray, idx_new: np.ndarray) -> int:
+    """Number of mask entries that differ between two searched masks.
+
+    [HZ24 abstract] defines a "flip rate" to monitor the stability of 2:4
+    training but prints no formula.  Reading: the entries whose kept/pruned
+    state changed between two consecutive masks, counted over the whole
+    matrix; ``flip_rate`` divides by the number of entries.
+    """
+    if idx_prev.shape != idx_new.shape:
+        raise ValueError("mask shapes differ")
+    masks = pattern_masks().astype(np.int64)
+    diff = masks[idx_prev.astype(np.int64)] != masks[idx_new.astype(np.int64)]
+    return int(diff.sum())
+
+
+def flip_rate(idx_prev: np.ndarray, idx_new: np.ndarray) -> float:
+    """flip_count divided by the number of matrix entries (16 per block)."""
+    n = 16 * idx_new.size
+    return flip_count(idx_prev, idx_new) / n if n else 0.0
 
 
 def gemm_errors(out: np.ndarray, ref: np.ndarray) -> tuple:

@@ -344,3 +344,37 @@ def test_gemm_error_metric():
     out = ref + np.array([[0.0, 0.04], [0.0, -0.02]])
     mr, ma = O.gemm_errors(out, ref)
     assert abs(mr - 0.01) < 1e-15 and abs(ma - 0.015) < 1e-15
+
+
+# ----------------------------------------------------------------------------
+# flip rate
+def test_flip_count_pins():
+    # identical masks do not flip; pattern 0 (1100 1100 0011 0011) and 89
+    # (0011 0011 1100 1100) differ everywhere; patterns 0 and 1 (row 1 keeps
+    # {0,2} instead of {0,1}, row 2 keeps {1,3} instead of {2,3}) differ in 4
+    a = np.zeros((2, 3), np.uint8)
+    assert O.flip_count(a, a) == 0
+    b = a.copy()
+    b[0, 0] = 89
+    assert O.flip_count(a, b) == 16
+    b[1, 2] = 1
+    assert O.flip_count(a, b) == 20
+    assert O.flip_rate(a, b) == 20 / 96
+
+
+def test_flip_count_matches_dense_masks():
+    rng = np.random.default_rng(30)
+    W = (rng.standard_normal((64, 96)) * 0.02).astype(np.float16)
+    W2 = (W.astype(np.float32) + rng.standard_normal(W.shape).astype(np.float32) * 1e-2).astype(np.float16)
+    i1, i2 = O.mask_search(W), O.mask_search(W2)
+    dense = int((O.idx_to_mask(i1) != O.idx_to_mask(i2)).sum())
+    assert O.flip_count(i1, i2) == dense == O.flip_count(i2, i1)
+    # flips within a block come in pairs (a row keeps exactly two entries)
+    per_block = (O.idx_to_mask(i1) != O.idx_to_mask(i2)).reshape(16, 4, 24, 4).sum(axis=(1, 3))
+    assert (per_block % 2 == 0).all() and per_block.max() <= 16
+    # all 90 x 90 pattern pairs against explicit 4x4 comparisons
+    masks = O.pattern_masks()
+    p, q = np.meshgrid(np.arange(90), np.arange(90), indexing="ij")
+    got = [O.flip_count(np.array([[x]], np.uint8), np.array([[y]], np.uint8)) for x, y in zip(p.ravel(), q.ravel())]
+    want = [int((masks[x] != masks[y]).sum()) for x, y in zip(p.ravel(), q.ravel())]
+    assert got == want
