@@ -6,14 +6,17 @@ W_s = fp16(f32(W_{s-1}) + N(0, 1e-3)) (precomputed and resident in HBM before
 timing), and each step runs
 
     search+compress(W1_s and W2_s, one launch)         (sp24_search_compress_batch)
+        with the flip count of each weight fused in: each weight's index
+        buffer is updated in place and the entries that changed are counted
     Y1  = X   W1s^T,  dX1 = dY1 W1s                     (sp24_spmm_fwd / _bwd_input)
     Y2  = H   W2s^T,  dX2 = dY2 W2s
 
 Prints one JSON line.  ``value`` is dense-equivalent GEMM TFLOP/s over the
 whole step (2*T*N*K summed over the four GEMMs, divided by the wall time of
-the step including both search+compress calls).  The line also carries the
-search+compress GB/s (4.3125 algorithmic bytes per weight element), the GEMM
-kernel's roofline fraction and the CPU oracle baseline.
+the step including the search+compress launch).  The line also carries the
+search+compress GB/s (4.375 algorithmic bytes per weight element), the GEMM
+kernel's roofline fraction, the per-step flip rates and the CPU oracle
+baseline.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
 """
@@ -35,7 +38,7 @@ from structured_sparse_transformer_amd import workloads as WL  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0      # dense fp16 matrix-core peak of MI355X
-SC_BYTES_PER_ELEM = 4.3125          # read W 2, idx 1/16, two 2:4 forms 2 x (1 + 1/8)
+SC_BYTES_PER_ELEM = 4.375           # read W 2 and previous idx 1/16; write idx 1/16, two 2:4 forms 2 x (1 + 1/8)
 COUNTERS = os.path.join(ROOT, "profiles", "spmm_nt_gpt2-1.5b_counters.json")
 GEMM_SRC = os.path.join(ROOT, "structured_sparse_transformer_amd", "csrc", "sp24_spmm.hip")
 
@@ -68,10 +71,15 @@ def cpu_baseline(cfg, inp, sample_tokens: int):
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         blas_threads = os.cpu_count() or 1
+    # stand-in previous masks (seeded indices): the count's cost does not
+    # depend on their values
+    prev = [WL.random_idx(cfg.seed, 200 + k, (w.shape[0] // 4, w.shape[1] // 4))
+            for k, w in enumerate((inp.w1, inp.w2))]
     t0 = time.perf_counter()
     forms = []
-    for W in (inp.w1, inp.w2):
+    for W, p in zip((inp.w1, inp.w2), prev):
         idx = O.mask_search(W)
+        O.flip_count(p, idx)
         forms.append(O.compress(W, idx))
     t_sc = time.perf_counter() - t0
     Ts = sample_tokens
@@ -89,14 +97,15 @@ def cpu_baseline(cfg, inp, sample_tokens: int):
         "unit": "TFLOP/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": (f"mask search + compress of W1 and W2 in full (NumPy, single thread, {t_sc:.1f} s) and the "
+        "sample": (f"mask search + flip count + compress of W1 and W2 in full (NumPy, single thread, "
+                   f"{t_sc:.1f} s) and the "
                    f"four float64 GEMMs on the first {Ts} of {cfg.tokens} tokens (BLAS, {blas_threads} threads, "
                    f"{t_gemm:.1f} s), GEMM time scaled linearly to all tokens; one step of the 1.5B loop"),
         "search_compress_GBps": round(SC_BYTES_PER_ELEM * (inp.w1.size + inp.w2.size) / t_sc / 1e9, 4),
     }
 
 
-def profile_only(args, sp24, torch, dev, cfg, F1, F2, W1s, W2s, X, dY1, H, dY2, Y1, dX1, Y2, dX2):
+def profile_only(args, sp24, torch, dev, cfg, F1, F2, FL, W1s, W2s, X, dY1, H, dY2, Y1, dX1, Y2, dX2):
     """Runs one kernel family alone so that counter passes see only it."""
     d, f = cfg.d, cfg.dff
     n = args.steps
@@ -110,7 +119,8 @@ def profile_only(args, sp24, torch, dev, cfg, F1, F2, W1s, W2s, X, dY1, H, dY2, 
         log(f"copy: {n} x 512 MiB")
         return
     for s in range(len(W1s)):
-        sp24.sp24_search_compress_batch([W1s[s], W2s[s]], outs=[F1, F2])
+        sp24.sp24_search_compress_batch([W1s[s], W2s[s]], outs=[F1, F2], prev=[F1["idx"], F2["idx"]],
+                                        flips=[FL[s, 0:1], FL[s, 1:2]])
         if args.profile_kernel == "search_compress" and s + 1 >= n:
             break
     torch.cuda.synchronize()
@@ -165,17 +175,22 @@ def main():
                 "vals_col": torch.empty(C, R // 2, dtype=torch.float16, device=dev),
                 "meta_col": torch.empty(C, R // 16, dtype=torch.int16, device=dev)}
     F1, F2 = forms(f, d), forms(d, f)
+    # masks of the initial weights: the "previous" masks of step 0
+    sp24.sp24_search_compress_batch([to(inp.w1), to(inp.w2)], outs=[F1, F2])
+    FL = torch.zeros(nsteps, 2, dtype=torch.int64, device=dev)     # flips of W1, W2 per step
+    FLb = torch.zeros(nsteps, 2, dtype=torch.int64, device=dev)    # the breakdown pass's own counters
     Y1 = torch.empty(T, f, dtype=torch.float16, device=dev)
     dX1 = torch.empty(T, d, dtype=torch.float16, device=dev)
     Y2 = torch.empty(T, d, dtype=torch.float16, device=dev)
     dX2 = torch.empty(T, f, dtype=torch.float16, device=dev)
 
-    def step(s, ev=None):
+    def step(s, ev=None, fl=FL):
         def mark(i):
             if ev is not None:
                 ev[i].record()
         mark(0)
-        sp24.sp24_search_compress_batch([W1s[s], W2s[s]], outs=[F1, F2])
+        sp24.sp24_search_compress_batch([W1s[s], W2s[s]], outs=[F1, F2], prev=[F1["idx"], F2["idx"]],
+                                        flips=[fl[s, 0:1], fl[s, 1:2]])
         mark(1)
         sp24.sp24_spmm_fwd(X, F1["vals_row"], F1["meta_row"], f, d, Y=Y1)
         mark(2)
@@ -187,7 +202,7 @@ def main():
         mark(5)
 
     if args.profile_kernel:
-        profile_only(args, sp24, torch, dev, cfg, F1, F2, W1s, W2s, X, dY1, H, dY2, Y1, dX1, Y2, dX2)
+        profile_only(args, sp24, torch, dev, cfg, F1, F2, FL, W1s, W2s, X, dY1, H, dY2, Y1, dX1, Y2, dX2)
         return
 
     for s in range(args.warmup):
@@ -214,7 +229,7 @@ def main():
     evs = []
     for s in range(args.warmup, nsteps):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        step(s, ev)
+        step(s, ev, FLb)
         evs.append(ev)
     torch.cuda.synchronize()
     seg = np.zeros(5)
@@ -232,6 +247,7 @@ def main():
     achieved = float(np.mean(launch_flops)) / (avg_launch_ms * 1e-3) / 1e12
     traffic = traffic_from_counters()
 
+    flips = FL[args.warmup:].cpu().numpy().astype(np.float64) / np.array([f * d, d * f], dtype=np.float64)
     flops_step = cfg.dense_equiv_flops()
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
@@ -283,12 +299,17 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": "gpt2-1.5b-ffn noisy 20-step loop: search+compress W1,W2 then 4 sparse GEMMs per step",
+        "config": {"workload": "gpt2-1.5b-ffn noisy 20-step loop: search+compress W1,W2 (flip counts fused) then "
+                               "4 sparse GEMMs per step",
                    "d": d, "d_ff": f, "tokens": T, "weights": [[f, d], [d, f]], "seed": cfg.seed},
         "value_definition": "dense-equivalent GEMM flops per step (sum of 2*T*N*K) / step wall time incl. search+compress",
         "search_compress_GBps": round(sc_gbps, 1),
         "search_compress_frac_hbm": round(sc_gbps / HBM_PEAK_GBPS, 4),
         "search_compress_us_both_weights": round(sc_ms * 1e3, 2),
+        "flip_rate": {"definition": "mask entries changed since the previous step's search / entries",
+                      "w1_mean": float(f"{flips[:, 0].mean():.4g}"), "w2_mean": float(f"{flips[:, 1].mean():.4g}"),
+                      "w1_first_last": [float(f"{flips[0, 0]:.4g}"), float(f"{flips[-1, 0]:.4g}")],
+                      "w2_first_last": [float(f"{flips[0, 1]:.4g}"), float(f"{flips[-1, 1]:.4g}")]},
         "gemm_TFLOPs_dense_equiv": {n: round(v, 1) for (n, *_), v in zip(gemm_shapes, gemm_dense_tflops)},
         "gemm_us": {n: round(ms * 1e3, 1) for (n, *_), ms in zip(gemm_shapes, gemm_ms)},
         "roofline": {"kernel": "spmm_nt (one sp24_spmm_* call)", "bound": "mfma", "achieved": round(achieved, 1),

@@ -11,6 +11,10 @@
  *              2:4 sparse matrix multiplication for the FFN layers.
  *   [SW]       reproducibility table, "Software Dependencies" row: separate
  *              mask-search and pruning kernels, and 2:4 sparse MMs.
+ *   [Flip]     the abstract's "flip rate", a monitor of the stability of 2:4
+ *              training.  The pages give no formula; the library counts the
+ *              mask entries (of the R*C) whose kept/pruned state differs
+ *              between two masks, and the rate is that count over R*C.
  *
  * Conventions shared by every entry point:
  *   - W is the fp16 weight [R, C], row-major, PyTorch Linear layout [out, in].
@@ -113,9 +117,22 @@ int sp24_search_compress(const void* W, int64_t R, int64_t C, uint8_t* idx,
                          void* vals_col, uint16_t* meta_col, void* stream);
 
 /*
- * One weight of a batched search + compression call.  The fields mean what
- * the arguments of sp24_search_compress mean; idx and either (vals, meta)
- * pair may be NULL, as there.
+ * One weight of a batched search + compression call.  W .. meta_col mean
+ * what the arguments of sp24_search_compress mean; idx and either (vals,
+ * meta) pair may be NULL, as there.
+ *
+ * Flip counting [Flip] (optional; both NULL to skip, both set to count):
+ *   idx_prev  in   uint8 [R/4, C/4], the masks of the previous search (values
+ *                  >= 90 are read as pattern 0).  It may be the same buffer as
+ *                  idx, which is then updated in place (each block's previous
+ *                  index is read before its new one is written), but it must
+ *                  not overlap any other buffer of the call.
+ *   flips     in/out  one uint64 in device memory, 8-byte aligned.  The call
+ *                  ADDS the number of mask entries whose kept/pruned state
+ *                  differs from idx_prev (an even number, at most R*C); the
+ *                  caller clears it when it wants a fresh count, and several
+ *                  jobs or calls may add into one counter.  The additions are
+ *                  device atomics, so the total does not depend on order.
  */
 typedef struct sp24_sc_job {
   const void* W;
@@ -126,6 +143,8 @@ typedef struct sp24_sc_job {
   uint16_t* meta_row;
   void* vals_col;
   uint16_t* meta_col;
+  const uint8_t* idx_prev;
+  uint64_t* flips;
 } sp24_sc_job;
 
 #define SP24_MAX_BATCH 8
@@ -137,10 +156,27 @@ typedef struct sp24_sc_job {
  * HOST array, read during the call only.  Every job is validated first; on
  * any error nothing is launched and the first failing job's status is
  * returned.  Results are identical to separate sp24_search_compress calls.
- * Errors: NULL (jobs NULL, or a job as in sp24_search_compress), SHAPE (also
- * count outside 1..SP24_MAX_BATCH), ALIGN, TOO_LARGE, LAUNCH.
+ * Errors: NULL (jobs NULL, a job as in sp24_search_compress, or only one of
+ * idx_prev and flips given), SHAPE (also count outside 1..SP24_MAX_BATCH),
+ * ALIGN (flips needs 8 bytes, every other pointer 16), TOO_LARGE, LAUNCH.
  */
 int sp24_search_compress_batch(const sp24_sc_job* jobs, int count, void* stream);
+
+/*
+ * Flip count between two mask-index arrays [Flip]: ADDS to *flips the number
+ * of mask entries whose kept/pruned state differs between pattern idx_prev[i]
+ * and pattern idx_new[i], summed over i in [0, nblocks).  Indices >= 90 are
+ * read as pattern 0.  Dividing by 16*nblocks gives the flip rate.  The fused
+ * form inside sp24_search_compress_batch saves this extra pass.
+ *
+ *   idx_prev, idx_new  in   uint8 [nblocks], 16-byte aligned
+ *   nblocks                 >= 0, below 2^40
+ *   flips     in/out  one uint64 in device memory, 8-byte aligned (as for
+ *                     sp24_sc_job: the call adds, the caller clears)
+ * Errors: NULL, SHAPE (negative nblocks), ALIGN, TOO_LARGE, LAUNCH.
+ */
+int sp24_flip_count(const uint8_t* idx_prev, const uint8_t* idx_new, int64_t nblocks,
+                    uint64_t* flips, void* stream);
 
 /*
  * Forward 2:4 sparse GEMM  Y = X * Ws^T  [Abstract, SW].
@@ -177,7 +213,7 @@ const char* sp24_status_str(int status);
  */
 int sp24_pattern_table(uint16_t* out);
 
-/* Host only: the library's ABI version (1 for this header). */
+/* Host only: the library's ABI version (2 for this header). */
 int sp24_abi_version(void);
 
 #ifdef __cplusplus

@@ -16,6 +16,7 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;        // each dimension below 2^3
 constexpr int64_t kMaxElems = (int64_t)1 << 40;      // each matrix below 2^40 entries
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 int check_dims(int64_t a, int64_t b, int64_t mult) {
   if (a < 0 || b < 0 || a % mult != 0 || b % mult != 0) return SP24_ERR_SHAPE;
@@ -105,13 +106,27 @@ int sp24_search_compress_batch(const sp24_sc_job* jobs, int count, void* stream)
     const sp24_sc_job& j = jobs[k];
     const int st = check_compress(j.W, nullptr, j.idx, j.R, j.C, j.vals_row, j.meta_row, j.vals_col, j.meta_col);
     if (st != SP24_OK) return st;
+    if ((j.idx_prev == nullptr) != (j.flips == nullptr)) return SP24_ERR_NULL;
     if (j.R == 0 || j.C == 0) continue;
+    if (j.flips && (!aligned16(j.idx_prev) || !aligned8(j.flips))) return SP24_ERR_ALIGN;
     batch.j[batch.count++] = sp24::ScJob{static_cast<const uint16_t*>(j.W), j.R, j.C, nullptr, j.idx,
                                          static_cast<uint16_t*>(j.vals_row), j.meta_row,
-                                         static_cast<uint16_t*>(j.vals_col), j.meta_col, 0, 0};
+                                         static_cast<uint16_t*>(j.vals_col), j.meta_col, j.idx_prev,
+                                         reinterpret_cast<unsigned long long*>(j.flips), 0, 0};
   }
   if (batch.count == 0) return SP24_OK;
   return launch_status(sp24::launch_search_compress_jobs(batch, true, as_stream(stream)));
+}
+
+int sp24_flip_count(const uint8_t* idx_prev, const uint8_t* idx_new, int64_t nblocks, uint64_t* flips,
+                    void* stream) {
+  if (nblocks < 0) return SP24_ERR_SHAPE;
+  if (nblocks >= kMaxElems) return SP24_ERR_TOO_LARGE;
+  if (nblocks == 0) return SP24_OK;
+  if (idx_prev == nullptr || idx_new == nullptr || flips == nullptr) return SP24_ERR_NULL;
+  if (!aligned16(idx_prev) || !aligned16(idx_new) || !aligned8(flips)) return SP24_ERR_ALIGN;
+  return launch_status(sp24::launch_flip_count(idx_prev, idx_new, nblocks,
+                                               reinterpret_cast<unsigned long long*>(flips), as_stream(stream)));
 }
 
 int sp24_spmm_fwd(const void* X, const void* vals_row, const uint16_t* meta_row, int64_t T, int64_t R, int64_t C,
@@ -145,6 +160,6 @@ int sp24_pattern_table(uint16_t* out) {
   return SP24_OK;
 }
 
-int sp24_abi_version(void) { return 1; }
+int sp24_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -18,6 +18,8 @@ struct ScJob {
   uint16_t* meta_row;
   uint16_t* vals_col;        // (vals_col, meta_col) may both be nullptr
   uint16_t* meta_col;
+  const uint8_t* idx_prev;   // previous masks (search only), or nullptr
+  unsigned long long* flips; // receives += entries changed vs idx_prev; set iff idx_prev is
   int64_t tiles_c;           // filled in by the launcher
   int64_t tile_begin;        // filled in by the launcher
 };
@@ -37,6 +39,11 @@ hipError_t launch_search_compress_jobs(ScJobs jobs, bool search, hipStream_t s);
 hipError_t launch_search_compress(const uint16_t* W, int64_t R, int64_t C, const uint8_t* idx_in,
                                   uint8_t* idx_out, uint16_t* vals_row, uint16_t* meta_row,
                                   uint16_t* vals_col, uint16_t* meta_col, hipStream_t s);
+
+// *flips += number of mask entries that differ between the patterns
+// a[0..n) and b[0..n) (indices >= 90 read as pattern 0).
+hipError_t launch_flip_count(const uint8_t* a, const uint8_t* b, int64_t n, unsigned long long* flips,
+                             hipStream_t s);
 
 // out[T][N] = A[T][K] * S[N][K]^T with S in 2:4 row form along K:
 // vals [N][K/2] fp16, meta [N][K/16].  N, K multiples of 16.

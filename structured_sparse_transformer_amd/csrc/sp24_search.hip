@@ -194,6 +194,9 @@ constexpr int kTile = 128;            // rows and columns of W per workgroup
 constexpr int kTB = kTile / 4;        // blocks per tile side (32)
 constexpr int kCompressThreads = 256;
 constexpr int kBlocksPerThread = kTB * kTB / kCompressThreads;  // 4
+constexpr int kCompressWaves = kCompressThreads / 64;
+// Each workgroup handles kTilesPerWg tiles (see search_compress_kernel).
+constexpr int kTilesPerWg = 2;
 
 // byte selectors for v_perm_b32 that gather halves i0 and i1 of a 4-half group
 constexpr uint32_t pair_selector(int i0, int i1) {
@@ -204,6 +207,7 @@ struct SelTable {
   uint32_t row_sel[kNumPatterns][4];
   uint32_t col_sel[kNumPatterns][4];
   uint32_t nibs[kNumPatterns];  // row nibbles (bits 0..15) | column nibbles << 16
+  uint16_t mask[kNumPatterns + 2];  // kept entries, bit 4r+c (two pad entries keep the size in dwords)
 };
 
 constexpr SelTable build_sel_table() {
@@ -216,6 +220,7 @@ constexpr SelTable build_sel_table() {
       s.col_sel[p][r] = pair_selector(c & 3, c >> 2);
     }
     s.nibs[p] = (uint32_t)kTables.row_nib[p] | (uint32_t)kTables.col_nib[p] << 16;
+    s.mask[p] = kTables.mask[p];
   }
   return s;
 }
@@ -229,7 +234,9 @@ struct CompressSmem {
   uint8_t nib_row[kTile][kTB + 4];       // [row][group]: nibble
   uint8_t nib_col[kTile][kTB + 4];       // [column][row group]
   uint8_t idx[kTB][kTB];
+  uint32_t flips[kTilesPerWg][kCompressWaves];  // per-wave flip counts of each tile
 };
+static_assert(sizeof(SelTable) % 4 == 0, "SelTable is copied in dwords");
 
 // Tile geometry of one workgroup-tile of one job.  The job is copied by
 // value (selected with static indices), so the kernel-argument table never
@@ -260,6 +267,7 @@ __device__ __forceinline__ TileRef tile_ref(const ScJobs& jobs, int64_t t) {
 // bi = tid/32 + 8q, columns 4*bj .. 4*bj+3.
 struct TileData {
   uint32_t w[kBlocksPerThread][4][2];
+  uint32_t prev[kBlocksPerThread];   // previous pattern of each block (flip counting only)
 };
 
 __device__ __forceinline__ void load_tile(const TileRef& tr, int tid, TileData& d) {
@@ -268,6 +276,7 @@ __device__ __forceinline__ void load_tile(const TileRef& tr, int tid, TileData& 
   for (int q = 0; q < kBlocksPerThread; ++q) {
     const int bi = tid / kTB + q * (kCompressThreads / kTB);
     if (bi >= tr.rows / 4 || bj >= tr.cols / 4) continue;
+    if (tr.jb.idx_prev) d.prev[q] = tr.jb.idx_prev[(tr.r0 / 4 + bi) * (tr.jb.C / 4) + tr.c0 / 4 + bj];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint2 v = *reinterpret_cast<const uint2*>(tr.jb.W + (tr.r0 + 4 * bi + r) * tr.jb.C + tr.c0 + 4 * bj);
@@ -278,12 +287,14 @@ __device__ __forceinline__ void load_tile(const TileRef& tr, int tid, TileData& 
 }
 
 // Search (or read the given masks), then stage both compressed forms of the
-// tile in LDS.
+// tile in LDS.  Returns this thread's count of mask entries that changed
+// against the previous masks (0 unless the job counts flips).
 template <bool kSearch>
-__device__ __forceinline__ void stage_tile(const TileRef& tr, int tid, const TileData& d, CompressSmem& sm) {
+__device__ __forceinline__ uint32_t stage_tile(const TileRef& tr, int tid, const TileData& d, CompressSmem& sm) {
   const ScJob& jb = tr.jb;
   const int bj = tid % kTB;
   const int nbc_t = tr.cols / 4, nbr_t = tr.rows / 4;
+  uint32_t flips = 0;
 #pragma unroll
   for (int q = 0; q < kBlocksPerThread; ++q) {
     const int bi = tid / kTB + q * (kCompressThreads / kTB);
@@ -297,6 +308,10 @@ __device__ __forceinline__ void stage_tile(const TileRef& tr, int tid, const Til
       p = p < kNumPatterns ? p : 0;
     }
     sm.idx[bi][bj] = (uint8_t)p;
+    if (kSearch && jb.idx_prev) {
+      const uint32_t prev = d.prev[q] < (uint32_t)kNumPatterns ? d.prev[q] : 0u;
+      flips += (uint32_t)__builtin_popcount((uint32_t)(sm.sel.mask[p] ^ sm.sel.mask[prev]));
+    }
     const uint32_t nibs = sm.sel.nibs[p];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -312,6 +327,13 @@ __device__ __forceinline__ void stage_tile(const TileRef& tr, int tid, const Til
       sm.nib_col[4 * bj + c][bi] = (uint8_t)((nibs >> (16 + 4 * c)) & 0xF);
     }
   }
+  return flips;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, 64);
+  return v;
 }
 
 // Coalesced stores of a staged tile: 16-byte row and column segments.
@@ -354,8 +376,8 @@ __device__ __forceinline__ void write_tile(const TileRef& tr, int tid, const Com
 // Each workgroup handles kTilesPerWg tiles.  All of their loads are issued
 // first; tile k+1 is searched while the global stores of tile k drain, so
 // loading, searching and storing overlap within the workgroup instead of
-// running as three GPU-wide phases.
-constexpr int kTilesPerWg = 2;
+// running as three GPU-wide phases.  A job that counts flips gets one atomic
+// add per tile, after the tile's waves have pooled their counts in LDS.
 
 template <bool kSearch>
 __global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(ScJobs jobs) {
@@ -387,10 +409,66 @@ __global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(ScJob
 #pragma unroll
   for (int k = 0; k < kTilesPerWg; ++k) {
     if (!have[k]) continue;
-    stage_tile<kSearch>(tr[k], tid, td[k], sm);
+    const uint32_t f = stage_tile<kSearch>(tr[k], tid, td[k], sm);
+    if (kSearch && tr[k].jb.flips) {
+      const uint32_t w = wave_sum(f);
+      if (tid % 64 == 0) sm.flips[k][tid / 64] = w;
+    }
     __syncthreads();
     write_tile(tr[k], tid, sm);
     __syncthreads();    // the staging buffer is read out before the next tile overwrites it
+  }
+  if (kSearch && tid == 0) {
+#pragma unroll
+    for (int k = 0; k < kTilesPerWg; ++k) {
+      if (!have[k] || !tr[k].jb.flips) continue;
+      uint32_t sum = 0;
+#pragma unroll
+      for (int w = 0; w < kCompressWaves; ++w) sum += sm.flips[k][w];
+      if (sum) atomicAdd(tr[k].jb.flips, (unsigned long long)sum);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// flip count between two index arrays: 16 blocks per thread per step
+
+constexpr int kFlipThreads = 256;
+
+__global__ __launch_bounds__(kFlipThreads) void flip_count_kernel(const uint8_t* __restrict__ a,
+                                                                  const uint8_t* __restrict__ b, int64_t n,
+                                                                  unsigned long long* __restrict__ flips) {
+  __shared__ uint16_t mask[kNumPatterns];
+  __shared__ uint32_t part[kFlipThreads / 64];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kNumPatterns; i += kFlipThreads) mask[i] = g_sel.mask[i];
+  __syncthreads();
+  auto diff = [&](uint32_t x, uint32_t y) -> uint32_t {
+    x = x < (uint32_t)kNumPatterns ? x : 0u;
+    y = y < (uint32_t)kNumPatterns ? y : 0u;
+    return (uint32_t)__builtin_popcount((uint32_t)(mask[x] ^ mask[y]));
+  };
+  uint32_t cnt = 0;
+  const int64_t nvec = n / 16;
+  const int64_t stride = (int64_t)gridDim.x * kFlipThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kFlipThreads + tid; i < nvec; i += stride) {
+    const uint4 va = reinterpret_cast<const uint4*>(a)[i];
+    const uint4 vb = reinterpret_cast<const uint4*>(b)[i];
+    const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cnt += diff((wa[j] >> (8 * e)) & 0xFF, (wb[j] >> (8 * e)) & 0xFF);
+  }
+  if (blockIdx.x == 0 && tid < (int)(n - 16 * nvec)) cnt += diff(a[16 * nvec + tid], b[16 * nvec + tid]);
+  const uint32_t w = wave_sum(cnt);
+  if (tid % 64 == 0) part[tid / 64] = w;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < kFlipThreads / 64; ++k) sum += part[k];
+    if (sum) atomicAdd(flips, (unsigned long long)sum);
   }
 }
 
@@ -430,8 +508,18 @@ hipError_t launch_search_compress(const uint16_t* W, int64_t R, int64_t C, const
   if (R == 0 || C == 0) return hipSuccess;
   ScJobs jobs{};
   jobs.count = 1;
-  jobs.j[0] = ScJob{W, R, C, idx_in, idx_out, vals_row, meta_row, vals_col, meta_col, 0, 0};
+  jobs.j[0] = ScJob{W, R, C, idx_in, idx_out, vals_row, meta_row, vals_col, meta_col, nullptr, nullptr, 0, 0};
   return launch_search_compress_jobs(jobs, idx_in == nullptr, s);
+}
+
+hipError_t launch_flip_count(const uint8_t* a, const uint8_t* b, int64_t n, unsigned long long* flips,
+                             hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  // enough workgroups to stream the arrays; each thread covers 16 blocks a step
+  const int64_t want = (n / 16 + kFlipThreads - 1) / kFlipThreads;
+  const int64_t grid = want < 1 ? 1 : (want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(flip_count_kernel, dim3((unsigned)grid), dim3(kFlipThreads), 0, s, a, b, n, flips);
+  return hipGetLastError();
 }
 
 }  // namespace sp24

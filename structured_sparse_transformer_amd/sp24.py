@@ -25,7 +25,8 @@ SP24_OK = 0
 STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_LAUNCH",
                 5: "ERR_UNSUPPORTED", 6: "ERR_TOO_LARGE"}
 EXPORTS = ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
-           "sp24_spmm_fwd", "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table", "sp24_abi_version")
+           "sp24_flip_count", "sp24_spmm_fwd", "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table",
+           "sp24_abi_version")
 MAX_BATCH = 8
 
 
@@ -33,7 +34,8 @@ class ScJob(ctypes.Structure):
     """Mirror of sp24_sc_job (include/sp24.h)."""
     _fields_ = [("W", ctypes.c_void_p), ("R", ctypes.c_int64), ("C", ctypes.c_int64), ("idx", ctypes.c_void_p),
                 ("vals_row", ctypes.c_void_p), ("meta_row", ctypes.c_void_p),
-                ("vals_col", ctypes.c_void_p), ("meta_col", ctypes.c_void_p)]
+                ("vals_col", ctypes.c_void_p), ("meta_col", ctypes.c_void_p),
+                ("idx_prev", ctypes.c_void_p), ("flips", ctypes.c_void_p)]
 
 
 class Sp24Error(RuntimeError):
@@ -58,6 +60,7 @@ def lib() -> ctypes.CDLL:
             "sp24_compress": [p, p, i64, i64, p, p, p, p, p],
             "sp24_search_compress": [p, i64, i64, p, p, p, p, p, p],
             "sp24_search_compress_batch": [p, i32, p],
+            "sp24_flip_count": [p, p, i64, p, p],
             "sp24_spmm_fwd": [p, p, p, i64, i64, i64, p, p],
             "sp24_spmm_bwd_input": [p, p, p, i64, i64, i64, p, p],
             "sp24_status_str": [i32],
@@ -149,11 +152,33 @@ def sp24_search_compress(W, want_idx=True, row=True, col=True, out=None, stream=
     return o
 
 
-def sp24_search_compress_batch(Ws, outs=None, want_idx=True, row=True, col=True, stream=None):
-    """sp24_search_compress for several weights in one launch; returns one dict per weight."""
+def _flip_counter(f):
+    """A uint64 flip counter travels as an int64 tensor view of one element."""
+    if f is None:
+        return None
+    if f.dtype != torch.int64 or f.numel() != 1:
+        raise ValueError("a flip counter is a one-element int64 tensor (or a view of one)")
+    if not f.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    return f.data_ptr()
+
+
+def sp24_search_compress_batch(Ws, outs=None, want_idx=True, row=True, col=True, prev=None, flips=None,
+                               stream=None):
+    """sp24_search_compress for several weights in one launch; returns one dict per weight.
+
+    ``prev[k]`` (uint8 [R/4, C/4]) and ``flips[k]`` (a one-element int64 tensor)
+    make weight k count its flipped mask entries against ``prev[k]``: the
+    count is ADDED to ``flips[k]``.  ``prev[k]`` may be the weight's own
+    ``outs[k]["idx"]``, which is then updated in place.
+    """
     if not 1 <= len(Ws) <= MAX_BATCH:
         raise ValueError(f"between 1 and {MAX_BATCH} weights per batch")
     outs = list(outs) if outs is not None else [None] * len(Ws)
+    prev = list(prev) if prev is not None else [None] * len(Ws)
+    flips = list(flips) if flips is not None else [None] * len(Ws)
+    if len(prev) != len(Ws) or len(flips) != len(Ws):
+        raise ValueError("prev and flips need one entry per weight")
     res, jobs = [], (ScJob * len(Ws))()
     for k, W in enumerate(Ws):
         R, C = _w(W)
@@ -161,12 +186,26 @@ def sp24_search_compress_batch(Ws, outs=None, want_idx=True, row=True, col=True,
         if want_idx:
             o["idx"] = _out(o.get("idx"), (R // 4, C // 4), torch.uint8, W.device)
         ptr = lambda t: _ptr(t).value if t is not None and t.numel() else None  # noqa: E731
+        if prev[k] is not None:
+            _out(prev[k], (R // 4, C // 4), torch.uint8, W.device)
         jobs[k] = ScJob(ptr(W), R, C, ptr(o.get("idx")), ptr(o.get("vals_row")), ptr(o.get("meta_row")),
-                        ptr(o.get("vals_col")), ptr(o.get("meta_col")))
+                        ptr(o.get("vals_col")), ptr(o.get("meta_col")), ptr(prev[k]), _flip_counter(flips[k]))
         res.append(o)
     _check("sp24_search_compress_batch",
            lib().sp24_search_compress_batch(ctypes.cast(jobs, ctypes.c_void_p), len(Ws), _stream(stream)))
     return res
+
+
+def sp24_flip_count(idx_prev, idx_new, flips=None, stream=None):
+    """Adds to ``flips`` (a one-element int64 tensor, zeroed when not given)
+    the number of mask entries that differ between the two index arrays."""
+    if idx_prev.dtype != torch.uint8 or idx_new.dtype != torch.uint8 or idx_prev.shape != idx_new.shape:
+        raise ValueError("idx_prev and idx_new must be uint8 tensors of one shape")
+    if flips is None:
+        flips = torch.zeros(1, dtype=torch.int64, device=idx_new.device)
+    _check("sp24_flip_count", lib().sp24_flip_count(_ptr(idx_prev), _ptr(idx_new), idx_new.numel(),
+                                                    _flip_counter(flips), _stream(stream)))
+    return flips
 
 
 def sp24_spmm_fwd(X, vals_row, meta_row, R, C, Y=None, stream=None):

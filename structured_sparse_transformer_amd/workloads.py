@@ -50,6 +50,12 @@ def add_noise_f16(w: np.ndarray, noise: np.ndarray) -> np.ndarray:
     return (w.astype(np.float32) + noise).astype(np.float16)
 
 
+def random_idx(base: int, k: int, shape, hi: int = 90) -> np.ndarray:
+    """Uniform uint8 pattern indices in [0, hi): stand-in mask arrays."""
+    rng = np.random.default_rng([base, k])
+    return rng.integers(0, hi, size=shape, dtype=np.uint8)
+
+
 def stress_weight(base: int, R: int = 4096, C: int = 4096) -> np.ndarray:
     """Tie-heavy stress weight.
 

@@ -37,7 +37,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_spmm_fwd",
+    for n in ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
+              "sp24_flip_count", "sp24_spmm_fwd",
               "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table", "sp24_abi_version"):
         assert n in names
 
@@ -57,7 +58,7 @@ def test_pattern_table_matches_oracle(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sp24_abi_version() == 1
+    assert L.sp24_abi_version() == 2
     for s in range(7):
         assert L.sp24_status_str(s)
     assert L.sp24_status_str(99) == b"unknown status"
@@ -147,3 +148,29 @@ def test_search_compress_batch_validation(L):
     empty = (ScJob * 2)(ScJob(None, 0, 16, None, 0x3000, 0x4000, None, None),
                         ScJob(None, 16, 0, None, 0x3000, 0x4000, None, None))
     assert f(ctypes.cast(empty, ctypes.c_void_p), 2, NUL) == 0         # all empty: nothing launched
+
+
+def test_search_compress_batch_flip_validation(L):
+    from structured_sparse_transformer_amd.sp24 import ScJob
+    f = L.sp24_search_compress_batch
+    base = (0x1000, 16, 16, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000)
+    one = lambda *extra: ctypes.cast((ScJob * 1)(ScJob(*base, *extra)), ctypes.c_void_p)  # noqa: E731
+    assert f(one(0x7000, None), 1, NUL) == 1          # previous masks without a counter
+    assert f(one(None, 0x8000), 1, NUL) == 1          # counter without previous masks
+    assert f(one(0x7008, 0x8000), 1, NUL) == 3        # idx_prev needs 16 bytes
+    assert f(one(0x7000, 0x8004), 1, NUL) == 3        # the counter needs 8
+    empty = (ScJob * 1)(ScJob(None, 0, 16, None, 0x3000, 0x4000, None, None, 0x7000, 0x8008))
+    assert f(ctypes.cast(empty, ctypes.c_void_p), 1, NUL) == 0
+
+
+def test_flip_count_validation(L):
+    f = L.sp24_flip_count
+    assert f(FAKE, FAKE, -1, FAKE, NUL) == 2
+    assert f(FAKE, FAKE, 1 << 40, FAKE, NUL) == 6
+    assert f(NUL, FAKE, 4, FAKE, NUL) == 1
+    assert f(FAKE, NUL, 4, FAKE, NUL) == 1
+    assert f(FAKE, FAKE, 4, NUL, NUL) == 1
+    assert f(MIS, FAKE, 4, FAKE, NUL) == 3
+    assert f(FAKE, MIS, 4, FAKE, NUL) == 3
+    assert f(FAKE, FAKE, 4, ctypes.c_void_p(0x1004), NUL) == 3
+    assert f(NUL, NUL, 0, NUL, NUL) == 0
