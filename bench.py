@@ -118,6 +118,14 @@ def profile_only(args, sp24, torch, dev, cfg, F1, F2, FL, W1s, W2s, X, dY1, H, d
         torch.cuda.synchronize()
         log(f"copy: {n} x 512 MiB")
         return
+    if args.profile_kernel == "flip_count":
+        prev = F1["idx"].clone()
+        sp24.sp24_search_compress_batch([W1s[0], W2s[0]], outs=[F1, F2])
+        for _ in range(n):
+            sp24.sp24_flip_count(prev, F1["idx"], FL[0, 0:1])
+        torch.cuda.synchronize()
+        log(f"flip_count: {n} calls")
+        return
     for s in range(len(W1s)):
         sp24.sp24_search_compress_batch([W1s[s], W2s[s]], outs=[F1, F2], prev=[F1["idx"], F2["idx"]],
                                         flips=[FL[s, 0:1], FL[s, 1:2]])
@@ -142,7 +150,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy context numbers")
-    ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "copy"],
+    ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "flip_count", "copy"],
                     help="run only this kernel --steps times (for rocprofv3 counter passes); prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -248,6 +256,19 @@ def main():
     traffic = traffic_from_counters()
 
     flips = FL[args.warmup:].cpu().numpy().astype(np.float64) / np.array([f * d, d * f], dtype=np.float64)
+
+    # the standalone flip count (two index arrays of W1, 640000 blocks each),
+    # back-to-back calls: launch-bound at this size
+    fl_prev, fl_ctr, fl_calls = torch.roll(F1["idx"], 1, 0).contiguous(), FLb[0, 0:1], 50
+    sp24.sp24_flip_count(fl_prev, F1["idx"], fl_ctr)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(fl_calls):
+        sp24.sp24_flip_count(fl_prev, F1["idx"], fl_ctr)
+    e1.record()
+    torch.cuda.synchronize()
+    fl_us = e0.elapsed_time(e1) * 1e3 / fl_calls
+    fl_bytes = 2 * F1["idx"].numel()
     flops_step = cfg.dense_equiv_flops()
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
@@ -309,7 +330,9 @@ def main():
         "flip_rate": {"definition": "mask entries changed since the previous step's search / entries",
                       "w1_mean": float(f"{flips[:, 0].mean():.4g}"), "w2_mean": float(f"{flips[:, 1].mean():.4g}"),
                       "w1_first_last": [float(f"{flips[0, 0]:.4g}"), float(f"{flips[-1, 0]:.4g}")],
-                      "w2_first_last": [float(f"{flips[0, 1]:.4g}"), float(f"{flips[-1, 1]:.4g}")]},
+                      "w2_first_last": [float(f"{flips[0, 1]:.4g}"), float(f"{flips[-1, 1]:.4g}")],
+                      "standalone_sp24_flip_count_us": round(fl_us, 2),
+                      "standalone_GBps": round(fl_bytes / (fl_us * 1e-6) / 1e9, 1)},
         "gemm_TFLOPs_dense_equiv": {n: round(v, 1) for (n, *_), v in zip(gemm_shapes, gemm_dense_tflops)},
         "gemm_us": {n: round(ms * 1e3, 1) for (n, *_), ms in zip(gemm_shapes, gemm_ms)},
         "roofline": {"kernel": "spmm_nt (one sp24_spmm_* call)", "bound": "mfma", "achieved": round(achieved, 1),

@@ -234,6 +234,7 @@ struct CompressSmem {
   uint8_t nib_row[kTile][kTB + 4];       // [row][group]: nibble
   uint8_t nib_col[kTile][kTB + 4];       // [column][row group]
   uint8_t idx[kTB][kTB];
+  uint8_t prev[kTilesPerWg][kTB][kTB];          // previous indices of each tile (flip counting)
   uint32_t flips[kTilesPerWg][kCompressWaves];  // per-wave flip counts of each tile
 };
 static_assert(sizeof(SelTable) % 4 == 0, "SelTable is copied in dwords");
@@ -267,8 +268,17 @@ __device__ __forceinline__ TileRef tile_ref(const ScJobs& jobs, int64_t t) {
 // bi = tid/32 + 8q, columns 4*bj .. 4*bj+3.
 struct TileData {
   uint32_t w[kBlocksPerThread][4][2];
-  uint32_t prev[kBlocksPerThread];   // previous pattern of each block (flip counting only)
+  uint32_t prev4;   // four previous indices: block row tid/8, block columns 4*(tid%8) .. +3
 };
+
+// Previous indices of a tile, one dword (four blocks) per thread, issued
+// before the tile's W loads so that only they need to have arrived when the
+// dword is parked in LDS.
+__device__ __forceinline__ void load_prev(const TileRef& tr, int tid, TileData& d) {
+  const int bi = tid / 8, bj4 = 4 * (tid % 8);
+  if (bi < tr.rows / 4 && bj4 < tr.cols / 4)
+    d.prev4 = *reinterpret_cast<const uint32_t*>(tr.jb.idx_prev + (tr.r0 / 4 + bi) * (tr.jb.C / 4) + tr.c0 / 4 + bj4);
+}
 
 __device__ __forceinline__ void load_tile(const TileRef& tr, int tid, TileData& d) {
   const int bj = tid % kTB;
@@ -276,7 +286,6 @@ __device__ __forceinline__ void load_tile(const TileRef& tr, int tid, TileData& 
   for (int q = 0; q < kBlocksPerThread; ++q) {
     const int bi = tid / kTB + q * (kCompressThreads / kTB);
     if (bi >= tr.rows / 4 || bj >= tr.cols / 4) continue;
-    if (tr.jb.idx_prev) d.prev[q] = tr.jb.idx_prev[(tr.r0 / 4 + bi) * (tr.jb.C / 4) + tr.c0 / 4 + bj];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint2 v = *reinterpret_cast<const uint2*>(tr.jb.W + (tr.r0 + 4 * bi + r) * tr.jb.C + tr.c0 + 4 * bj);
@@ -290,7 +299,8 @@ __device__ __forceinline__ void load_tile(const TileRef& tr, int tid, TileData& 
 // tile in LDS.  Returns this thread's count of mask entries that changed
 // against the previous masks (0 unless the job counts flips).
 template <bool kSearch>
-__device__ __forceinline__ uint32_t stage_tile(const TileRef& tr, int tid, const TileData& d, CompressSmem& sm) {
+__device__ __forceinline__ uint32_t stage_tile(const TileRef& tr, int k, int tid, const TileData& d,
+                                               CompressSmem& sm) {
   const ScJob& jb = tr.jb;
   const int bj = tid % kTB;
   const int nbc_t = tr.cols / 4, nbr_t = tr.rows / 4;
@@ -309,7 +319,8 @@ __device__ __forceinline__ uint32_t stage_tile(const TileRef& tr, int tid, const
     }
     sm.idx[bi][bj] = (uint8_t)p;
     if (kSearch && jb.idx_prev) {
-      const uint32_t prev = d.prev[q] < (uint32_t)kNumPatterns ? d.prev[q] : 0u;
+      const uint32_t pv = sm.prev[k][bi][bj];
+      const uint32_t prev = pv < (uint32_t)kNumPatterns ? pv : 0u;
       flips += (uint32_t)__builtin_popcount((uint32_t)(sm.sel.mask[p] ^ sm.sel.mask[prev]));
     }
     const uint32_t nibs = sm.sel.nibs[p];
@@ -402,14 +413,20 @@ __global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(ScJob
     have[k] = t < jobs.total_tiles;
     if (have[k]) {
       tr[k] = tile_ref(jobs, t);
+      if (kSearch && tr[k].jb.idx_prev) load_prev(tr[k], tid, td[k]);
       load_tile(tr[k], tid, td[k]);
     }
+  }
+#pragma unroll
+  for (int k = 0; k < kTilesPerWg; ++k) {
+    if (kSearch && have[k] && tr[k].jb.idx_prev && tid / 8 < tr[k].rows / 4 && 4 * (tid % 8) < tr[k].cols / 4)
+      *reinterpret_cast<uint32_t*>(&sm.prev[k][tid / 8][4 * (tid % 8)]) = td[k].prev4;
   }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < kTilesPerWg; ++k) {
     if (!have[k]) continue;
-    const uint32_t f = stage_tile<kSearch>(tr[k], tid, td[k], sm);
+    const uint32_t f = stage_tile<kSearch>(tr[k], k, tid, td[k], sm);
     if (kSearch && tr[k].jb.flips) {
       const uint32_t w = wave_sum(f);
       if (tid % 64 == 0) sm.flips[k][tid / 64] = w;
@@ -419,19 +436,34 @@ __global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(ScJob
     __syncthreads();    // the staging buffer is read out before the next tile overwrites it
   }
   if (kSearch && tid == 0) {
+    // one atomic per counter: same-address device atomics serialise, and all
+    // workgroups reach this point at about the same time
+    unsigned long long* ctr[kTilesPerWg];
+    unsigned long long sum[kTilesPerWg];
 #pragma unroll
     for (int k = 0; k < kTilesPerWg; ++k) {
-      if (!have[k] || !tr[k].jb.flips) continue;
-      uint32_t sum = 0;
+      ctr[k] = have[k] ? tr[k].jb.flips : nullptr;
+      sum[k] = 0;
+      if (ctr[k] == nullptr) continue;
 #pragma unroll
-      for (int w = 0; w < kCompressWaves; ++w) sum += sm.flips[k][w];
-      if (sum) atomicAdd(tr[k].jb.flips, (unsigned long long)sum);
+      for (int w = 0; w < kCompressWaves; ++w) sum[k] += sm.flips[k][w];
+#pragma unroll
+      for (int j = 0; j < k; ++j)
+        if (ctr[j] == ctr[k]) {
+          sum[j] += sum[k];
+          sum[k] = 0;
+          break;
+        }
     }
+#pragma unroll
+    for (int k = 0; k < kTilesPerWg; ++k)
+      if (ctr[k] != nullptr && sum[k] != 0) atomicAdd(ctr[k], sum[k]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// flip count between two index arrays: 16 blocks per thread per step
+// flip count between two index arrays: 16 blocks per thread per step, at most
+// 128 workgroups (one same-address atomic each: those serialise)
 
 constexpr int kFlipThreads = 256;
 
@@ -515,9 +547,8 @@ hipError_t launch_search_compress(const uint16_t* W, int64_t R, int64_t C, const
 hipError_t launch_flip_count(const uint8_t* a, const uint8_t* b, int64_t n, unsigned long long* flips,
                              hipStream_t s) {
   if (n == 0) return hipSuccess;
-  // enough workgroups to stream the arrays; each thread covers 16 blocks a step
   const int64_t want = (n / 16 + kFlipThreads - 1) / kFlipThreads;
-  const int64_t grid = want < 1 ? 1 : (want < 4096 ? want : 4096);
+  const int64_t grid = want < 1 ? 1 : (want < 128 ? want : 128);
   hipLaunchKernelGGL(flip_count_kernel, dim3((unsigned)grid), dim3(kFlipThreads), 0, s, a, b, n, flips);
   return hipGetLastError();
 }
