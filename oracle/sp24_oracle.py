@@ -48,6 +48,14 @@ What the method computes, and the readings taken where the pages are silent:
 4. Flip rate [HZ24 abstract] (no formula on the pages): the number of mask
    entries whose kept/pruned state differs between two consecutive masks,
    over the number of entries.
+5. Weight gradient with masked decay [HZ24 abstract: the sparse-refined
+   straight-through estimator, modified by applying the masked decay term on
+   gradients; HZ24 SW: a masked-decay kernel].  No formula is on the pages.
+   Reading: the gradient that reaches the dense weight is the straight-through
+   product ``dY^T X`` (summed over tokens), and the masked decay term
+   ``decay * (1 - M) * W`` (M the searched transposable mask, 1 where kept) is
+   added to that gradient rather than applied to the weights.  Computed in
+   float64; the library returns float32.
 """
 from __future__ import annotations
 
@@ -242,6 +250,21 @@ def flip_rate(idx_prev: np.ndarray, idx_new: np.ndarray) -> float:
     """flip_count divided by the number of matrix entries (16 per block)."""
     n = 16 * idx_new.size
     return flip_count(idx_prev, idx_new) / n if n else 0.0
+
+
+def weight_grad(dY: np.ndarray, X: np.ndarray, W: np.ndarray | None, idx: np.ndarray | None,
+                decay: float) -> np.ndarray:
+    """``dW = dY^T X + decay * (1 - M) * W`` in float64 (item 5 above).
+
+    dY [T, R] and X [T, C] are the output gradient and the input of the
+    linear layer; W [R, C] its dense weight and idx [R/4, C/4] the searched
+    masks.  With W or idx None the decay term is left out.
+    """
+    dW = dY.astype(np.float64).T @ X.astype(np.float64)
+    if W is not None and idx is not None:
+        pruned = 1.0 - idx_to_mask(idx).astype(np.float64)
+        dW = dW + float(decay) * pruned * W.astype(np.float64)
+    return dW
 
 
 def gemm_errors(out: np.ndarray, ref: np.ndarray) -> tuple:

@@ -378,3 +378,53 @@ def test_flip_count_matches_dense_masks():
     got = [O.flip_count(np.array([[x]], np.uint8), np.array([[y]], np.uint8)) for x, y in zip(p.ravel(), q.ravel())]
     want = [int((masks[x] != masks[y]).sum()) for x, y in zip(p.ravel(), q.ravel())]
     assert got == want
+
+
+# ----------------------------------------------------------------------------
+# weight gradient with masked decay
+def test_weight_grad_explicit_loop():
+    rng = np.random.default_rng(40)
+    T, R, C = 5, 8, 12
+    dY = rng.standard_normal((T, R)).astype(np.float16)
+    X = rng.standard_normal((T, C)).astype(np.float16)
+    W = rng.standard_normal((R, C)).astype(np.float16)
+    idx = rng.integers(0, 90, size=(R // 4, C // 4)).astype(np.uint8)
+    decay = 0.37
+    masks = O.pattern_masks()
+    want = np.zeros((R, C))
+    for r in range(R):
+        for c in range(C):
+            s = 0.0
+            for t in range(T):
+                s += float(dY[t, r]) * float(X[t, c])
+            kept = masks[idx[r // 4, c // 4], r % 4, c % 4]
+            want[r, c] = s + (0.0 if kept else decay * float(W[r, c]))
+    got = O.weight_grad(dY, X, W, idx, decay)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_weight_grad_special_cases():
+    rng = np.random.default_rng(41)
+    R, C = 16, 32
+    W = rng.standard_normal((R, C)).astype(np.float16)
+    idx = O.mask_search(W)
+    # one-hot tokens: X = I picks the rows of dY, so dW = dY^T exactly
+    dY = rng.standard_normal((C, R)).astype(np.float16)
+    X = np.eye(C, dtype=np.float16)
+    assert (O.weight_grad(dY, X, None, None, 0.0) == dY.astype(np.float64).T).all()
+    # no tokens: only the decay term, which is zero on every kept entry and
+    # decay * W on every pruned one, 8 of each 16 per block
+    e = np.zeros((0, R), np.float16), np.zeros((0, C), np.float16)
+    d = O.weight_grad(e[0], e[1], W, idx, 0.5)
+    kept = O.idx_to_mask(idx).astype(bool)
+    assert (d[kept] == 0).all()
+    assert (d[~kept] == 0.5 * W.astype(np.float64)[~kept]).all()
+    assert (~kept).reshape(R // 4, 4, C // 4, 4).sum(axis=(1, 3)).tolist() == [[8] * (C // 4)] * (R // 4)
+    # linear in the decay factor, and decay 0 leaves the plain product
+    dY2 = rng.standard_normal((7, R)).astype(np.float16)
+    X2 = rng.standard_normal((7, C)).astype(np.float16)
+    g0 = O.weight_grad(dY2, X2, W, idx, 0.0)
+    g1 = O.weight_grad(dY2, X2, W, idx, 1.0)
+    g3 = O.weight_grad(dY2, X2, W, idx, 3.0)
+    assert np.allclose(g3 - g0, 3 * (g1 - g0), rtol=1e-12, atol=1e-12)
+    assert (g0 == O.weight_grad(dY2, X2, None, None, 5.0)).all()
