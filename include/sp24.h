@@ -11,6 +11,11 @@
  *              2:4 sparse matrix multiplication for the FFN layers.
  *   [SW]       reproducibility table, "Software Dependencies" row: separate
  *              mask-search and pruning kernels, and 2:4 sparse MMs.
+ *   [Decay]    the abstract's modified sparse-refined straight-through
+ *              estimator, which applies the masked decay term on gradients,
+ *              and the "Software Dependencies" row's masked-decay kernel.
+ *              The pages give no formula; the library adds
+ *              decay * (1 - M) * W to the straight-through weight gradient.
  *   [Flip]     the abstract's "flip rate", a monitor of the stability of 2:4
  *              training.  The pages give no formula; the library counts the
  *              mask entries (of the R*C) whose kept/pruned state differs
@@ -203,6 +208,31 @@ int sp24_spmm_fwd(const void* X, const void* vals_row, const uint16_t* meta_row,
 int sp24_spmm_bwd_input(const void* dY, const void* vals_col, const uint16_t* meta_col,
                         int64_t T, int64_t R, int64_t C, void* dX, void* stream);
 
+/*
+ * Weight gradient of a 2:4 FFN linear layer with the masked decay term
+ * [Decay]:
+ *     dW[r][c] = sum_t dY[t][r] * X[t][c]  +  decay * (1 - M[r][c]) * W[r][c]
+ * The straight-through gradient reaches the dense weight W as the dense
+ * product dY^T X (fp16 products, fp32 accumulation); M is the transposable
+ * mask (1 where kept) given by idx.
+ *
+ *   dY        in   fp16 [T, R] output gradient of the layer
+ *   X         in   fp16 [T, C] input of the layer
+ *   W         in   fp16 [R, C] dense weight, or NULL (no decay term)
+ *   idx       in   uint8 [R/4, C/4] pattern indices (values >= 90 read as 0),
+ *                  NULL exactly when W is NULL
+ *   decay          the decay factor (fp32)
+ *   T, R, C        T >= 0; R, C >= 0, multiples of 16; T*R and T*C < 2^30
+ *   dW        out  fp32 [R, C] (written, not accumulated).  T == 0 gives the
+ *                  decay term alone (zeros without W).
+ * Results are deterministic: every output element is reduced by one
+ * workgroup in a fixed order.
+ * Errors: NULL (also exactly one of W and idx given), SHAPE, ALIGN,
+ * TOO_LARGE, LAUNCH.
+ */
+int sp24_weight_grad(const void* dY, const void* X, const void* W, const uint8_t* idx, float decay,
+                     int64_t T, int64_t R, int64_t C, float* dW, void* stream);
+
 /* Host only: a static, human-readable name for a status code. */
 const char* sp24_status_str(int status);
 
@@ -213,7 +243,7 @@ const char* sp24_status_str(int status);
  */
 int sp24_pattern_table(uint16_t* out);
 
-/* Host only: the library's ABI version (2 for this header). */
+/* Host only: the library's ABI version (3 for this header). */
 int sp24_abi_version(void);
 
 #ifdef __cplusplus

@@ -141,6 +141,24 @@ int sp24_spmm_bwd_input(const void* dY, const void* vals_col, const uint16_t* me
   return spmm_common(dY, vals_col, meta_col, T, C, R, dX, stream);
 }
 
+int sp24_weight_grad(const void* dY, const void* X, const void* W, const uint8_t* idx, float decay, int64_t T,
+                     int64_t R, int64_t C, float* dW, void* stream) {
+  if (T < 0) return SP24_ERR_SHAPE;
+  int st = check_dims(R, C, 16);
+  if (st != SP24_OK) return st;
+  if (T >= kMaxDim) return SP24_ERR_TOO_LARGE;
+  // token-row offsets of the direct loads are 32-bit byte offsets
+  if (T != 0 && (R >= ((int64_t)1 << 30) / T || C >= ((int64_t)1 << 30) / T)) return SP24_ERR_TOO_LARGE;
+  if ((W == nullptr) != (idx == nullptr)) return SP24_ERR_NULL;
+  if (R == 0 || C == 0) return SP24_OK;
+  if (dW == nullptr || (T != 0 && (dY == nullptr || X == nullptr))) return SP24_ERR_NULL;
+  if (!aligned16(dW) || (T != 0 && (!aligned16(dY) || !aligned16(X))) || (W && (!aligned16(W) || !aligned16(idx))))
+    return SP24_ERR_ALIGN;
+  return launch_status(sp24::launch_weight_grad(static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(X),
+                                                static_cast<const uint16_t*>(W), idx, decay, T, R, C, dW,
+                                                as_stream(stream)));
+}
+
 const char* sp24_status_str(int status) {
   switch (status) {
     case SP24_OK: return "ok";
@@ -160,6 +178,6 @@ int sp24_pattern_table(uint16_t* out) {
   return SP24_OK;
 }
 
-int sp24_abi_version(void) { return 2; }
+int sp24_abi_version(void) { return 3; }
 
 }  // extern "C"

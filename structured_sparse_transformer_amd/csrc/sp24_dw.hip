@@ -1,0 +1,357 @@
+// Weight gradient of a 2:4 FFN linear layer with the masked decay term, for
+// gfx950 matrix cores.
+//
+//   dW[r][c] = sum_t dY[t][r] * X[t][c]  +  decay * (1 - M[r][c]) * W[r][c]
+//
+// "Accelerating Transformer Pre-training with 2:4 Sparsity": the abstract
+// modifies the sparse-refined straight-through estimator by applying the
+// masked decay term on gradients, and the reproducibility table's "Software
+// Dependencies" row lists a masked-decay kernel.  The straight-through
+// gradient of the dense weight is the dense product dY^T X; the decay term
+// (M the transposable mask, 1 where kept) is added to it in the epilogue, so
+// the gradient is written once.  Output fp32 [R][C].
+//
+// The reduction runs over tokens, the slow axis of both operands in HBM
+// (dY [T][R], X [T][C]), so neither operand is contiguous along K.  Rows of
+// both are copied as they are into LDS by direct global->LDS loads, and the
+// gfx950 transpose read ds_read_b64_tr_b16 turns them into MFMA fragments:
+// within each 16-lane group it hands lane i element i of four 16-half rows,
+// row j being the 8-byte chunks addressed by lanes 4j .. 4j+3.  Lane i of a
+// group therefore addresses LDS row k0 + i/4 at column m0 + 4*(i%4), and
+// receives A[m0 + i][k0 .. k0+3].
+//
+// v_mfma_f32_32x32x16_f16 operands (lane l, g = l / 32):
+//   A: row l % 32 (the weight row r), k in [8g, 8g + 8)   (two transpose reads)
+//   B: column l % 32 (the weight column c), k in [8g, 8g + 8)
+//   D: column l % 32, rows 8*(i/4) + 4g + i%4 for accumulator i
+// Each group of four accumulators is four consecutive rows of one column
+// inside one 4x4 mask block, which the decay epilogue uses.
+//
+// Tiling: a workgroup computes BM rows x BN columns of dW with four waves
+// (one per SIMD) of WM x WN, K (tokens) in stages of 32 through a 3-stage
+// LDS ring filled two stages ahead.  Rows of dY/X past T read as zero (buffer
+// bounds); columns past R or C feed only outputs that are not stored.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "sp24_device.hpp"
+#include "sp24_internal.hpp"
+#include "sp24_patterns.hpp"
+
+namespace sp24 {
+namespace {
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4 lds_s4;
+
+constexpr int kBK = 32;   // tokens per stage
+
+struct MaskTable {
+  uint16_t mask[kNumPatterns + 2];   // kept entries of each pattern, bit 4r+c
+};
+constexpr MaskTable build_mask_table() {
+  MaskTable t{};
+  for (int p = 0; p < kNumPatterns; ++p) t.mask[p] = kTables.mask[p];
+  return t;
+}
+__constant__ MaskTable g_masks = build_mask_table();
+
+template <int BM, int BN, int WM, int WN>
+struct DwCfg {
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int A_BYTES = kBK * BM * 2, B_BYTES = kBK * BN * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = A_BYTES / 1024, B_LOADS = B_BYTES / 1024;   // 1 KiB direct loads
+  static constexpr int NLOADS = A_LOADS + B_LOADS;
+  static constexpr int LOADS_HI = (NLOADS + WAVES - 1) / WAVES;   // per wave (the first NLOADS % WAVES waves)
+  static constexpr int LOADS_LO = NLOADS / WAVES;
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % WM == 0 && BN % WN == 0, "tile shape");
+  static_assert(BM % 16 == 0 && BN % 16 == 0, "rows must split into whole direct loads");
+  static_assert(LOADS_HI <= 15, "vmcnt immediate");
+  static constexpr size_t SMEM = 3 * (size_t)STAGE + sizeof(MaskTable);
+};
+
+// LDS row layout of a stage: a row of `slots` 16-byte chunks (the chunk of
+// columns 8q .. 8q+7 is q) stores chunk q at slot (q + rot(row & 3)) % slots.
+// A transpose read touches 32 bytes (two chunks, q even) in each of four
+// consecutive rows; the rotation puts those four windows on disjoint banks:
+// their byte offsets modulo 128 are distinct multiples of 32.
+constexpr int rot_slots(int row_bytes, int j) { return (row_bytes % 128 == 0) ? 2 * j : 2 * (j >> 1); }
+static_assert((3 * 512 + 16 * rot_slots(512, 3)) % 128 == 96 && (3 * 320 + 16 * rot_slots(320, 3)) % 128 == 96 &&
+                  (2 * 320 + 16 * rot_slots(320, 2)) % 128 == 32 && (1 * 320 + 16 * rot_slots(320, 1)) % 128 == 64,
+              "row windows must fall on distinct banks");
+
+// vmcnt wait (expcnt and lgkmcnt not waited for)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void weight_grad_kernel(
+    const uint16_t* __restrict__ dY, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+    const uint8_t* __restrict__ idx, float decay, int64_t T, int64_t R, int64_t C, float* __restrict__ dW,
+    int tiles_m, int tiles_n) {
+  using Cfg = DwCfg<BM, BN, WM, WN>;
+  __shared__ __align__(1024) unsigned char smem[Cfg::SMEM];
+  MaskTable* masks = reinterpret_cast<MaskTable*>(smem + 3 * Cfg::STAGE);
+
+  // tile order: groups of 8 row tiles, column tiles within a group; each XCD
+  // (workgroups are dealt round-robin to 8 XCDs) takes a contiguous run
+  constexpr int kGroupM = 8;
+  const int ntiles = tiles_m * tiles_n;
+  const int per_xcd = (ntiles + 7) / 8;
+  const int lin = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (lin >= ntiles) return;
+  const int group = lin / (kGroupM * tiles_n);
+  const int gm0 = group * kGroupM;
+  const int gsize = min(kGroupM, tiles_m - gm0);
+  const int in_group = lin - group * kGroupM * tiles_n;
+  const int tn = __builtin_amdgcn_readfirstlane(in_group / gsize);
+  const int tm = __builtin_amdgcn_readfirstlane(gm0 + in_group % gsize);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % Cfg::WAVES_M, wn = wave / Cfg::WAVES_M;
+  const int nk = (int)((T + kBK - 1) / kBK);
+
+  if (tid < (int)(sizeof(MaskTable) / 4))
+    reinterpret_cast<uint32_t*>(masks)[tid] = reinterpret_cast<const uint32_t*>(&g_masks)[tid];
+
+  // buffer descriptors from this tile's first column to the matrix end;
+  // bytes past it (token rows beyond T) load as zero
+  const i32x4 ra = make_rsrc(dY + m0, (uint32_t)((T * R - m0) * 2));
+  const i32x4 rb = make_rsrc(X + n0, (uint32_t)((T * C - n0) * 2));
+
+  // This wave's direct loads: loads w, w + WAVES, ... of a stage.  Load j
+  // fills LDS slots 64j .. 64j+63 (16 bytes each) of the stage, A rows first;
+  // each lane fetches the chunk that the rotation puts in its slot.
+  const int nl = wave < Cfg::NLOADS % Cfg::WAVES ? Cfg::LOADS_HI : Cfg::LOADS_LO;
+  int goff[Cfg::LOADS_HI];
+#pragma unroll
+  for (int u = 0; u < Cfg::LOADS_HI; ++u) {
+    const int j = wave + u * Cfg::WAVES;
+    goff[u] = 0;
+    if (j < Cfg::A_LOADS) {
+      constexpr int n = BM / 8;
+      const int s = 64 * j + lane, row = s / n, slot = s % n;
+      goff[u] = row * (int)R * 2 + ((slot + n - rot_slots(2 * BM, row & 3)) % n) * 16;
+    } else if (j < Cfg::NLOADS) {
+      constexpr int n = BN / 8;
+      const int s = 64 * (j - Cfg::A_LOADS) + lane, row = s / n, slot = s % n;
+      goff[u] = row * (int)C * 2 + ((slot + n - rot_slots(2 * BN, row & 3)) % n) * 16;
+    }
+  }
+  auto issue_one = [&](int u, int kt, int slot_ring) {
+    const int j = wave + u * Cfg::WAVES;
+    const uint32_t dst = lds_addr(smem) + slot_ring * Cfg::STAGE + 1024 * j;
+    if (j < Cfg::A_LOADS)
+      dma_b128(ra, dst, goff[u] + kt * kBK * (int)R * 2);
+    else
+      dma_b128(rb, dst, goff[u] + kt * kBK * (int)C * 2);
+  };
+  auto issue = [&](int kt, int slot_ring) {
+#pragma unroll
+    for (int u = 0; u < Cfg::LOADS_HI; ++u)
+      if (u < nl) issue_one(u, kt, slot_ring);
+  };
+  // allow `stages` stages of this wave's loads to stay in flight
+  auto wait_loads = [&](int stages) {
+    if (stages == 0) {
+      wait_vm<0>();
+    } else if (nl == Cfg::LOADS_HI) {
+      if (stages >= 2) wait_vm<2 * Cfg::LOADS_HI>(); else wait_vm<Cfg::LOADS_HI>();
+    } else {
+      if (stages >= 2) wait_vm<2 * Cfg::LOADS_LO>(); else wait_vm<Cfg::LOADS_LO>();
+    }
+  };
+
+  // transpose-read offsets of this lane inside a stage, per 32-row block:
+  // lane i of 16-lane group G addresses row 8*(G/2) + i/4 (+ 16 per k16 step,
+  // + 4 for the second half) at column 32*block + 16*(G%2) + 4*(i%4)
+  const int G = lane >> 4, i16 = lane & 15, j4 = i16 >> 2, c4 = i16 & 3;
+  const int krow = 8 * (G >> 1) + j4;
+  int a_off[Cfg::TM], b_off[Cfg::TN];
+#pragma unroll
+  for (int mt = 0; mt < Cfg::TM; ++mt) {
+    constexpr int n = BM / 8;
+    const int q = (wm * WM + mt * 32 + 16 * (G & 1)) / 8 + (c4 >> 1);
+    a_off[mt] = krow * (2 * BM) + ((q + rot_slots(2 * BM, j4)) % n) * 16 + (c4 & 1) * 8;
+  }
+#pragma unroll
+  for (int nt = 0; nt < Cfg::TN; ++nt) {
+    constexpr int n = BN / 8;
+    const int q = (wn * WN + nt * 32 + 16 * (G & 1)) / 8 + (c4 >> 1);
+    b_off[nt] = Cfg::A_BYTES + krow * (2 * BN) + ((q + rot_slots(2 * BN, j4)) % n) * 16 + (c4 & 1) * 8;
+  }
+
+  f16v acc[Cfg::TM][Cfg::TN];
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  struct Frags {
+    h8 a[Cfg::TM];
+    h8 b[Cfg::TN];
+  };
+  auto tr_read = [&](int byte) -> h4 {
+    return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)((lds_u8*)smem + byte)));
+  };
+  // fragments of k16 step ks (0 or 1) of the stage in ring slot `sl`
+  auto load_frags = [&](int sl, int ks, Frags& f) {
+    const int base = sl * Cfg::STAGE;
+#pragma unroll
+    for (int mt = 0; mt < Cfg::TM; ++mt) {
+      const int o = base + a_off[mt] + ks * 16 * (2 * BM);
+      const h4 lo = tr_read(o), hi = tr_read(o + 4 * (2 * BM));
+      f.a[mt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int nt = 0; nt < Cfg::TN; ++nt) {
+      const int o = base + b_off[nt] + ks * 16 * (2 * BN);
+      const h4 lo = tr_read(o), hi = tr_read(o + 4 * (2 * BN));
+      f.b[nt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  // the MFMAs of one k16 step; when kt_load >= 0 this wave's direct loads of
+  // stage kt_load go out one per MFMA so the texture path drains steadily
+  auto mfmas = [&](const Frags& f, int kt_load, int slot_ring) {
+#pragma unroll
+    for (int mt = 0; mt < Cfg::TM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < Cfg::TN; ++nt) {
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mt], f.b[nt], acc[mt][nt], 0, 0, 0);
+        const int u = mt * Cfg::TN + nt;
+        if (u < Cfg::LOADS_HI && kt_load >= 0 && u < nl) issue_one(u, kt_load, slot_ring);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+    for (int u = Cfg::TM * Cfg::TN; u < Cfg::LOADS_HI; ++u)
+      if (kt_load >= 0 && u < nl) issue_one(u, kt_load, slot_ring);
+  };
+
+  if (nk > 0) {
+    // Pipeline: stage s goes to ring slot s % 3, three stages ahead.  In
+    // stage kt the second k16 step's fragments are read during the first
+    // step's MFMAs; mid-stage the wave waits for stage kt+1, all waves meet
+    // (nobody reads slot kt % 3 afterwards), stage kt+3 is issued into it,
+    // and stage kt+1's first fragments are read during the second step.
+    for (int s = 0; s < 3; ++s)
+      if (s < nk) issue(s, s);
+    wait_loads(min(nk, 3) - 1);
+    __builtin_amdgcn_s_barrier();
+    Frags f0, f1;
+    load_frags(0, 0, f0);
+    auto stage = [&](int kt, int cur, int nxt) {
+      load_frags(cur, 1, f1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(f0, -1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_loads(kt + 2 < nk ? 1 : 0);
+      // lgkmcnt(0): this wave's reads of slot kt % 3 are done before the
+      // barrier lets stage kt+3 overwrite it
+      __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
+      __builtin_amdgcn_s_barrier();
+      if (kt + 1 < nk) load_frags(nxt, 0, f0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(f1, kt + 3 < nk ? kt + 3 : -1, cur);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int kt = 0; kt < nk; kt += 3) {
+      stage(kt, 0, 1);
+      if (kt + 1 < nk) stage(kt + 1, 1, 2);
+      if (kt + 2 < nk) stage(kt + 2, 2, 0);
+    }
+  }
+  __syncthreads();   // the mask table is visible (and the ring idle)
+
+  // Epilogue: each group of four accumulators is rows r4 .. r4+3 (one mask
+  // block row) of column c; add the decay term to the pruned entries.
+  const int l32 = lane & 31, g = lane >> 5;
+  const bool with_decay = W != nullptr;
+#pragma unroll
+  for (int mt = 0; mt < Cfg::TM; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < Cfg::TN; ++nt) {
+      const int64_t c = n0 + wn * WN + nt * 32 + l32;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int64_t r4 = m0 + wm * WM + mt * 32 + 8 * i4 + 4 * g;
+        if (r4 >= R || c >= C) continue;
+        float v[4] = {acc[mt][nt][4 * i4], acc[mt][nt][4 * i4 + 1], acc[mt][nt][4 * i4 + 2], acc[mt][nt][4 * i4 + 3]};
+        if (with_decay) {
+          uint32_t p = idx[(r4 / 4) * (C / 4) + c / 4];
+          p = p < (uint32_t)kNumPatterns ? p : 0u;
+          const uint32_t kept = (uint32_t)masks->mask[p] >> (c & 3);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!((kept >> (4 * e)) & 1u)) {
+              const float w = (float)__builtin_bit_cast(_Float16, W[(r4 + e) * C + c]);
+              v[e] = v[e] + decay * w;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dW[(r4 + e) * C + c] = v[e];
+      }
+    }
+}
+
+struct DwShape {
+  int bm, bn;
+};
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_dw(const uint16_t* dY, const uint16_t* X, const uint16_t* W, const uint8_t* idx, float decay,
+                     int64_t T, int64_t R, int64_t C, float* dW, hipStream_t s) {
+  using Cfg = DwCfg<BM, BN, WM, WN>;
+  const int tiles_m = (int)((R + BM - 1) / BM), tiles_n = (int)((C + BN - 1) / BN);
+  const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
+  hipLaunchKernelGGL((weight_grad_kernel<BM, BN, WM, WN>), dim3(grid), dim3(Cfg::THREADS), 0, s, dY, X, W, idx, decay,
+                     T, R, C, dW, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_weight_grad(const uint16_t* dY, const uint16_t* X, const uint16_t* W, const uint8_t* idx,
+                              float decay, int64_t T, int64_t R, int64_t C, float* dW, hipStream_t s) {
+  if (R == 0 || C == 0) return hipSuccess;
+  // Tile shape: each candidate's time is modelled as (rounds of one tile per
+  // CU) x (tile area / relative speed of the shape); the cheapest wins.  The
+  // 256 x 160 shapes fill 256 CUs with a GPT-2-1.5B FFN weight (6400 x 1600)
+  // in one round, which a 256 x 256 tile leaves 32 % idle.
+  struct Cand {
+    int bm, bn;
+    double speed;
+  };
+  const Cand cands[] = {{256, 256, 1.0}, {256, 160, 0.9}, {160, 256, 0.9}, {128, 128, 0.75}};
+  const int64_t cus = device_cu_count();
+  int best = 0;
+  double best_t = 0.0;
+  for (int k = 0; k < 4; ++k) {
+    const int64_t tiles = ((R + cands[k].bm - 1) / cands[k].bm) * ((C + cands[k].bn - 1) / cands[k].bn);
+    const double t = (double)((tiles + cus - 1) / cus) * cands[k].bm * cands[k].bn / cands[k].speed;
+    if (k == 0 || t < best_t) {
+      best = k;
+      best_t = t;
+    }
+  }
+  switch (best) {
+    case 0: return launch_dw<256, 256, 128, 128>(dY, X, W, idx, decay, T, R, C, dW, s);
+    case 1: return launch_dw<256, 160, 64, 160>(dY, X, W, idx, decay, T, R, C, dW, s);
+    case 2: return launch_dw<160, 256, 160, 64>(dY, X, W, idx, decay, T, R, C, dW, s);
+    default: return launch_dw<128, 128, 64, 64>(dY, X, W, idx, decay, T, R, C, dW, s);
+  }
+}
+
+}  // namespace sp24

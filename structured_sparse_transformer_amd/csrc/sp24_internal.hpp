@@ -45,6 +45,12 @@ hipError_t launch_search_compress(const uint16_t* W, int64_t R, int64_t C, const
 hipError_t launch_flip_count(const uint8_t* a, const uint8_t* b, int64_t n, unsigned long long* flips,
                              hipStream_t s);
 
+// dW[R][C] (fp32) = dY[T][R]^T X[T][C] + decay * (1 - M) * W, M from idx;
+// W == nullptr leaves the decay term out.  R, C multiples of 16; T*R and T*C
+// below 2^30.
+hipError_t launch_weight_grad(const uint16_t* dY, const uint16_t* X, const uint16_t* W, const uint8_t* idx,
+                              float decay, int64_t T, int64_t R, int64_t C, float* dW, hipStream_t s);
+
 // out[T][N] = A[T][K] * S[N][K]^T with S in 2:4 row form along K:
 // vals [N][K/2] fp16, meta [N][K/16].  N, K multiples of 16.
 hipError_t launch_spmm_nt(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T,

@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "sp24_device.hpp"
 #include "sp24_internal.hpp"
 
 namespace sp24 {
@@ -252,39 +253,6 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* vals, const uint16_t* m
 //   meta [BM rows][2 dwords]
 // A direct load writes 64 consecutive 16-byte LDS slots, one per lane, so each
 // lane fetches the global chunk whose swizzled slot is its own lane index.
-
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, gfx9 family
-
-// Raw buffer descriptor over [base, base + bytes), kept in scalar registers.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);   // stride 0
-  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-  r[3] = (int)kRsrcWord3;
-  return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_u8*)p;
-}
-
-// Direct global->LDS loads: lane l's bytes land at LDS address M0 + l * size.
-// Written as asm so that the compiler's wait-count pass does not make every
-// later LDS read wait for all outstanding loads (it cannot tell the stage
-// buffers apart); completion is tracked with explicit vmcnt waits instead.
-// The LDS address is an input bound to M0, so the compiler sets M0; the asm
-// has no register outputs, and its s_nop 0 covers the M0-write hazard.
-__device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t lds, int voffset) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voffset), "s"(rsrc), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void dma_b32(i32x4 rsrc, uint32_t lds, int voffset) {
-  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" : : "v"(voffset), "s"(rsrc), "{m0}"(lds) : "memory");
-}
 
 __device__ __forceinline__ int swz_s(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 __device__ __forceinline__ int swz_b(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -571,18 +539,6 @@ hipError_t launch_fast(const uint16_t* A, const uint16_t* vals, const uint16_t* 
   hipLaunchKernelGGL((spmm_nt_fast_kernel<BM, BN, WM, WN>), dim3(grid), dim3(Cfg::THREADS), 0, s, A, vals, meta, T, N,
                      K, out, ldo, tiles_m, tiles_n);
   return hipGetLastError();
-}
-
-int device_cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
 }
 
 }  // namespace

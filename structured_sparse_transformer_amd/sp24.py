@@ -25,7 +25,7 @@ SP24_OK = 0
 STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_LAUNCH",
                 5: "ERR_UNSUPPORTED", 6: "ERR_TOO_LARGE"}
 EXPORTS = ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
-           "sp24_flip_count", "sp24_spmm_fwd", "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table",
+           "sp24_flip_count", "sp24_weight_grad", "sp24_spmm_fwd", "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table",
            "sp24_abi_version")
 MAX_BATCH = 8
 
@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
             "sp24_search_compress": [p, i64, i64, p, p, p, p, p, p],
             "sp24_search_compress_batch": [p, i32, p],
             "sp24_flip_count": [p, p, i64, p, p],
+            "sp24_weight_grad": [p, p, p, p, ctypes.c_float, i64, i64, i64, p, p],
             "sp24_spmm_fwd": [p, p, p, i64, i64, i64, p, p],
             "sp24_spmm_bwd_input": [p, p, p, i64, i64, i64, p, p],
             "sp24_status_str": [i32],
@@ -206,6 +207,22 @@ def sp24_flip_count(idx_prev, idx_new, flips=None, stream=None):
     _check("sp24_flip_count", lib().sp24_flip_count(_ptr(idx_prev), _ptr(idx_new), idx_new.numel(),
                                                     _flip_counter(flips), _stream(stream)))
     return flips
+
+
+def sp24_weight_grad(dY, X, W=None, idx=None, decay=0.0, dW=None, stream=None):
+    """dW[R, C] (float32) = dY^T X + decay * (1 - M) * W, M the masks ``idx``."""
+    T, R = dY.shape
+    C = X.shape[1]
+    if dY.dtype != torch.float16 or X.dtype != torch.float16 or X.shape[0] != T:
+        raise ValueError("dY and X must be float16 [T, R] and [T, C]")
+    if W is not None and (W.dtype != torch.float16 or tuple(W.shape) != (R, C)):
+        raise ValueError("W must be float16 [R, C]")
+    if idx is not None and (idx.dtype != torch.uint8 or tuple(idx.shape) != (R // 4, C // 4)):
+        raise ValueError("idx must be uint8 [R/4, C/4]")
+    dW = _out(dW, (R, C), torch.float32, dY.device)
+    _check("sp24_weight_grad", lib().sp24_weight_grad(_ptr(dY), _ptr(X), _ptr(W), _ptr(idx), float(decay), T, R, C,
+                                                      _ptr(dW), _stream(stream)))
+    return dW
 
 
 def sp24_spmm_fwd(X, vals_row, meta_row, R, C, Y=None, stream=None):

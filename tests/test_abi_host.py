@@ -38,7 +38,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
-              "sp24_flip_count", "sp24_spmm_fwd",
+              "sp24_flip_count", "sp24_weight_grad", "sp24_spmm_fwd",
               "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table", "sp24_abi_version"):
         assert n in names
 
@@ -58,7 +58,7 @@ def test_pattern_table_matches_oracle(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sp24_abi_version() == 2
+    assert L.sp24_abi_version() == 3
     for s in range(7):
         assert L.sp24_status_str(s)
     assert L.sp24_status_str(99) == b"unknown status"
@@ -174,3 +174,20 @@ def test_flip_count_validation(L):
     assert f(FAKE, MIS, 4, FAKE, NUL) == 3
     assert f(FAKE, FAKE, 4, ctypes.c_void_p(0x1004), NUL) == 3
     assert f(NUL, NUL, 0, NUL, NUL) == 0
+
+
+def test_weight_grad_validation(L):
+    f = L.sp24_weight_grad
+    c = ctypes.c_float(0.5)
+    assert f(FAKE, FAKE, FAKE, FAKE, c, 8, 16, 20, FAKE, NUL) == 2          # C % 16
+    assert f(FAKE, FAKE, FAKE, FAKE, c, -1, 16, 16, FAKE, NUL) == 2
+    assert f(FAKE, FAKE, FAKE, NUL, c, 8, 16, 16, FAKE, NUL) == 1           # W without idx
+    assert f(FAKE, FAKE, NUL, FAKE, c, 8, 16, 16, FAKE, NUL) == 1
+    assert f(NUL, FAKE, NUL, NUL, c, 8, 16, 16, FAKE, NUL) == 1
+    assert f(FAKE, FAKE, NUL, NUL, c, 8, 16, 16, NUL, NUL) == 1
+    assert f(MIS, FAKE, NUL, NUL, c, 8, 16, 16, FAKE, NUL) == 3
+    assert f(FAKE, FAKE, NUL, NUL, c, 8, 16, 16, MIS, NUL) == 3
+    assert f(FAKE, FAKE, MIS, FAKE, c, 8, 16, 16, FAKE, NUL) == 3
+    assert f(FAKE, FAKE, NUL, NUL, c, 1 << 20, 1024, 16, FAKE, NUL) == 6    # T*R >= 2^30
+    assert f(FAKE, FAKE, NUL, NUL, c, 1 << 20, 16, 1024, FAKE, NUL) == 6
+    assert f(NUL, NUL, NUL, NUL, c, 8, 0, 16, NUL, NUL) == 0                # empty output
