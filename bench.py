@@ -40,6 +40,7 @@ HBM_PEAK_GBPS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0      # dense fp16 matrix-core peak of MI355X
 SC_BYTES_PER_ELEM = 4.375           # read W 2 and previous idx 1/16; write idx 1/16, two 2:4 forms 2 x (1 + 1/8)
 COUNTERS = os.path.join(ROOT, "profiles", "spmm_nt_gpt2-1.5b_counters.json")
+DECAY = 2e-4                         # masked decay factor of the weight-gradient leg
 GEMM_SRC = os.path.join(ROOT, "structured_sparse_transformer_amd", "csrc", "sp24_spmm.hip")
 
 
@@ -118,6 +119,16 @@ def profile_only(args, sp24, torch, dev, cfg, F1, F2, FL, W1s, W2s, X, dY1, H, d
         torch.cuda.synchronize()
         log(f"copy: {n} x 512 MiB")
         return
+    if args.profile_kernel == "weight_grad":
+        sp24.sp24_search_compress_batch([W1s[0], W2s[0]], outs=[F1, F2])
+        dW1 = torch.empty(d * 4, d, dtype=torch.float32, device=dev)
+        dW2 = torch.empty(d, d * 4, dtype=torch.float32, device=dev)
+        for _ in range(n):
+            sp24.sp24_weight_grad(dY1, X, W1s[0], F1["idx"], DECAY, dW=dW1)
+            sp24.sp24_weight_grad(dY2, H, W2s[0], F2["idx"], DECAY, dW=dW2)
+        torch.cuda.synchronize()
+        log(f"weight_grad: {n} rounds")
+        return
     if args.profile_kernel == "flip_count":
         prev = F1["idx"].clone()
         sp24.sp24_search_compress_batch([W1s[0], W2s[0]], outs=[F1, F2])
@@ -150,7 +161,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy context numbers")
-    ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "flip_count", "copy"],
+    ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "flip_count", "weight_grad", "copy"],
                     help="run only this kernel --steps times (for rocprofv3 counter passes); prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -269,6 +280,30 @@ def main():
     torch.cuda.synchronize()
     fl_us = e0.elapsed_time(e1) * 1e3 / fl_calls
     fl_bytes = 2 * F1["idx"].numel()
+
+    # next row: the weight gradients of both linears with the masked decay
+    # term (dense fp16 MFMA, fp32 out), timed back to back after the step
+    dW1 = torch.empty(f, d, dtype=torch.float32, device=dev)
+    dW2 = torch.empty(d, f, dtype=torch.float32, device=dev)
+    wg = lambda: (sp24.sp24_weight_grad(dY1, X, W1s[-1], F1["idx"], DECAY, dW=dW1),  # noqa: E731
+                  sp24.sp24_weight_grad(dY2, H, W2s[-1], F2["idx"], DECAY, dW=dW2))
+    wg()
+    torch.cuda.synchronize()
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    wg_ms = np.zeros(2)
+    wg_reps = 5
+    for _ in range(wg_reps):
+        wev[0].record()
+        sp24.sp24_weight_grad(dY1, X, W1s[-1], F1["idx"], DECAY, dW=dW1)
+        wev[1].record()
+        sp24.sp24_weight_grad(dY2, H, W2s[-1], F2["idx"], DECAY, dW=dW2)
+        wev[2].record()
+        torch.cuda.synchronize()
+        wg_ms += [wev[0].elapsed_time(wev[1]), wev[1].elapsed_time(wev[2])]
+    wg_ms /= wg_reps
+    wg_flops = 2 * T * f * d
+    wg_tflops = [wg_flops / (ms * 1e-3) / 1e12 for ms in wg_ms]
+    wg_achieved = wg_flops / (float(np.mean(wg_ms)) * 1e-3) / 1e12
     flops_step = cfg.dense_equiv_flops()
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
@@ -289,6 +324,17 @@ def main():
         ms = e0.elapsed_time(e1) / 10
         context["dense_torch_matmul_fp16_TFLOPs"] = round(2 * T * f * d / (ms * 1e-3) / 1e12, 1)
         context["dense_torch_matmul_ms"] = round(ms, 4)
+        # the library's dense weight-gradient product, dY1^T X, fp16 out
+        dYt = dY1.t()
+        torch.matmul(dYt, X)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            torch.matmul(dYt, X)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        context["dense_torch_matmul_dYT_X_fp16_TFLOPs"] = round(2 * T * f * d / (ms * 1e-3) / 1e12, 1)
         src = torch.empty(512 * 1024 * 1024 // 2, dtype=torch.float16, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -340,6 +386,12 @@ def main():
                      "traffic": traffic,
                      "note": "executed non-zero flops T*N*K per launch (half the dense-equivalent 2*T*N*K) over the "
                              "dense fp16 MFMA peak; equal to dense-equivalent flops over the 2:4 sparse peak"},
+        "weight_grad": {"definition": "dW = dY^T X + decay * (1 - M) * W, fp16 in, fp32 out (sp24_weight_grad)",
+                        "decay": DECAY, "us": {"dW1": round(wg_ms[0] * 1e3, 1), "dW2": round(wg_ms[1] * 1e3, 1)},
+                        "TFLOPs": {"dW1": round(wg_tflops[0], 1), "dW2": round(wg_tflops[1], 1)},
+                        "roofline": {"bound": "mfma", "achieved": round(wg_achieved, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(wg_achieved / FP16_MFMA_PEAK_TFLOPS, 4),
+                                     "note": "2*T*R*C flops per launch (dense product) over the dense fp16 MFMA peak"}},
         "cpu_baseline": cpu,
         "context": context,
     }

@@ -79,13 +79,23 @@ struct DwCfg {
 
 // LDS row layout of a stage: a row of `slots` 16-byte chunks (the chunk of
 // columns 8q .. 8q+7 is q) stores chunk q at slot (q + rot(row & 3)) % slots.
-// A transpose read touches 32 bytes (two chunks, q even) in each of four
-// consecutive rows; the rotation puts those four windows on disjoint banks:
-// their byte offsets modulo 128 are distinct multiples of 32.
-constexpr int rot_slots(int row_bytes, int j) { return (row_bytes % 128 == 0) ? 2 * j : 2 * (j >> 1); }
-static_assert((3 * 512 + 16 * rot_slots(512, 3)) % 128 == 96 && (3 * 320 + 16 * rot_slots(320, 3)) % 128 == 96 &&
-                  (2 * 320 + 16 * rot_slots(320, 2)) % 128 == 32 && (1 * 320 + 16 * rot_slots(320, 1)) % 128 == 64,
-              "row windows must fall on distinct banks");
+// The LDS serves 32 lanes of a read per cycle from 64 four-byte banks, and
+// the 32 lanes of a transpose read fetch two 32-byte windows (q even, and
+// q + 2) in each of four consecutive rows.  The rotation makes the window
+// offsets of rows j = 0..3 congruent to 64*j bytes modulo 256, so the eight
+// windows cover the 64 banks once (checked for the row sizes used below).
+constexpr int rot_slots(int row_bytes, int j) { return ((4 - row_bytes / 16) * j % 16 + 16) % 16; }
+constexpr bool windows_disjoint(int row_bytes) {
+  bool used[16] = {};
+  for (int j = 0; j < 4; ++j)
+    for (int p = 0; p < 2; ++p) {
+      const int slot = (j * row_bytes / 16 + rot_slots(row_bytes, j) + 2 * p) % 16;
+      if (used[slot] || used[(slot + 1) % 16]) return false;
+      used[slot] = used[(slot + 1) % 16] = true;
+    }
+  return true;
+}
+static_assert(windows_disjoint(512) && windows_disjoint(320) && windows_disjoint(256), "bank-disjoint windows");
 
 // vmcnt wait (expcnt and lgkmcnt not waited for)
 template <int N>
