@@ -56,10 +56,20 @@ What the method computes, and the readings taken where the pages are silent:
    ``decay * (1 - M) * W`` (M the searched transposable mask, 1 where kept) is
    added to that gradient rather than applied to the weights.  Computed in
    float64; the library returns float32.
+6. GEGLU [HZ24 abstract: accelerating gated activation functions; HZ24 SW:
+   a GEGLU kernel].  The pages name the operation only.  Reading: the gated
+   linear unit with a GELU gate, out = value * GELU(gate), GELU the exact
+   x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), on the first linear's output U
+   [T, 2h].  Column layout: blocks of G value columns followed by the G
+   matching gate columns (G = h is the two-halves layout; a small G keeps each
+   pair close together in memory).  The backward gives d value = dOut *
+   GELU(gate) and d gate = dOut * value * GELU'(gate), GELU'(x) = Phi(x) + x
+   phi(x).  Computed in float64.
 """
 from __future__ import annotations
 
 import itertools
+import math
 
 import numpy as np
 
@@ -265,6 +275,47 @@ def weight_grad(dY: np.ndarray, X: np.ndarray, W: np.ndarray | None, idx: np.nda
         pruned = 1.0 - idx_to_mask(idx).astype(np.float64)
         dW = dW + float(decay) * pruned * W.astype(np.float64)
     return dW
+
+
+def _geglu_split(U: np.ndarray, group: int):
+    """Value and gate columns of U [T, 2h] laid out in blocks of `group`."""
+    T, two_h = U.shape
+    if two_h % (2 * group) != 0:
+        raise ValueError("2h must be a multiple of 2 * group")
+    blocks = U.astype(np.float64).reshape(T, two_h // (2 * group), 2, group)
+    return blocks[:, :, 0, :].reshape(T, -1), blocks[:, :, 1, :].reshape(T, -1)
+
+
+_erf = np.vectorize(math.erf, otypes=[np.float64])
+
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """Exact GELU, x * Phi(x), in float64."""
+    return 0.5 * x * (1.0 + _erf(x / math.sqrt(2.0)))
+
+
+def gelu_grad(x: np.ndarray) -> np.ndarray:
+    """d GELU / dx = Phi(x) + x * phi(x)."""
+    return 0.5 * (1.0 + _erf(x / math.sqrt(2.0))) + x * np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def geglu_fwd(U: np.ndarray, group: int) -> np.ndarray:
+    """out [T, h] = value * GELU(gate) (item 6 above), float64."""
+    v, g = _geglu_split(U, group)
+    return v * gelu(g)
+
+
+def geglu_bwd(U: np.ndarray, dout: np.ndarray, group: int) -> np.ndarray:
+    """dU [T, 2h] in U's layout: d value = dout * GELU(gate), d gate =
+    dout * value * GELU'(gate) (item 6 above), float64."""
+    v, g = _geglu_split(U, group)
+    d = dout.astype(np.float64)
+    dv, dg = d * gelu(g), d * v * gelu_grad(g)
+    T, h = dv.shape
+    out = np.empty((T, h // group, 2, group))
+    out[:, :, 0, :] = dv.reshape(T, -1, group)
+    out[:, :, 1, :] = dg.reshape(T, -1, group)
+    return out.reshape(T, 2 * h)
 
 
 def gemm_errors(out: np.ndarray, ref: np.ndarray) -> tuple:

@@ -428,3 +428,50 @@ def test_weight_grad_special_cases():
     g3 = O.weight_grad(dY2, X2, W, idx, 3.0)
     assert np.allclose(g3 - g0, 3 * (g1 - g0), rtol=1e-12, atol=1e-12)
     assert (g0 == O.weight_grad(dY2, X2, None, None, 5.0)).all()
+
+
+# ----------------------------------------------------------------------------
+# GEGLU
+def test_gelu_closed_forms():
+    # GELU(0) = 0, GELU(x) - GELU(-x) = x, GELU'(0) = 1/2, GELU(x) -> x for
+    # large x and -> 0 for very negative x; Phi(1) = 0.841344746068543 (table)
+    x = np.array([0.0, 1.0, -1.0, 3.0, -3.0, 10.0, -10.0])
+    g = O.gelu(x)
+    assert g[0] == 0.0
+    assert abs(g[1] - 0.841344746068543) < 1e-15
+    assert np.allclose(g[1::2] - g[2::2], x[1::2], rtol=0, atol=1e-15)
+    assert abs(g[5] - 10.0) < 1e-15 and abs(g[6]) < 1e-20
+    assert O.gelu_grad(np.array([0.0]))[0] == 0.5
+
+
+def test_gelu_grad_matches_finite_differences():
+    x = np.linspace(-6, 6, 241)
+    h = 1e-6
+    fd = (O.gelu(x + h) - O.gelu(x - h)) / (2 * h)
+    assert np.allclose(O.gelu_grad(x), fd, rtol=0, atol=1e-8)
+
+
+def test_geglu_layouts_and_backward():
+    rng = np.random.default_rng(50)
+    T, h = 3, 8
+    v = rng.standard_normal((T, h))
+    g = rng.standard_normal((T, h))
+    # two halves (group = h): U = [v | g]
+    U = np.concatenate([v, g], axis=1)
+    assert np.allclose(O.geglu_fwd(U, h), v * O.gelu(g), rtol=0, atol=0)
+    # group 2: v0 v1 g0 g1 v2 v3 g2 g3 ...
+    U2 = np.concatenate([np.stack([v[:, 2 * b: 2 * b + 2], g[:, 2 * b: 2 * b + 2]], axis=1).reshape(T, 4)
+                         for b in range(h // 2)], axis=1)
+    assert (O.geglu_fwd(U2, 2) == O.geglu_fwd(U, h)).all()
+    # the backward is the gradient of sum(dout * out) with respect to U
+    dout = rng.standard_normal((T, h))
+    dU = O.geglu_bwd(U2, dout, 2)
+    eps = 1e-6
+    num = np.zeros_like(U2)
+    for t in range(T):
+        for c in range(2 * h):
+            up, dn = U2.copy(), U2.copy()
+            up[t, c] += eps
+            dn[t, c] -= eps
+            num[t, c] = ((dout * O.geglu_fwd(up, 2)).sum() - (dout * O.geglu_fwd(dn, 2)).sum()) / (2 * eps)
+    assert np.allclose(dU, num, rtol=0, atol=1e-7)
