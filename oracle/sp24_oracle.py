@@ -286,17 +286,23 @@ def _geglu_split(U: np.ndarray, group: int):
     return blocks[:, :, 0, :].reshape(T, -1), blocks[:, :, 1, :].reshape(T, -1)
 
 
-_erf = np.vectorize(math.erf, otypes=[np.float64])
+_erfc = np.vectorize(math.erfc, otypes=[np.float64])
+
+
+def _phi_cdf(x: np.ndarray) -> np.ndarray:
+    """Phi(x) = erfc(-x / sqrt 2) / 2, the form that keeps its relative
+    accuracy in the negative tail (1 + erf(x / sqrt 2) cancels there)."""
+    return 0.5 * _erfc(-x / math.sqrt(2.0))
 
 
 def gelu(x: np.ndarray) -> np.ndarray:
     """Exact GELU, x * Phi(x), in float64."""
-    return 0.5 * x * (1.0 + _erf(x / math.sqrt(2.0)))
+    return x * _phi_cdf(x)
 
 
 def gelu_grad(x: np.ndarray) -> np.ndarray:
     """d GELU / dx = Phi(x) + x * phi(x)."""
-    return 0.5 * (1.0 + _erf(x / math.sqrt(2.0))) + x * np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+    return _phi_cdf(x) + x * np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
 
 
 def geglu_fwd(U: np.ndarray, group: int) -> np.ndarray:

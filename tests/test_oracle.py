@@ -442,6 +442,8 @@ def test_gelu_closed_forms():
     assert np.allclose(g[1::2] - g[2::2], x[1::2], rtol=0, atol=1e-15)
     assert abs(g[5] - 10.0) < 1e-15 and abs(g[6]) < 1e-20
     assert O.gelu_grad(np.array([0.0]))[0] == 0.5
+    # the negative tail keeps full relative accuracy: Phi(-6) = 9.865876450377e-10 (table)
+    assert abs(O.gelu(np.array([-6.0]))[0] / -6.0 - 9.865876450377e-10) < 1e-12 * 9.865876450377e-10 * 100
 
 
 def test_gelu_grad_matches_finite_differences():
