@@ -41,6 +41,18 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0      # dense fp16 matrix-core peak of MI355X
 SC_BYTES_PER_ELEM = 4.375           # read W 2 and previous idx 1/16; write idx 1/16, two 2:4 forms 2 x (1 + 1/8)
 COUNTERS = os.path.join(ROOT, "profiles", "spmm_nt_gpt2-1.5b_counters.json")
 DECAY = 2e-4                         # masked decay factor of the weight-gradient leg
+GEGLU_GROUP = 16                     # GEGLU column layout: blocks of 16 values, then their 16 gates
+
+
+def geglu_inputs(torch, dev, cfg):
+    """GEGLU input of a gated FFN of the same width: U [T, 2 * 4d] (values and
+    gates in blocks of GEGLU_GROUP), dOut [T, 4d]; N(0, 1) draws made on the
+    device (a fixed torch seed) to keep the host side short."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    U = torch.randn(cfg.tokens, 2 * cfg.dff, generator=g, device=dev).half()
+    gd = torch.randn(cfg.tokens, cfg.dff, generator=g, device=dev).half()
+    return U, gd
 GEMM_SRC = os.path.join(ROOT, "structured_sparse_transformer_amd", "csrc", "sp24_spmm.hip")
 
 
@@ -119,6 +131,15 @@ def profile_only(args, sp24, torch, dev, cfg, F1, F2, FL, W1s, W2s, X, dY1, H, d
         torch.cuda.synchronize()
         log(f"copy: {n} x 512 MiB")
         return
+    if args.profile_kernel == "geglu":
+        U, gd = geglu_inputs(torch, dev, cfg)
+        out, dU = torch.empty_like(gd), torch.empty_like(U)
+        for _ in range(n):
+            sp24.sp24_geglu_fwd(U, GEGLU_GROUP, out=out)
+            sp24.sp24_geglu_bwd(U, gd, GEGLU_GROUP, dU=dU)
+        torch.cuda.synchronize()
+        log(f"geglu: {n} rounds")
+        return
     if args.profile_kernel == "weight_grad":
         sp24.sp24_search_compress_batch([W1s[0], W2s[0]], outs=[F1, F2])
         dW1 = torch.empty(d * 4, d, dtype=torch.float32, device=dev)
@@ -161,7 +182,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy context numbers")
-    ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "flip_count", "weight_grad", "copy"],
+    ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "flip_count", "weight_grad", "geglu",
+                                                 "copy"],
                     help="run only this kernel --steps times (for rocprofv3 counter passes); prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -281,6 +303,27 @@ def main():
     fl_us = e0.elapsed_time(e1) * 1e3 / fl_calls
     fl_bytes = 2 * F1["idx"].numel()
 
+    # next row: GEGLU forward and backward at the FFN width (HBM-bound)
+    U, gd = geglu_inputs(torch, dev, cfg)
+    g_out, g_dU = torch.empty_like(gd), torch.empty_like(U)
+    sp24.sp24_geglu_fwd(U, GEGLU_GROUP, out=g_out)
+    sp24.sp24_geglu_bwd(U, gd, GEGLU_GROUP, dU=g_dU)
+    torch.cuda.synchronize()
+    gev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    geglu_ms = np.zeros(2)
+    for _ in range(5):
+        gev[0].record()
+        sp24.sp24_geglu_fwd(U, GEGLU_GROUP, out=g_out)
+        gev[1].record()
+        sp24.sp24_geglu_bwd(U, gd, GEGLU_GROUP, dU=g_dU)
+        gev[2].record()
+        torch.cuda.synchronize()
+        geglu_ms += [gev[0].elapsed_time(gev[1]), gev[1].elapsed_time(gev[2])]
+    geglu_ms /= 5
+    units = T * f
+    geglu_gbps = [6 * units / (geglu_ms[0] * 1e-3) / 1e9, 10 * units / (geglu_ms[1] * 1e-3) / 1e9]
+    del U, gd, g_out, g_dU
+
     # next row: the weight gradients of both linears with the masked decay
     # term (dense fp16 MFMA, fp32 out), timed back to back after the step
     dW1 = torch.empty(f, d, dtype=torch.float32, device=dev)
@@ -392,6 +435,15 @@ def main():
                         "roofline": {"bound": "mfma", "achieved": round(wg_achieved, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
                                      "unit": "TFLOP/s", "frac": round(wg_achieved / FP16_MFMA_PEAK_TFLOPS, 4),
                                      "note": "2*T*R*C flops per launch (dense product) over the dense fp16 MFMA peak"}},
+        "geglu": {"definition": "out = value * GELU(gate) (exact erf GELU), and its backward; U [T, 2h] in blocks "
+                             "of 16 values then 16 gates (sp24_geglu_fwd / _bwd)",
+                  "shape": {"tokens": T, "h": f, "group": GEGLU_GROUP},
+                  "us": {"fwd": round(geglu_ms[0] * 1e3, 1), "bwd": round(geglu_ms[1] * 1e3, 1)},
+                  "GBps": {"fwd": round(geglu_gbps[0], 1), "bwd": round(geglu_gbps[1], 1)},
+                  "roofline": {"bound": "hbm", "achieved": round(geglu_gbps[1], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                               "frac": round(geglu_gbps[1] / HBM_PEAK_GBPS, 4),
+                               "note": "backward kernel: 10 B per hidden unit and token (read value, gate, dOut; "
+                                       "write both gradients); forward moves 6 B"}},
         "cpu_baseline": cpu,
         "context": context,
     }

@@ -16,6 +16,9 @@
  *              and the "Software Dependencies" row's masked-decay kernel.
  *              The pages give no formula; the library adds
  *              decay * (1 - M) * W to the straight-through weight gradient.
+ *   [GEGLU]    the abstract's acceleration of gated activation functions and
+ *              the "Software Dependencies" row's GEGLU kernel (no formula
+ *              on the pages).
  *   [Flip]     the abstract's "flip rate", a monitor of the stability of 2:4
  *              training.  The pages give no formula; the library counts the
  *              mask entries (of the R*C) whose kept/pruned state differs
@@ -233,6 +236,34 @@ int sp24_spmm_bwd_input(const void* dY, const void* vals_col, const uint16_t* me
 int sp24_weight_grad(const void* dY, const void* X, const void* W, const uint8_t* idx, float decay,
                      int64_t T, int64_t R, int64_t C, float* dW, void* stream);
 
+/*
+ * GEGLU forward [GEGLU]: out[t][j] = value[t][j] * GELU(gate[t][j]), GELU the
+ * exact x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), fp32 arithmetic, fp16
+ * result rounded to nearest even.
+ *
+ *   U      in   fp16 [T, 2h], the first linear's output.  Its columns come in
+ *               blocks of `group` value columns followed by the `group`
+ *               matching gate columns: value j is column
+ *               2*group*(j/group) + j%group, its gate is `group` columns
+ *               later.  group = h is the two-halves layout [value | gate].
+ *   T, h, group  T >= 0; h >= 0 and group > 0, multiples of 8; h % group == 0
+ *   out    out  fp16 [T, h]
+ * Errors: NULL, SHAPE, ALIGN, TOO_LARGE (T*2h >= 2^40), LAUNCH.
+ */
+int sp24_geglu_fwd(const void* U, int64_t T, int64_t h, int64_t group, void* out, void* stream);
+
+/*
+ * GEGLU backward [GEGLU]: dU in U's layout, with
+ *   d value = dout * GELU(gate),  d gate = dout * value * GELU'(gate),
+ *   GELU'(x) = Phi(x) + x * phi(x).
+ *   U      in   fp16 [T, 2h] as for sp24_geglu_fwd
+ *   dout   in   fp16 [T, h]
+ *   dU     out  fp16 [T, 2h] (may not overlap U or dout)
+ * Errors: as sp24_geglu_fwd.
+ */
+int sp24_geglu_bwd(const void* U, const void* dout, int64_t T, int64_t h, int64_t group,
+                   void* dU, void* stream);
+
 /* Host only: a static, human-readable name for a status code. */
 const char* sp24_status_str(int status);
 
@@ -243,7 +274,7 @@ const char* sp24_status_str(int status);
  */
 int sp24_pattern_table(uint16_t* out);
 
-/* Host only: the library's ABI version (3 for this header). */
+/* Host only: the library's ABI version (4 for this header). */
 int sp24_abi_version(void);
 
 #ifdef __cplusplus

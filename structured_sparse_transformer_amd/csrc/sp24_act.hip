@@ -1,0 +1,132 @@
+// GEGLU forward and backward, streaming kernels.
+//
+// "Accelerating Transformer Pre-training with 2:4 Sparsity" names the
+// acceleration of gated activation functions (abstract) and a GEGLU kernel
+// (reproducibility table, "Software Dependencies" row) without further
+// detail.  The library's operation: out = value * GELU(gate), GELU the exact
+// x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), on the first linear's output
+// U [T, 2h], whose columns come in blocks of G value columns followed by the G
+// matching gate columns.  With a small G (16, say) a value and its gate share
+// a 128-byte line, so the pair is fetched together; G = h is the plain
+// two-halves layout, where they sit h columns apart.
+//
+// Per hidden unit and token the forward moves 6 bytes (read value and gate,
+// write out) and the backward 10 (read value, gate and dOut, write both
+// gradients).  At these rates the kernels sit between the HBM roof and the
+// fp32 vector roof: each erfcf costs a few dozen VALU operations.  Each lane handles 8 consecutive hidden
+// units of one token with 16-byte loads and stores; arithmetic is fp32, with
+// results rounded to nearest even in fp16.  Phi is evaluated as
+// erfc(-x / sqrt 2) / 2, which keeps its relative accuracy for negative x,
+// where 1 + erf(x / sqrt 2) cancels to zero in fp32 (below about x = -5.3).
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "sp24_internal.hpp"
+
+namespace sp24 {
+namespace {
+
+constexpr int kActThreads = 256;
+constexpr float kInvSqrt2 = 0.70710678118654752440f;
+constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// streaming 16-byte accesses: every byte is touched once
+__device__ __forceinline__ h8 ld16(const uint16_t* p) {
+  return __builtin_bit_cast(h8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+__device__ __forceinline__ void st16(uint16_t* p, h8 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
+
+// One lane per vector of 8 hidden units of one token: vector i is token
+// i / (h/8), units 8*(i % (h/8)) ..; Index is uint32_t when the vector count
+// fits, so the divisions stay 32-bit.  Offsets into U and out:
+template <typename Index>
+struct Pos {
+  int64_t u_val, u_gate, o;
+};
+template <typename Index>
+__device__ __forceinline__ Pos<Index> position(Index i, Index hv, Index group) {
+  const Index t = i / hv, unit = (i - t * hv) * 8;
+  const Index b = unit / group, w = unit - b * group;
+  Pos<Index> p;
+  p.u_val = (int64_t)t * 2 * (int64_t)hv * 8 + (int64_t)(2 * group * b + w);
+  p.u_gate = p.u_val + (int64_t)group;
+  p.o = (int64_t)t * (int64_t)hv * 8 + (int64_t)unit;
+  return p;
+}
+
+template <typename Index>
+__global__ __launch_bounds__(kActThreads) void geglu_fwd_kernel(const uint16_t* __restrict__ U, Index n, Index hv,
+                                                               Index group, uint16_t* __restrict__ out) {
+  const Index i = (Index)blockIdx.x * kActThreads + threadIdx.x;
+  if (i >= n) return;
+  const Pos<Index> p = position<Index>(i, hv, group);
+  const h8 v = ld16(U + p.u_val);
+  const h8 g = ld16(U + p.u_gate);
+  h8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = (float)g[e];
+    const float gelu = 0.5f * x * erfcf(-x * kInvSqrt2);
+    o[e] = (_Float16)((float)v[e] * gelu);
+  }
+  st16(out + p.o, o);
+}
+
+template <typename Index>
+__global__ __launch_bounds__(kActThreads) void geglu_bwd_kernel(const uint16_t* __restrict__ U,
+                                                               const uint16_t* __restrict__ dout, Index n, Index hv,
+                                                               Index group, uint16_t* __restrict__ dU) {
+  const Index i = (Index)blockIdx.x * kActThreads + threadIdx.x;
+  if (i >= n) return;
+  const Pos<Index> p = position<Index>(i, hv, group);
+  const h8 v = ld16(U + p.u_val);
+  const h8 g = ld16(U + p.u_gate);
+  const h8 d = ld16(dout + p.o);
+  h8 dv, dg;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = (float)g[e], dy = (float)d[e];
+    const float cdf = 0.5f * erfcf(-x * kInvSqrt2);
+    const float pdf = kInvSqrt2Pi * expf(-0.5f * x * x);
+    dv[e] = (_Float16)(dy * (x * cdf));
+    dg[e] = (_Float16)(dy * (float)v[e] * (cdf + x * pdf));
+  }
+  st16(dU + p.u_val, dv);
+  st16(dU + p.u_gate, dg);
+}
+
+}  // namespace
+
+hipError_t launch_geglu_fwd(const uint16_t* U, int64_t T, int64_t h, int64_t group, uint16_t* out, hipStream_t s) {
+  const int64_t n = T * (h / 8);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + kActThreads - 1) / kActThreads));
+  if (n < ((int64_t)1 << 32) - kActThreads)
+    hipLaunchKernelGGL(geglu_fwd_kernel<uint32_t>, grid, dim3(kActThreads), 0, s, U, (uint32_t)n, (uint32_t)(h / 8),
+                       (uint32_t)group, out);
+  else
+    hipLaunchKernelGGL(geglu_fwd_kernel<uint64_t>, grid, dim3(kActThreads), 0, s, U, (uint64_t)n, (uint64_t)(h / 8),
+                       (uint64_t)group, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_geglu_bwd(const uint16_t* U, const uint16_t* dout, int64_t T, int64_t h, int64_t group,
+                            uint16_t* dU, hipStream_t s) {
+  const int64_t n = T * (h / 8);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + kActThreads - 1) / kActThreads));
+  if (n < ((int64_t)1 << 32) - kActThreads)
+    hipLaunchKernelGGL(geglu_bwd_kernel<uint32_t>, grid, dim3(kActThreads), 0, s, U, dout, (uint32_t)n,
+                       (uint32_t)(h / 8), (uint32_t)group, dU);
+  else
+    hipLaunchKernelGGL(geglu_bwd_kernel<uint64_t>, grid, dim3(kActThreads), 0, s, U, dout, (uint64_t)n,
+                       (uint64_t)(h / 8), (uint64_t)group, dU);
+  return hipGetLastError();
+}
+
+}  // namespace sp24

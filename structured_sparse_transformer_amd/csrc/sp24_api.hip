@@ -74,6 +74,13 @@ int spmm_common(const void* A, const void* vals, const uint16_t* meta, int64_t T
                                             T, N, K, static_cast<uint16_t*>(out), as_stream(stream)));
 }
 
+int check_geglu(int64_t T, int64_t h, int64_t group) {
+  if (T < 0 || h < 0 || group <= 0 || h % 8 != 0 || group % 8 != 0 || (h != 0 && h % group != 0))
+    return SP24_ERR_SHAPE;
+  if (T >= kMaxDim || h >= kMaxDim || (T != 0 && 2 * h >= kMaxElems / T)) return SP24_ERR_TOO_LARGE;
+  return SP24_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -159,6 +166,24 @@ int sp24_weight_grad(const void* dY, const void* X, const void* W, const uint8_t
                                                 as_stream(stream)));
 }
 
+int sp24_geglu_fwd(const void* U, int64_t T, int64_t h, int64_t group, void* out, void* stream) {
+  const int st = check_geglu(T, h, group);
+  if (st != SP24_OK || T == 0 || h == 0) return st;
+  if (U == nullptr || out == nullptr) return SP24_ERR_NULL;
+  if (!aligned16(U) || !aligned16(out)) return SP24_ERR_ALIGN;
+  return launch_status(sp24::launch_geglu_fwd(static_cast<const uint16_t*>(U), T, h, group,
+                                              static_cast<uint16_t*>(out), as_stream(stream)));
+}
+
+int sp24_geglu_bwd(const void* U, const void* dout, int64_t T, int64_t h, int64_t group, void* dU, void* stream) {
+  const int st = check_geglu(T, h, group);
+  if (st != SP24_OK || T == 0 || h == 0) return st;
+  if (U == nullptr || dout == nullptr || dU == nullptr) return SP24_ERR_NULL;
+  if (!aligned16(U) || !aligned16(dout) || !aligned16(dU)) return SP24_ERR_ALIGN;
+  return launch_status(sp24::launch_geglu_bwd(static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(dout), T,
+                                              h, group, static_cast<uint16_t*>(dU), as_stream(stream)));
+}
+
 const char* sp24_status_str(int status) {
   switch (status) {
     case SP24_OK: return "ok";
@@ -178,6 +203,6 @@ int sp24_pattern_table(uint16_t* out) {
   return SP24_OK;
 }
 
-int sp24_abi_version(void) { return 3; }
+int sp24_abi_version(void) { return 4; }
 
 }  // extern "C"

@@ -51,6 +51,13 @@ hipError_t launch_flip_count(const uint8_t* a, const uint8_t* b, int64_t n, unsi
 hipError_t launch_weight_grad(const uint16_t* dY, const uint16_t* X, const uint16_t* W, const uint8_t* idx,
                               float decay, int64_t T, int64_t R, int64_t C, float* dW, hipStream_t s);
 
+// GEGLU over U [T][2h] (blocks of `group` value columns, then `group` gate
+// columns): out [T][h] = value * GELU(gate); the backward writes dU in U's
+// layout.  h and group multiples of 8, h % group == 0.
+hipError_t launch_geglu_fwd(const uint16_t* U, int64_t T, int64_t h, int64_t group, uint16_t* out, hipStream_t s);
+hipError_t launch_geglu_bwd(const uint16_t* U, const uint16_t* dout, int64_t T, int64_t h, int64_t group,
+                            uint16_t* dU, hipStream_t s);
+
 // out[T][N] = A[T][K] * S[N][K]^T with S in 2:4 row form along K:
 // vals [N][K/2] fp16, meta [N][K/16].  N, K multiples of 16.
 hipError_t launch_spmm_nt(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T,

@@ -25,7 +25,7 @@ SP24_OK = 0
 STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_LAUNCH",
                 5: "ERR_UNSUPPORTED", 6: "ERR_TOO_LARGE"}
 EXPORTS = ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
-           "sp24_flip_count", "sp24_weight_grad", "sp24_spmm_fwd", "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table",
+           "sp24_flip_count", "sp24_weight_grad", "sp24_geglu_fwd", "sp24_geglu_bwd", "sp24_spmm_fwd", "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table",
            "sp24_abi_version")
 MAX_BATCH = 8
 
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
             "sp24_search_compress_batch": [p, i32, p],
             "sp24_flip_count": [p, p, i64, p, p],
             "sp24_weight_grad": [p, p, p, p, ctypes.c_float, i64, i64, i64, p, p],
+            "sp24_geglu_fwd": [p, i64, i64, i64, p, p],
+            "sp24_geglu_bwd": [p, p, i64, i64, i64, p, p],
             "sp24_spmm_fwd": [p, p, p, i64, i64, i64, p, p],
             "sp24_spmm_bwd_input": [p, p, p, i64, i64, i64, p, p],
             "sp24_status_str": [i32],
@@ -223,6 +225,33 @@ def sp24_weight_grad(dY, X, W=None, idx=None, decay=0.0, dW=None, stream=None):
     _check("sp24_weight_grad", lib().sp24_weight_grad(_ptr(dY), _ptr(X), _ptr(W), _ptr(idx), float(decay), T, R, C,
                                                       _ptr(dW), _stream(stream)))
     return dW
+
+
+def _geglu_shape(U, group):
+    if U.dtype != torch.float16 or U.dim() != 2 or U.shape[1] % 2:
+        raise ValueError("U must be float16 [T, 2h]")
+    T, h = U.shape[0], U.shape[1] // 2
+    group = h if group is None else group
+    return T, h, group
+
+
+def sp24_geglu_fwd(U, group=None, out=None, stream=None):
+    """out [T, h] = value * GELU(gate); U's columns in blocks of `group`
+    values then `group` gates (default: the two halves)."""
+    T, h, group = _geglu_shape(U, group)
+    out = _out(out, (T, h), torch.float16, U.device)
+    _check("sp24_geglu_fwd", lib().sp24_geglu_fwd(_ptr(U), T, h, group, _ptr(out), _stream(stream)))
+    return out
+
+
+def sp24_geglu_bwd(U, dout, group=None, dU=None, stream=None):
+    """dU [T, 2h] in U's layout from dout [T, h]."""
+    T, h, group = _geglu_shape(U, group)
+    if dout.dtype != torch.float16 or tuple(dout.shape) != (T, h):
+        raise ValueError("dout must be float16 [T, h]")
+    dU = _out(dU, (T, 2 * h), torch.float16, U.device)
+    _check("sp24_geglu_bwd", lib().sp24_geglu_bwd(_ptr(U), _ptr(dout), T, h, group, _ptr(dU), _stream(stream)))
+    return dU
 
 
 def sp24_spmm_fwd(X, vals_row, meta_row, R, C, Y=None, stream=None):

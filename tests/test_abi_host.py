@@ -38,7 +38,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
-              "sp24_flip_count", "sp24_weight_grad", "sp24_spmm_fwd",
+              "sp24_flip_count", "sp24_weight_grad", "sp24_geglu_fwd", "sp24_geglu_bwd", "sp24_spmm_fwd",
               "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table", "sp24_abi_version"):
         assert n in names
 
@@ -58,7 +58,7 @@ def test_pattern_table_matches_oracle(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sp24_abi_version() == 3
+    assert L.sp24_abi_version() == 4
     for s in range(7):
         assert L.sp24_status_str(s)
     assert L.sp24_status_str(99) == b"unknown status"
@@ -191,3 +191,20 @@ def test_weight_grad_validation(L):
     assert f(FAKE, FAKE, NUL, NUL, c, 1 << 20, 1024, 16, FAKE, NUL) == 6    # T*R >= 2^30
     assert f(FAKE, FAKE, NUL, NUL, c, 1 << 20, 16, 1024, FAKE, NUL) == 6
     assert f(NUL, NUL, NUL, NUL, c, 8, 0, 16, NUL, NUL) == 0                # empty output
+
+
+def test_geglu_validation(L):
+    fw, bw = L.sp24_geglu_fwd, L.sp24_geglu_bwd
+    assert fw(FAKE, 4, 12, 4, FAKE, NUL) == 2          # h % 8
+    assert fw(FAKE, 4, 16, 4, FAKE, NUL) == 2          # group % 8
+    assert fw(FAKE, 4, 24, 16, FAKE, NUL) == 2         # h % group
+    assert fw(FAKE, 4, 16, 0, FAKE, NUL) == 2
+    assert fw(FAKE, -1, 16, 8, FAKE, NUL) == 2
+    assert fw(NUL, 4, 16, 8, FAKE, NUL) == 1
+    assert fw(FAKE, 4, 16, 8, MIS, NUL) == 3
+    assert fw(FAKE, 1 << 30, 1 << 10, 8, FAKE, NUL) == 6
+    assert fw(NUL, 0, 16, 8, NUL, NUL) == 0
+    assert bw(FAKE, NUL, 4, 16, 8, FAKE, NUL) == 1
+    assert bw(FAKE, FAKE, 4, 16, 8, MIS, NUL) == 3
+    assert bw(FAKE, FAKE, 4, 20, 8, FAKE, NUL) == 2
+    assert bw(NUL, NUL, 4, 0, 8, NUL, NUL) == 0

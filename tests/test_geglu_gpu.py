@@ -1,0 +1,124 @@
+"""GPU parity of the GEGLU forward and backward kernels.
+
+The oracle computes in float64 with the exact GELU; the kernels compute in
+fp32 (erfcf, expf: a few ulp) and round the result to fp16.  So each output
+must lie within half an fp16 ulp of the exact value, plus the fp32 error of
+the few operations before that rounding, plus 2^-25 absolute (below the
+smallest fp16 subnormal step).  The fp32 error is 2e-6 relative for
+GELU(gate) and the value gradient.  The gate gradient
+dout * value * (Phi(x) + x phi(x)) is different: its bracket has a root near
+x = -0.75, where the two terms cancel.  Its fp32 error is therefore bounded
+in absolute terms, 1e-6 * |dout * value| * (Phi(x) + |x| phi(x)) (about 16
+fp32 ulps of the larger term).  Inputs are seeded draws, with
+large-magnitude and signed-zero entries mixed in.  Results must not depend on
+the layout group.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import sp24_oracle as O
+from structured_sparse_transformer_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def sp():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from structured_sparse_transformer_amd import sp24
+    sp24.lib()
+    return sp24
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def ulp16(y):
+    a = np.abs(y)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -24)))
+    return np.where(a >= 2.0 ** -14, 2.0 ** (e - 10), 2.0 ** -24)
+
+
+def check(got, want, extra=0.0):
+    got = got.astype(np.float64)
+    bound = 0.5 * ulp16(want) + 2e-6 * np.abs(want) + 2.0 ** -25 + extra
+    bad = np.argwhere(np.abs(got - want) > bound)
+    assert bad.size == 0, f"{len(bad)} outside, first {bad[:3].tolist()}: got {got[tuple(bad[0])]} want {want[tuple(bad[0])]}"
+
+
+def gate_grad_slack(U, d, group):
+    """Absolute fp32 error budget of each entry of dU (zero on value columns)."""
+    T, two_h = U.shape
+    blocks = U.astype(np.float64).reshape(T, two_h // (2 * group), 2, group)
+    v, x = blocks[:, :, 0, :].reshape(T, -1), blocks[:, :, 1, :].reshape(T, -1)
+    cdf = 0.5 * np.vectorize(math.erfc)(-x / math.sqrt(2.0))
+    pdf = np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+    slack = 1e-6 * np.abs(d.astype(np.float64) * v) * (cdf + np.abs(x) * pdf)
+    out = np.zeros((T, two_h // (2 * group), 2, group))
+    out[:, :, 1, :] = slack.reshape(T, -1, group)
+    return out.reshape(T, two_h)
+
+
+def draw(seed, T, h):
+    U = WL.normal_f16(seed, 1, (T, 2 * h))
+    d = WL.normal_f16(seed, 2, (T, h))
+    rng = np.random.default_rng(seed)
+    # edge values: zeros of both signs, large magnitudes, tiny ones
+    edges = np.array([0.0, -0.0, 6.0, -6.0, 12.5, -12.5, 40.0, -40.0, 2.0 ** -20, -(2.0 ** -20), 3.0, -3.0],
+                     dtype=np.float16)
+    m = rng.random(U.shape) < 0.05
+    U[m] = rng.choice(edges, size=int(m.sum()))
+    return U, d
+
+
+@pytest.mark.parametrize("T,h,group", [(1, 8, 8), (3, 64, 16), (7, 48, 48), (5, 96, 32), (64, 512, 16),
+                                       (33, 6400, 16), (17, 6400, 6400)])
+def test_geglu_forward_backward(sp, T, h, group):
+    U, d = draw(T * 131 + h + group, T, h)
+    out = sp.sp24_geglu_fwd(dev(U), group).cpu().numpy()
+    check(out, O.geglu_fwd(U, group))
+    dU = sp.sp24_geglu_bwd(dev(U), dev(d), group).cpu().numpy()
+    check(dU, O.geglu_bwd(U, d, group), gate_grad_slack(U, d, group))
+
+
+def test_geglu_layout_group_does_not_change_results(sp):
+    T, h = 40, 256
+    U, d = draw(3, T, h)
+    v, g = U[:, :h], U[:, h:]
+    # the same values laid out in blocks of 16
+    U16 = np.concatenate([np.concatenate([v[:, 16 * b: 16 * b + 16], g[:, 16 * b: 16 * b + 16]], axis=1)
+                          for b in range(h // 16)], axis=1)
+    a = sp.sp24_geglu_fwd(dev(U), h)
+    b = sp.sp24_geglu_fwd(dev(U16), 16)
+    assert torch.equal(a, b)
+    da = sp.sp24_geglu_bwd(dev(U), dev(d), h).cpu().numpy()
+    db = sp.sp24_geglu_bwd(dev(U16), dev(d), 16).cpu().numpy()
+    db_halves = np.concatenate([db.reshape(T, h // 16, 2, 16)[:, :, 0, :].reshape(T, h),
+                                db.reshape(T, h // 16, 2, 16)[:, :, 1, :].reshape(T, h)], axis=1)
+    assert (da.view(np.uint16) == db_halves.view(np.uint16)).all()
+
+
+def test_geglu_empty(sp):
+    U = torch.empty(0, 32, dtype=torch.float16, device="cuda")
+    assert sp.sp24_geglu_fwd(U, 16).shape == (0, 16)
+    assert sp.sp24_geglu_bwd(U, torch.empty(0, 16, dtype=torch.float16, device="cuda"), 16).shape == (0, 32)
+
+
+@pytest.mark.parametrize("group", [16, 6400])
+def test_geglu_full_size_sampled(sp, group):
+    """A GPT-2-1.5B-wide GEGLU (h = 6400) over 16384 tokens; 64 sampled token
+    rows checked against the oracle."""
+    T, h = 16384, 6400
+    U = WL.normal_f16(70, 1, (T, 2 * h))
+    d = WL.normal_f16(70, 2, (T, h))
+    out = sp.sp24_geglu_fwd(dev(U), group)
+    dU = sp.sp24_geglu_bwd(dev(U), dev(d), group)
+    rows = np.sort(np.random.default_rng(group).choice(T, size=64, replace=False))
+    ri = torch.from_numpy(rows).cuda()
+    check(out[ri].cpu().numpy(), O.geglu_fwd(U[rows], group))
+    check(dU[ri].cpu().numpy(), O.geglu_bwd(U[rows], d[rows], group), gate_grad_slack(U[rows], d[rows], group))
