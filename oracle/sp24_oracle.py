@@ -65,6 +65,19 @@ What the method computes, and the readings taken where the pages are silent:
    pair close together in memory).  The backward gives d value = dOut *
    GELU(gate) and d gate = dOut * value * GELU'(gate), GELU'(x) = Phi(x) + x
    phi(x).  Computed in float64.
+7. MVUE [HZ24 SW: an MVUE kernel; only the name is on the pages].  Reading:
+   the minimum-variance unbiased estimator that keeps 2 of every 4
+   consecutive entries of a gradient row.  For a group a_0..a_3 the keep
+   probabilities are p_i = 2|a_i| / S (S = sum |a_i|), which minimise the
+   summed variance sum a_i^2 (1/p_i - 1) under sum p_i = 2; an entry with
+   p_k > 1 is capped at 1 and the others get |a_j| / (S - |a_k|).  Exactly two
+   entries are drawn by systematic sampling with one uniform u in [0, 1) per
+   group (the cumulative sums C_0 .. C_2 of p; the picks are the interval
+   holding u and the one holding u + 1), and a kept entry is a_i / p_i, which
+   makes the estimate unbiased.  A group with fewer than two non-zero entries
+   is kept as it is.  The output is the library's 2:4 row form.  Every
+   decision is taken in fp32 in the order written in ``mvue_group``, so that
+   an implementation with the same fp32 operations reproduces it bit for bit.
 """
 from __future__ import annotations
 
@@ -322,6 +335,66 @@ def geglu_bwd(U: np.ndarray, dout: np.ndarray, group: int) -> np.ndarray:
     out[:, :, 0, :] = dv.reshape(T, -1, group)
     out[:, :, 1, :] = dg.reshape(T, -1, group)
     return out.reshape(T, 2 * h)
+
+
+def mvue_group(a: np.ndarray, u: np.float32) -> tuple:
+    """One group of item 7: a = 4 fp16 values, u = fp32 uniform in [0, 1).
+
+    Returns (i, k, value_i, value_k) with i < k, values as fp32.  All
+    arithmetic is fp32 (numpy float32 scalars round every operation).
+    """
+    f = np.float32
+    m = [f(abs(f(x))) for x in a]
+    nz = [i for i in range(4) if m[i] != 0]
+    if len(nz) < 2:
+        # nothing to sample: keep the non-zero entry (if any) and the lowest
+        # other index, both exactly
+        i = nz[0] if nz else 0
+        k = 1 if i == 0 else 0
+        i, k = min(i, k), max(i, k)
+        return i, k, f(a[i]), f(a[k])
+    S = f(f(f(m[0] + m[1]) + m[2]) + m[3])
+    p = [f(f(2) * m[i]) / S for i in range(4)]
+    over = [i for i in range(4) if p[i] > f(1)]
+    if over:
+        kc = over[0]
+        rest = f(0)
+        for j in range(4):
+            if j != kc:
+                rest = f(rest + m[j])
+        p = [f(1) if j == kc else m[j] / rest for j in range(4)]
+    C0 = p[0]
+    C1 = f(C0 + p[1])
+    C2 = f(C1 + p[2])
+    u = f(u)
+    u1 = f(u + f(1))
+    i = int(C0 <= u) + int(C1 <= u) + int(C2 <= u)
+    k = int(C0 <= u1) + int(C1 <= u1) + int(C2 <= u1)
+    if k == i:
+        if i < 3:
+            k = i + 1
+        else:
+            i, k = 2, 3
+    val = lambda j: f(a[j]) / p[j] if p[j] > 0 else f(0)  # noqa: E731
+    return i, k, f(val(i)), f(val(k))
+
+
+def mvue(M: np.ndarray, U: np.ndarray) -> dict:
+    """Item 7 over a matrix: M fp16 [rows, cols] (cols a multiple of 16),
+    U fp32 [rows, cols/4].  Returns the row form {"vals": fp16 [rows,
+    cols/2], "meta": uint16 [rows, cols/16]}."""
+    rows, cols = M.shape
+    if cols % 16 != 0 or U.shape != (rows, cols // 4):
+        raise ValueError("cols must be a multiple of 16 and U [rows, cols/4]")
+    vals = np.zeros((rows, cols // 2), np.float16)
+    meta = np.zeros((rows, cols // 16), np.uint16)
+    for r in range(rows):
+        for g in range(cols // 4):
+            i, k, vi, vk = mvue_group(M[r, 4 * g: 4 * g + 4], U[r, g])
+            vals[r, 2 * g] = np.float16(vi)
+            vals[r, 2 * g + 1] = np.float16(vk)
+            meta[r, g // 4] |= np.uint16((i | (k << 2)) << (4 * (g % 4)))
+    return {"vals": vals, "meta": meta}
 
 
 def gemm_errors(out: np.ndarray, ref: np.ndarray) -> tuple:

@@ -477,3 +477,77 @@ def test_geglu_layouts_and_backward():
             dn[t, c] -= eps
             num[t, c] = ((dout * O.geglu_fwd(up, 2)).sum() - (dout * O.geglu_fwd(dn, 2)).sum()) / (2 * eps)
     assert np.allclose(dU, num, rtol=0, atol=1e-7)
+
+
+# ----------------------------------------------------------------------------
+# MVUE
+def _grid_stats(a, n=20000):
+    """Mean and mean square of the estimate over u on a uniform grid of
+    [0, 1) (the estimate is piecewise constant in u)."""
+    mean = np.zeros(4)
+    sq = np.zeros(4)
+    hits = np.zeros(4)
+    for j in range(n):
+        u = np.float32((j + 0.5) / n)
+        i, k, vi, vk = O.mvue_group(a, u)
+        assert 0 <= i < k <= 3
+        out = np.zeros(4)
+        out[i], out[k] = float(vi), float(vk)
+        mean += out
+        sq += out * out
+        hits[i] += 1
+        hits[k] += 1
+    return mean / n, sq / n, hits / n
+
+
+def test_mvue_worked_examples():
+    one = np.array([1, 1, 1, 1], np.float16)
+    assert O.mvue_group(one, np.float32(0.25)) == (0, 2, 2.0, 2.0)      # C = 0.5, 1, 1.5
+    assert O.mvue_group(one, np.float32(0.75)) == (1, 3, 2.0, 2.0)
+    dom = np.array([8, 1, 1, 0], np.float16)                          # p = 1 (capped), 1/2, 1/2, 0
+    assert O.mvue_group(dom, np.float32(0.1)) == (0, 1, 8.0, 2.0)
+    assert O.mvue_group(dom, np.float32(0.6)) == (0, 2, 8.0, 2.0)
+    neg = np.array([-1, 3, 0, 0], np.float16)                         # p = 1/2, 3/2 -> capped: 1, 1
+    i, k, vi, vk = O.mvue_group(neg, np.float32(0.3))
+    assert (i, k, vi, vk) == (0, 1, -1.0, 3.0)
+    # fewer than two non-zero entries: kept exactly
+    assert O.mvue_group(np.array([0, 0, 3, 0], np.float16), np.float32(0.9)) == (0, 2, 0.0, 3.0)
+    assert O.mvue_group(np.zeros(4, np.float16), np.float32(0.2)) == (0, 1, 0.0, 0.0)
+
+
+def test_mvue_unbiased_with_minimum_variance():
+    rng = np.random.default_rng(60)
+    for trial in range(6):
+        a = rng.standard_normal(4).astype(np.float16)
+        if trial == 0:
+            a[1] = np.float16(9.0)              # a capped entry
+        if trial == 1:
+            a[2] = np.float16(0.0)
+        mean, sq, hits = _grid_stats(a)
+        m = np.abs(a.astype(np.float64))
+        p = 2 * m / m.sum()
+        if p.max() > 1:
+            kc = int(p.argmax())
+            p = m / (m.sum() - m[kc])
+            p[kc] = 1.0
+        # unbiased, selected with probability p_i, variance a^2 (1/p - 1)
+        assert np.allclose(mean, a.astype(np.float64), rtol=0, atol=2e-3 * np.abs(a).max())
+        assert np.allclose(hits, p, atol=2e-4)
+        var = sq - a.astype(np.float64) ** 2
+        want = np.where(p > 0, a.astype(np.float64) ** 2 * (1 / np.where(p > 0, p, 1) - 1), 0)
+        assert np.allclose(var, want, rtol=0, atol=5e-3 * (a.astype(np.float64) ** 2).max() + 1e-9)
+
+
+def test_mvue_matrix_form():
+    rng = np.random.default_rng(61)
+    M = rng.standard_normal((4, 32)).astype(np.float16)
+    U = rng.random((4, 8), dtype=np.float32)
+    f = O.mvue(M, U)
+    for r in range(4):
+        for g in range(8):
+            i, k, vi, vk = O.mvue_group(M[r, 4 * g: 4 * g + 4], U[r, g])
+            nib = (int(f["meta"][r, g // 4]) >> (4 * (g % 4))) & 0xF
+            assert nib == (i | k << 2) and nib in (0x4, 0x8, 0xC, 0x9, 0xD, 0xE)
+            assert f["vals"][r, 2 * g] == np.float16(vi) and f["vals"][r, 2 * g + 1] == np.float16(vk)
+            # the estimate keeps the signs of the entries it keeps
+            assert np.sign(float(vi)) in (0, np.sign(float(M[r, 4 * g + i])))
