@@ -44,6 +44,14 @@ DECAY = 2e-4                         # masked decay factor of the weight-gradien
 GEGLU_GROUP = 16                     # GEGLU column layout: blocks of 16 values, then their 16 gates
 
 
+def mvue_uniforms(torch, dev, cfg):
+    """One fp32 uniform per group of 4 entries of dY1 [T, 4d], drawn on the
+    device with a fixed torch seed."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed + 1)
+    return torch.rand(cfg.tokens, cfg.dff // 4, generator=g, device=dev, dtype=torch.float32)
+
+
 def geglu_inputs(torch, dev, cfg):
     """GEGLU input of a gated FFN of the same width: U [T, 2 * 4d] (values and
     gates in blocks of GEGLU_GROUP), dOut [T, 4d]; N(0, 1) draws made on the
@@ -131,6 +139,13 @@ def profile_only(args, sp24, torch, dev, cfg, F1, F2, FL, W1s, W2s, X, dY1, H, d
         torch.cuda.synchronize()
         log(f"copy: {n} x 512 MiB")
         return
+    if args.profile_kernel == "mvue":
+        Um = mvue_uniforms(torch, dev, cfg)
+        for _ in range(n):
+            sp24.sp24_mvue(dY1, Um)
+        torch.cuda.synchronize()
+        log(f"mvue: {n} rounds")
+        return
     if args.profile_kernel == "geglu":
         U, gd = geglu_inputs(torch, dev, cfg)
         out, dU = torch.empty_like(gd), torch.empty_like(U)
@@ -183,7 +198,7 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy context numbers")
     ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "flip_count", "weight_grad", "geglu",
-                                                 "copy"],
+                                                 "mvue", "copy"],
                     help="run only this kernel --steps times (for rocprofv3 counter passes); prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -324,6 +339,20 @@ def main():
     geglu_gbps = [6 * units / (geglu_ms[0] * 1e-3) / 1e9, 10 * units / (geglu_ms[1] * 1e-3) / 1e9]
     del U, gd, g_out, g_dU
 
+    # next row: MVUE 2:4 estimate of the output gradient dY1 [T, 4d] (HBM-bound)
+    Um = mvue_uniforms(torch, dev, cfg)
+    mv_out = sp24.sp24_mvue(dY1, Um)
+    torch.cuda.synchronize()
+    e0m, e1m = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0m.record()
+    for _ in range(10):
+        sp24.sp24_mvue(dY1, Um, out=mv_out)
+    e1m.record()
+    torch.cuda.synchronize()
+    mvue_ms = e0m.elapsed_time(e1m) / 10
+    mvue_gbps = 4.125 * T * f / (mvue_ms * 1e-3) / 1e9
+    del Um, mv_out
+
     # next row: the weight gradients of both linears with the masked decay
     # term (dense fp16 MFMA, fp32 out), timed back to back after the step
     dW1 = torch.empty(f, d, dtype=torch.float32, device=dev)
@@ -444,6 +473,12 @@ def main():
                                "frac": round(geglu_gbps[1] / HBM_PEAK_GBPS, 4),
                                "note": "backward kernel: 10 B per hidden unit and token (read value, gate, dOut; "
                                        "write both gradients); forward moves 6 B"}},
+        "mvue": {"definition": "MVUE 2:4 estimate of dY1 [T, 4d] with one caller-supplied uniform per group, "
+                            "row-form output (sp24_mvue)",
+                 "us": round(mvue_ms * 1e3, 1), "GBps": round(mvue_gbps, 1),
+                 "roofline": {"bound": "hbm", "achieved": round(mvue_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": round(mvue_gbps / HBM_PEAK_GBPS, 4),
+                              "note": "4.125 B per entry: read 2 (gradient) + 1 (uniforms), write 1.125 (2:4 row form)"}},
         "cpu_baseline": cpu,
         "context": context,
     }

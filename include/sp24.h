@@ -19,6 +19,9 @@
  *   [GEGLU]    the abstract's acceleration of gated activation functions and
  *              the "Software Dependencies" row's GEGLU kernel (no formula
  *              on the pages).
+ *   [MVUE]     the "Software Dependencies" row's MVUE kernel (name only).
+ *              The library's reading: the minimum-variance unbiased
+ *              estimator that keeps 2 of 4 entries of a gradient.
  *   [Flip]     the abstract's "flip rate", a monitor of the stability of 2:4
  *              training.  The pages give no formula; the library counts the
  *              mask entries (of the R*C) whose kept/pruned state differs
@@ -264,6 +267,35 @@ int sp24_geglu_fwd(const void* U, int64_t T, int64_t h, int64_t group, void* out
 int sp24_geglu_bwd(const void* U, const void* dout, int64_t T, int64_t h, int64_t group,
                    void* dU, void* stream);
 
+/*
+ * MVUE 2:4 estimate of a gradient [MVUE]: every group of 4 consecutive
+ * entries a_0..a_3 of a row keeps exactly two, chosen at random so that the
+ * estimate is unbiased with the least summed variance.
+ *   - Keep probabilities: p_i = 2|a_i| / S with S = sum |a_i|, summed left to
+ *     right.  If some p_k > 1, p_k = 1 and the others are |a_j| / (S - |a_k|).
+ *   - Sampling: the cumulative sums C_0 = p_0, C_1 = C_0 + p_1,
+ *     C_2 = C_1 + p_2 split [0, 2).  The picks are i = #{C_j <= u} and
+ *     k = #{C_j <= u + 1}.  If rounding makes k == i, k = i + 1, or
+ *     (i, k) = (2, 3) when i == 3.
+ *   - Kept values are a_i / p_i (0 where p_i == 0).  A group with fewer than
+ *     two non-zero entries keeps its non-zero entry (if any) and the lowest
+ *     other index, unchanged.
+ * All arithmetic is fp32 in the order above, with IEEE division.  Values are
+ * rounded to nearest even in fp16, so results are reproducible bit for bit.
+ *
+ *   M      in   fp16 [rows, cols], the gradient (finite)
+ *   U      in   fp32 [rows, cols/4], one uniform u in [0, 1) per group,
+ *               supplied by the caller
+ *   rows, cols   >= 0, cols a multiple of 16
+ *   vals   out  fp16 [rows, cols/2]    meta  out  uint16 [rows, cols/16]
+ *               The library's 2:4 row form: the kept pair of group g in
+ *               order, and its nibble i | k << 2.  The sparse GEMMs accept it
+ *               as their sparse operand.
+ * Errors: NULL, SHAPE, ALIGN, TOO_LARGE, LAUNCH.
+ */
+int sp24_mvue(const void* M, const float* U, int64_t rows, int64_t cols, void* vals, uint16_t* meta,
+              void* stream);
+
 /* Host only: a static, human-readable name for a status code. */
 const char* sp24_status_str(int status);
 
@@ -274,7 +306,7 @@ const char* sp24_status_str(int status);
  */
 int sp24_pattern_table(uint16_t* out);
 
-/* Host only: the library's ABI version (4 for this header). */
+/* Host only: the library's ABI version (5 for this header). */
 int sp24_abi_version(void);
 
 #ifdef __cplusplus

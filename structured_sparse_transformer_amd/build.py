@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsp24.so")
-SOURCES = ["sp24_api.hip", "sp24_search.hip", "sp24_spmm.hip", "sp24_dw.hip", "sp24_act.hip"]
+SOURCES = ["sp24_api.hip", "sp24_search.hip", "sp24_spmm.hip", "sp24_dw.hip", "sp24_act.hip", "sp24_mvue.hip"]
 ARCH = os.environ.get("SP24_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

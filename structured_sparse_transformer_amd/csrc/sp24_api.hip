@@ -184,6 +184,17 @@ int sp24_geglu_bwd(const void* U, const void* dout, int64_t T, int64_t h, int64_
                                               h, group, static_cast<uint16_t*>(dU), as_stream(stream)));
 }
 
+int sp24_mvue(const void* M, const float* U, int64_t rows, int64_t cols, void* vals, uint16_t* meta, void* stream) {
+  int st = check_dims(rows, cols, 1);
+  if (st != SP24_OK) return st;
+  if (cols % 16 != 0) return SP24_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return SP24_OK;
+  if (M == nullptr || U == nullptr || vals == nullptr || meta == nullptr) return SP24_ERR_NULL;
+  if (!aligned16(M) || !aligned16(U) || !aligned16(vals) || !aligned16(meta)) return SP24_ERR_ALIGN;
+  return launch_status(sp24::launch_mvue(static_cast<const uint16_t*>(M), U, rows, cols, static_cast<uint16_t*>(vals),
+                                         meta, as_stream(stream)));
+}
+
 const char* sp24_status_str(int status) {
   switch (status) {
     case SP24_OK: return "ok";
@@ -203,6 +214,6 @@ int sp24_pattern_table(uint16_t* out) {
   return SP24_OK;
 }
 
-int sp24_abi_version(void) { return 4; }
+int sp24_abi_version(void) { return 5; }
 
 }  // extern "C"

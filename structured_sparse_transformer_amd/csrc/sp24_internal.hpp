@@ -58,6 +58,11 @@ hipError_t launch_geglu_fwd(const uint16_t* U, int64_t T, int64_t h, int64_t gro
 hipError_t launch_geglu_bwd(const uint16_t* U, const uint16_t* dout, int64_t T, int64_t h, int64_t group,
                             uint16_t* dU, hipStream_t s);
 
+// MVUE 2:4 estimate of M [rows][cols] (cols a multiple of 16) with one
+// uniform U [rows][cols/4] per group, into the row form vals/meta.
+hipError_t launch_mvue(const uint16_t* M, const float* U, int64_t rows, int64_t cols, uint16_t* vals, uint16_t* meta,
+                       hipStream_t s);
+
 // out[T][N] = A[T][K] * S[N][K]^T with S in 2:4 row form along K:
 // vals [N][K/2] fp16, meta [N][K/16].  N, K multiples of 16.
 hipError_t launch_spmm_nt(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T,

@@ -25,7 +25,8 @@ SP24_OK = 0
 STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_LAUNCH",
                 5: "ERR_UNSUPPORTED", 6: "ERR_TOO_LARGE"}
 EXPORTS = ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
-           "sp24_flip_count", "sp24_weight_grad", "sp24_geglu_fwd", "sp24_geglu_bwd", "sp24_spmm_fwd", "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table",
+           "sp24_flip_count", "sp24_weight_grad", "sp24_geglu_fwd", "sp24_geglu_bwd", "sp24_mvue",
+           "sp24_spmm_fwd", "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table",
            "sp24_abi_version")
 MAX_BATCH = 8
 
@@ -64,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "sp24_weight_grad": [p, p, p, p, ctypes.c_float, i64, i64, i64, p, p],
             "sp24_geglu_fwd": [p, i64, i64, i64, p, p],
             "sp24_geglu_bwd": [p, p, i64, i64, i64, p, p],
+            "sp24_mvue": [p, p, i64, i64, p, p, p],
             "sp24_spmm_fwd": [p, p, p, i64, i64, i64, p, p],
             "sp24_spmm_bwd_input": [p, p, p, i64, i64, i64, p, p],
             "sp24_status_str": [i32],
@@ -252,6 +254,23 @@ def sp24_geglu_bwd(U, dout, group=None, dU=None, stream=None):
     dU = _out(dU, (T, 2 * h), torch.float16, U.device)
     _check("sp24_geglu_bwd", lib().sp24_geglu_bwd(_ptr(U), _ptr(dout), T, h, group, _ptr(dU), _stream(stream)))
     return dU
+
+
+def sp24_mvue(M, U, out=None, stream=None):
+    """MVUE 2:4 estimate of M (fp16 [rows, cols]) with uniforms U (fp32
+    [rows, cols/4]); returns {"vals": fp16 [rows, cols/2], "meta": int16
+    [rows, cols/16]}."""
+    if M.dtype != torch.float16 or M.dim() != 2:
+        raise ValueError("M must be a 2-D float16 tensor")
+    rows, cols = M.shape
+    if U.dtype != torch.float32 or tuple(U.shape) != (rows, cols // 4):
+        raise ValueError("U must be float32 [rows, cols/4]")
+    out = dict(out or {})
+    out["vals"] = _out(out.get("vals"), (rows, cols // 2), torch.float16, M.device)
+    out["meta"] = _out(out.get("meta"), (rows, cols // 16), torch.int16, M.device)
+    _check("sp24_mvue", lib().sp24_mvue(_ptr(M), _ptr(U), rows, cols, _ptr(out["vals"]), _ptr(out["meta"]),
+                                        _stream(stream)))
+    return out
 
 
 def sp24_spmm_fwd(X, vals_row, meta_row, R, C, Y=None, stream=None):

@@ -56,6 +56,12 @@ def random_idx(base: int, k: int, shape, hi: int = 90) -> np.ndarray:
     return rng.integers(0, hi, size=shape, dtype=np.uint8)
 
 
+def uniform_f32(base: int, k: int, shape) -> np.ndarray:
+    """fp32 uniforms in [0, 1) (the random draws of a stochastic estimator)."""
+    rng = np.random.default_rng([base, k])
+    return rng.random(shape, dtype=np.float32)
+
+
 def stress_weight(base: int, R: int = 4096, C: int = 4096) -> np.ndarray:
     """Tie-heavy stress weight.
 

@@ -38,7 +38,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
-              "sp24_flip_count", "sp24_weight_grad", "sp24_geglu_fwd", "sp24_geglu_bwd", "sp24_spmm_fwd",
+              "sp24_flip_count", "sp24_weight_grad", "sp24_geglu_fwd", "sp24_geglu_bwd", "sp24_mvue",
+              "sp24_spmm_fwd",
               "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table", "sp24_abi_version"):
         assert n in names
 
@@ -58,7 +59,7 @@ def test_pattern_table_matches_oracle(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sp24_abi_version() == 4
+    assert L.sp24_abi_version() == 5
     for s in range(7):
         assert L.sp24_status_str(s)
     assert L.sp24_status_str(99) == b"unknown status"
@@ -208,3 +209,15 @@ def test_geglu_validation(L):
     assert bw(FAKE, FAKE, 4, 16, 8, MIS, NUL) == 3
     assert bw(FAKE, FAKE, 4, 20, 8, FAKE, NUL) == 2
     assert bw(NUL, NUL, 4, 0, 8, NUL, NUL) == 0
+
+
+def test_mvue_validation(L):
+    f = L.sp24_mvue
+    assert f(FAKE, FAKE, 4, 24, FAKE, FAKE, NUL) == 2           # cols % 16
+    assert f(FAKE, FAKE, -1, 16, FAKE, FAKE, NUL) == 2
+    assert f(NUL, FAKE, 4, 16, FAKE, FAKE, NUL) == 1
+    assert f(FAKE, NUL, 4, 16, FAKE, FAKE, NUL) == 1
+    assert f(FAKE, FAKE, 4, 16, FAKE, NUL, NUL) == 1
+    assert f(FAKE, MIS, 4, 16, FAKE, FAKE, NUL) == 3
+    assert f(FAKE, FAKE, 1 << 31, 16, FAKE, FAKE, NUL) == 6
+    assert f(NUL, NUL, 0, 16, NUL, NUL, NUL) == 0

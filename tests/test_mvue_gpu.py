@@ -1,0 +1,108 @@
+"""GPU parity of the MVUE 2:4 estimator: bit for bit against the oracle.
+
+Both sides take every decision in fp32 in the same order, so picks, values
+(fp16, round to nearest even) and metadata must be identical.  The uniforms
+are seeded inputs shared by both.  Special groups are mixed in: all zero,
+one non-zero entry, a dominant (capped) entry, equal entries, signed zeros,
+subnormals and large magnitudes.
+"""
+import numpy as np
+import pytest
+
+from oracle import sp24_oracle as O
+from structured_sparse_transformer_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def sp():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from structured_sparse_transformer_amd import sp24
+    sp24.lib()
+    return sp24
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def special_matrix(seed, rows, cols):
+    M = WL.normal_f16(seed, 1, (rows, cols))
+    rng = np.random.default_rng(seed)
+    groups = M.reshape(rows, cols // 4, 4)
+    kinds = rng.integers(0, 8, size=(rows, cols // 4))
+    for (r, g), kind in np.ndenumerate(kinds):
+        if kind == 0:
+            groups[r, g] = 0
+        elif kind == 1:
+            groups[r, g] = 0
+            groups[r, g, rng.integers(4)] = rng.standard_normal()
+        elif kind == 2:
+            groups[r, g, rng.integers(4)] *= 50          # dominant: capped at p = 1
+        elif kind == 3:
+            groups[r, g] = np.float16(0.5)
+        elif kind == 4:
+            groups[r, g, rng.integers(4)] = np.float16(-0.0)
+        elif kind == 5:
+            groups[r, g] = (rng.standard_normal(4) * 2.0 ** -18).astype(np.float16)   # subnormals
+        elif kind == 6:
+            groups[r, g] = (rng.standard_normal(4) * 3000).astype(np.float16)
+    return groups.reshape(rows, cols)
+
+
+def assert_same(got, want):
+    gv = got["vals"].cpu().numpy().view(np.uint16)
+    gm = got["meta"].cpu().numpy().view(np.uint16)
+    wv = want["vals"].view(np.uint16)
+    bad = np.argwhere(gv != wv)
+    assert bad.size == 0, f"vals: {len(bad)} differ, first {bad[:3].tolist()}"
+    bad = np.argwhere(gm != want["meta"])
+    assert bad.size == 0, f"meta: {len(bad)} differ, first {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (7, 48), (33, 256), (64, 1024)])
+def test_mvue_bit_exact(sp, rows, cols):
+    M = special_matrix(rows * 7 + cols, rows, cols)
+    U = WL.uniform_f32(rows + cols, 9, (rows, cols // 4))
+    U[0, : min(4, cols // 4)] = np.float32([0.0, 0.5, 0.999999940395, 0.25])[: min(4, cols // 4)]
+    assert_same(sp.sp24_mvue(dev(M), dev(U)), O.mvue(M, U))
+
+
+def test_mvue_empty(sp):
+    f = sp.sp24_mvue(torch.empty(0, 32, dtype=torch.float16, device="cuda"),
+                     torch.empty(0, 8, dtype=torch.float32, device="cuda"))
+    assert f["vals"].shape == (0, 16) and f["meta"].shape == (0, 2)
+
+
+def test_mvue_full_size_sampled_and_valid(sp):
+    """The output gradient of a GPT-2-1.5B FFN layer (16384 x 6400): 24
+    sampled rows bit for bit; every nibble legal everywhere."""
+    cfg = WL.GPT2_1P5B
+    M = WL.ffn_inputs(cfg).dy1
+    U = WL.uniform_f32(cfg.seed, 300, (M.shape[0], M.shape[1] // 4))
+    got = sp.sp24_mvue(dev(M), dev(U))
+    rows = np.sort(np.random.default_rng(3).choice(M.shape[0], size=24, replace=False))
+    ri = torch.from_numpy(rows).cuda()
+    want = O.mvue(M[rows], U[rows])
+    assert_same({"vals": got["vals"][ri], "meta": got["meta"][ri]}, want)
+    meta = got["meta"].cpu().numpy().view(np.uint16)
+    nib = np.stack([(meta >> (4 * q)) & 0xF for q in range(4)], axis=-1)
+    assert np.isin(nib, [0x4, 0x8, 0xC, 0x9, 0xD, 0xE]).all()
+
+
+def test_mvue_feeds_the_sparse_gemm(sp):
+    """The MVUE output is a valid sparse operand: Y = X * MVUE(G)^T through
+    sp24_spmm_fwd matches the oracle's product with the oracle's estimate."""
+    R, C, T = 256, 512, 300
+    G = WL.normal_f16(12, 1, (R, C), 0.02)
+    U = WL.uniform_f32(12, 2, (R, C // 4))
+    X = WL.normal_f16(12, 3, (T, C))
+    f = sp.sp24_mvue(dev(G), dev(U))
+    Y = sp.sp24_spmm_fwd(dev(X), f["vals"], f["meta"], R, C).cpu().numpy()
+    want = O.mvue(G, U)
+    ref = O.spmm_fwd(X, want["vals"], want["meta"], R, C)
+    mr, ma = O.gemm_errors(Y.astype(np.float64), ref)
+    assert mr <= 1e-2 and ma <= 1e-3, (mr, ma)
