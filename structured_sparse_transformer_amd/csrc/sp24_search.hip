@@ -198,46 +198,46 @@ constexpr int kCompressWaves = kCompressThreads / 64;
 // Each workgroup handles kTilesPerWg tiles (see search_compress_kernel).
 constexpr int kTilesPerWg = 2;
 
-// byte selectors for v_perm_b32 that gather halves i0 and i1 of a 4-half group
-constexpr uint32_t pair_selector(int i0, int i1) {
-  return (uint32_t)(2 * i0) | (uint32_t)(2 * i0 + 1) << 8 | (uint32_t)(2 * i1) << 16 | (uint32_t)(2 * i1 + 1) << 24;
+// v_perm_b32 byte selector that gathers halves i0 and i1 of a 4-half group
+// held in two dwords (bytes 2*i0, 2*i0+1, 2*i1, 2*i1+1), from the nibble
+// i0 | i1 << 2.  Computed in a few VALU operations rather than looked up:
+// per-lane lookups of a per-pattern table land on a quarter of the LDS banks.
+__device__ __forceinline__ uint32_t pair_selector(uint32_t nib) {
+  return 0x01000100u + (nib & 3u) * 0x0202u + ((nib >> 2) * 0x0202u << 16);
 }
 
-struct SelTable {
-  uint32_t row_sel[kNumPatterns][4];
-  uint32_t col_sel[kNumPatterns][4];
-  uint32_t nibs[kNumPatterns];  // row nibbles (bits 0..15) | column nibbles << 16
-  uint16_t mask[kNumPatterns + 2];  // kept entries, bit 4r+c (two pad entries keep the size in dwords)
+// One 8-byte entry per pattern: x = row nibbles (bits 0..15) | column
+// nibbles << 16, y = kept entries (bit 4r+c).
+struct PatTable {
+  uint2 entry[kNumPatterns];
 };
 
-constexpr SelTable build_sel_table() {
-  SelTable s{};
+constexpr PatTable build_pat_table() {
+  PatTable t{};
   for (int p = 0; p < kNumPatterns; ++p) {
-    for (int r = 0; r < 4; ++r) {
-      const int n = (kTables.row_nib[p] >> (4 * r)) & 0xF;
-      s.row_sel[p][r] = pair_selector(n & 3, n >> 2);
-      const int c = (kTables.col_nib[p] >> (4 * r)) & 0xF;
-      s.col_sel[p][r] = pair_selector(c & 3, c >> 2);
-    }
-    s.nibs[p] = (uint32_t)kTables.row_nib[p] | (uint32_t)kTables.col_nib[p] << 16;
-    s.mask[p] = kTables.mask[p];
+    t.entry[p].x = (uint32_t)kTables.row_nib[p] | (uint32_t)kTables.col_nib[p] << 16;
+    t.entry[p].y = kTables.mask[p];
   }
-  return s;
+  return t;
 }
 
-__constant__ SelTable g_sel = build_sel_table();
+__constant__ PatTable g_pat = build_pat_table();
+
+// The column form is staged with the row-group index of columns 64 .. 127 of
+// the tile XOR 1, so that the 32 lanes storing one row group of 32 block
+// columns (stride 4 rows of 33 dwords) cover 32 distinct banks.
+__device__ __forceinline__ int col_swz(int column) { return (column >> 6) & 1; }
 
 struct CompressSmem {
-  SelTable sel;
+  PatTable pat;
   uint32_t vals_row[kTile][kTB + 1];     // [row][group]: kept pair as one dword
-  uint32_t vals_col[kTile][kTB + 1];     // [column][row group]
-  uint8_t nib_row[kTile][kTB + 4];       // [row][group]: nibble
-  uint8_t nib_col[kTile][kTB + 4];       // [column][row group]
+  uint32_t vals_col[kTile][kTB + 1];     // [column][row group ^ col_swz(column)]
+  uint32_t bnibs[kTB][kTB + 1];          // [block row][block column]: nibbles of the block's pattern
   uint8_t idx[kTB][kTB];
   uint8_t prev[kTilesPerWg][kTB][kTB];          // previous indices of each tile (flip counting)
   uint32_t flips[kTilesPerWg][kCompressWaves];  // per-wave flip counts of each tile
 };
-static_assert(sizeof(SelTable) % 4 == 0, "SelTable is copied in dwords");
+static_assert(sizeof(PatTable) % 4 == 0, "the pattern table is copied in dwords");
 
 // Tile geometry of one workgroup-tile of one job.  The job is copied by
 // value (selected with static indices), so the kernel-argument table never
@@ -318,24 +318,24 @@ __device__ __forceinline__ uint32_t stage_tile(const TileRef& tr, int k, int tid
       p = p < kNumPatterns ? p : 0;
     }
     sm.idx[bi][bj] = (uint8_t)p;
+    const uint2 ent = sm.pat.entry[p];
     if (kSearch && jb.idx_prev) {
       const uint32_t pv = sm.prev[k][bi][bj];
       const uint32_t prev = pv < (uint32_t)kNumPatterns ? pv : 0u;
-      flips += (uint32_t)__builtin_popcount((uint32_t)(sm.sel.mask[p] ^ sm.sel.mask[prev]));
+      flips += (uint32_t)__builtin_popcount(ent.y ^ sm.pat.entry[prev].y);
     }
-    const uint32_t nibs = sm.sel.nibs[p];
+    const uint32_t nibs = ent.x;
+    sm.bnibs[bi][bj] = nibs;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sm.vals_row[4 * bi + r][bj] = __builtin_amdgcn_perm(w[r][1], w[r][0], sm.sel.row_sel[p][r]);
-      sm.nib_row[4 * bi + r][bj] = (uint8_t)((nibs >> (4 * r)) & 0xF);
-    }
+    for (int r = 0; r < 4; ++r)
+      sm.vals_row[4 * bi + r][bj] = __builtin_amdgcn_perm(w[r][1], w[r][0], pair_selector((nibs >> (4 * r)) & 0xF));
+    const int cs = col_swz(4 * bj);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t hsel = (c & 1) ? 0x07060302u : 0x05040100u;
       const uint32_t top = __builtin_amdgcn_perm(w[1][c >> 1], w[0][c >> 1], hsel);  // rows 0,1 of column c
       const uint32_t bot = __builtin_amdgcn_perm(w[3][c >> 1], w[2][c >> 1], hsel);  // rows 2,3
-      sm.vals_col[4 * bj + c][bi] = __builtin_amdgcn_perm(bot, top, sm.sel.col_sel[p][c]);
-      sm.nib_col[4 * bj + c][bi] = (uint8_t)((nibs >> (16 + 4 * c)) & 0xF);
+      sm.vals_col[4 * bj + c][bi ^ cs] = __builtin_amdgcn_perm(bot, top, pair_selector((nibs >> (16 + 4 * c)) & 0xF));
     }
   }
   return flips;
@@ -367,19 +367,27 @@ __device__ __forceinline__ void write_tile(const TileRef& tr, int tid, const Com
       const uint4 v = make_uint4(sm.vals_row[r][4 * g4 + 0], sm.vals_row[r][4 * g4 + 1], sm.vals_row[r][4 * g4 + 2],
                                  sm.vals_row[r][4 * g4 + 3]);
       *reinterpret_cast<uint4*>(jb.vals_row + (r0 + r) * (C / 2) + c0 / 2 + 8 * g4) = v;
-      const uint8_t* n = &sm.nib_row[r][4 * g4];
-      jb.meta_row[(r0 + r) * (C / 16) + c0 / 16 + g4] = (uint16_t)(n[0] | n[1] << 4 | n[2] << 8 | n[3] << 12);
+      // row r's nibble in each of the four blocks (r/4, 4*g4 + q)
+      const int sh = 4 * (r & 3);
+      uint32_t word = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) word |= ((sm.bnibs[r >> 2][4 * g4 + q] >> sh) & 0xFu) << (4 * q);
+      jb.meta_row[(r0 + r) * (C / 16) + c0 / 16 + g4] = (uint16_t)word;
     }
   }
   if (jb.vals_col) {
     const int q4 = nbr_t / 4;
     for (int i = tid; i < cols * q4; i += kCompressThreads) {
-      const int c = i / q4, g4 = i - c * q4;
-      const uint4 v = make_uint4(sm.vals_col[c][4 * g4 + 0], sm.vals_col[c][4 * g4 + 1], sm.vals_col[c][4 * g4 + 2],
-                                 sm.vals_col[c][4 * g4 + 3]);
+      const int c = i / q4, g4 = i - c * q4, cs = col_swz(c);
+      const uint4 v = make_uint4(sm.vals_col[c][(4 * g4 + 0) ^ cs], sm.vals_col[c][(4 * g4 + 1) ^ cs],
+                                 sm.vals_col[c][(4 * g4 + 2) ^ cs], sm.vals_col[c][(4 * g4 + 3) ^ cs]);
       *reinterpret_cast<uint4*>(jb.vals_col + (c0 + c) * (R / 2) + r0 / 2 + 8 * g4) = v;
-      const uint8_t* n = &sm.nib_col[c][4 * g4];
-      jb.meta_col[(c0 + c) * (R / 16) + r0 / 16 + g4] = (uint16_t)(n[0] | n[1] << 4 | n[2] << 8 | n[3] << 12);
+      // column c's nibble in each of the four blocks (4*g4 + q, c/4)
+      const int sh = 16 + 4 * (c & 3);
+      uint32_t word = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) word |= ((sm.bnibs[4 * g4 + q][c >> 2] >> sh) & 0xFu) << (4 * q);
+      jb.meta_col[(c0 + c) * (R / 16) + r0 / 16 + g4] = (uint16_t)word;
     }
   }
 }
@@ -394,8 +402,8 @@ template <bool kSearch>
 __global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(ScJobs jobs) {
   __shared__ CompressSmem sm;
   const int tid = threadIdx.x;
-  for (int i = tid; i < (int)(sizeof(SelTable) / 4); i += kCompressThreads)
-    reinterpret_cast<uint32_t*>(&sm.sel)[i] = reinterpret_cast<const uint32_t*>(&g_sel)[i];
+  for (int i = tid; i < (int)(sizeof(PatTable) / 4); i += kCompressThreads)
+    reinterpret_cast<uint32_t*>(&sm.pat)[i] = reinterpret_cast<const uint32_t*>(&g_pat)[i];
 
   // Workgroups are dealt round-robin to the 8 XCDs; remap so each XCD walks a
   // contiguous run of tiles (neighbouring output lines then meet in its L2).
@@ -473,7 +481,7 @@ __global__ __launch_bounds__(kFlipThreads) void flip_count_kernel(const uint8_t*
   __shared__ uint16_t mask[kNumPatterns];
   __shared__ uint32_t part[kFlipThreads / 64];
   const int tid = threadIdx.x;
-  for (int i = tid; i < kNumPatterns; i += kFlipThreads) mask[i] = g_sel.mask[i];
+  for (int i = tid; i < kNumPatterns; i += kFlipThreads) mask[i] = (uint16_t)g_pat.entry[i].y;
   __syncthreads();
   auto diff = [&](uint32_t x, uint32_t y) -> uint32_t {
     x = x < (uint32_t)kNumPatterns ? x : 0u;
