@@ -339,6 +339,30 @@ def main():
     geglu_gbps = [6 * units / (geglu_ms[0] * 1e-3) / 1e9, 10 * units / (geglu_ms[1] * 1e-3) / 1e9]
     del U, gd, g_out, g_dU
 
+    # GEGLU fused into the forward GEMM: W1 (6400 x 1600) read as a gated
+    # layer with h = 3200 (rows in blocks of 16 values then 16 gates), against
+    # the same GEMM followed by the GEGLU kernel
+    Uf = torch.empty(T, f, dtype=torch.float16, device=dev)
+    gf = torch.empty(T, f // 2, dtype=torch.float16, device=dev)
+    fused_variants = {
+        "gemm_then_geglu": lambda: (sp24.sp24_spmm_fwd(X, F1["vals_row"], F1["meta_row"], f, d, Y=Uf),
+                                    sp24.sp24_geglu_fwd(Uf, 16, out=gf)),
+        "fused_storing_U": lambda: sp24.sp24_spmm_fwd_geglu(X, F1["vals_row"], F1["meta_row"], f, d, out=gf, U=Uf),
+        "fused_without_U": lambda: sp24.sp24_spmm_fwd_geglu(X, F1["vals_row"], F1["meta_row"], f, d, out=gf),
+    }
+    fused_us = {}
+    for name, fn in fused_variants.items():
+        fn()
+        torch.cuda.synchronize()
+        e0f, e1f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0f.record()
+        for _ in range(5):
+            fn()
+        e1f.record()
+        torch.cuda.synchronize()
+        fused_us[name] = round(e0f.elapsed_time(e1f) / 5 * 1e3, 1)
+    del Uf, gf
+
     # next row: MVUE 2:4 estimate of the output gradient dY1 [T, 4d] (HBM-bound)
     Um = mvue_uniforms(torch, dev, cfg)
     mv_out = sp24.sp24_mvue(dY1, Um)
@@ -468,6 +492,9 @@ def main():
                              "of 16 values then 16 gates (sp24_geglu_fwd / _bwd)",
                   "shape": {"tokens": T, "h": f, "group": GEGLU_GROUP},
                   "us": {"fwd": round(geglu_ms[0] * 1e3, 1), "bwd": round(geglu_ms[1] * 1e3, 1)},
+                  "fused_forward_gemm_us": fused_us,
+                  "fused_note": "W1 (6400 x 1600) as a gated layer, h = 3200, 16384 tokens: sp24_spmm_fwd_geglu "
+                                "against sp24_spmm_fwd + sp24_geglu_fwd",
                   "GBps": {"fwd": round(geglu_gbps[0], 1), "bwd": round(geglu_gbps[1], 1)},
                   "roofline": {"bound": "hbm", "achieved": round(geglu_gbps[1], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                "frac": round(geglu_gbps[1] / HBM_PEAK_GBPS, 4),

@@ -202,6 +202,32 @@ int sp24_spmm_fwd(const void* X, const void* vals_row, const uint16_t* meta_row,
                   int64_t T, int64_t R, int64_t C, void* Y, void* stream);
 
 /*
+ * Forward 2:4 sparse GEMM of a gated FFN's first linear with GEGLU fused
+ * into its epilogue [Abstract, SW, GEGLU]:
+ *     U = X * Ws^T (fp16, as sp24_spmm_fwd), out = value * GELU(gate) of U
+ * The rows of W (the output features of U) come in blocks of 32: rows
+ * 32b .. 32b+15 are the value units 16b .. 16b+15 and rows 32b+16 .. 32b+31
+ * their gate units, so U has sp24_geglu_fwd's layout with group 16.  `out`
+ * is GEGLU of the fp16 products with the same fp32 GELU code as
+ * sp24_geglu_fwd; the two agree to within one fp16 ulp (near rounding ties
+ * the device library's erfc may round differently in the two kernels).
+ * Each value meets its gate in the same lane's accumulators, so U need not
+ * be stored or read back.
+ *
+ *   X         in   fp16 [T, C]
+ *   vals_row, meta_row   in   row form of the pruned W [R, C]
+ *   T, R, C        as sp24_spmm_fwd, and R a multiple of 32
+ *   U         out  fp16 [T, R], the products (for the backward), or NULL
+ *   out       out  fp16 [T, R/2]
+ * When C is not a multiple of 64 (or an operand exceeds 2 GiB) the library
+ * stores U and runs the GEGLU kernel on it; U must then be given, else
+ * SP24_ERR_UNSUPPORTED.
+ * Errors: NULL, SHAPE, ALIGN, TOO_LARGE, UNSUPPORTED, LAUNCH.
+ */
+int sp24_spmm_fwd_geglu(const void* X, const void* vals_row, const uint16_t* meta_row,
+                        int64_t T, int64_t R, int64_t C, void* U, void* out, void* stream);
+
+/*
  * Input-gradient 2:4 sparse GEMM  dX = dY * Ws  [Abstract, SW].  Uses the
  * column form, which exists because the mask is transposable.
  *
@@ -306,7 +332,7 @@ const char* sp24_status_str(int status);
  */
 int sp24_pattern_table(uint16_t* out);
 
-/* Host only: the library's ABI version (5 for this header). */
+/* Host only: the library's ABI version (6 for this header). */
 int sp24_abi_version(void);
 
 #ifdef __cplusplus

@@ -13,21 +13,20 @@
 // Per hidden unit and token the forward moves 6 bytes (read value and gate,
 // write out) and the backward 10 (read value, gate and dOut, write both
 // gradients).  At these rates the kernels sit between the HBM roof and the
-// fp32 vector roof: each erfcf costs a few dozen VALU operations.  Each lane handles 8 consecutive hidden
-// units of one token with 16-byte loads and stores; arithmetic is fp32, with
-// results rounded to nearest even in fp16.  Phi is evaluated as
-// erfc(-x / sqrt 2) / 2, which keeps its relative accuracy for negative x,
-// where 1 + erf(x / sqrt 2) cancels to zero in fp32 (below about x = -5.3).
+// fp32 vector roof: each erfcf costs a few dozen VALU operations.  Each lane
+// handles 8 consecutive hidden units of one token with 16-byte loads and
+// stores; arithmetic is fp32, with results rounded to nearest even in fp16.
+// Phi is evaluated as erfc(-x / sqrt 2) / 2 (gelu_cdf in sp24_device.hpp).
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "sp24_device.hpp"
 #include "sp24_internal.hpp"
 
 namespace sp24 {
 namespace {
 
 constexpr int kActThreads = 256;
-constexpr float kInvSqrt2 = 0.70710678118654752440f;
 constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -69,11 +68,7 @@ __global__ __launch_bounds__(kActThreads) void geglu_fwd_kernel(const uint16_t* 
   const h8 g = ld16(U + p.u_gate);
   h8 o;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = (float)g[e];
-    const float gelu = 0.5f * x * erfcf(-x * kInvSqrt2);
-    o[e] = (_Float16)((float)v[e] * gelu);
-  }
+  for (int e = 0; e < 8; ++e) o[e] = geglu_f16(v[e], g[e]);
   st16(out + p.o, o);
 }
 
@@ -91,7 +86,7 @@ __global__ __launch_bounds__(kActThreads) void geglu_bwd_kernel(const uint16_t* 
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float x = (float)g[e], dy = (float)d[e];
-    const float cdf = 0.5f * erfcf(-x * kInvSqrt2);
+    const float cdf = gelu_cdf(x);
     const float pdf = kInvSqrt2Pi * expf(-0.5f * x * x);
     dv[e] = (_Float16)(dy * (x * cdf));
     dg[e] = (_Float16)(dy * (float)v[e] * (cdf + x * pdf));

@@ -142,6 +142,26 @@ int sp24_spmm_fwd(const void* X, const void* vals_row, const uint16_t* meta_row,
   return spmm_common(X, vals_row, meta_row, T, R, C, Y, stream);
 }
 
+int sp24_spmm_fwd_geglu(const void* X, const void* vals_row, const uint16_t* meta_row, int64_t T, int64_t R,
+                        int64_t C, void* U, void* out, void* stream) {
+  if (T < 0) return SP24_ERR_SHAPE;
+  int st = check_dims(R, C, 16);
+  if (st != SP24_OK) return st;
+  if (R % 32 != 0) return SP24_ERR_SHAPE;
+  if (T >= kMaxDim) return SP24_ERR_TOO_LARGE;
+  if (T != 0 && (C >= kMaxElems / T || R >= kMaxElems / T)) return SP24_ERR_TOO_LARGE;
+  if (T == 0 || R == 0) return SP24_OK;
+  if (out == nullptr || (C != 0 && (X == nullptr || vals_row == nullptr || meta_row == nullptr))) return SP24_ERR_NULL;
+  if (!aligned16(out) || (U && !aligned16(U)) ||
+      (C != 0 && (!aligned16(X) || !aligned16(vals_row) || !aligned16(meta_row))))
+    return SP24_ERR_ALIGN;
+  const hipError_t e = sp24::launch_spmm_nt_geglu(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(vals_row),
+                                                  meta_row, T, R, C, static_cast<uint16_t*>(U),
+                                                  static_cast<uint16_t*>(out), as_stream(stream));
+  if (e == hipErrorNotSupported) return SP24_ERR_UNSUPPORTED;
+  return launch_status(e);
+}
+
 int sp24_spmm_bwd_input(const void* dY, const void* vals_col, const uint16_t* meta_col, int64_t T, int64_t R,
                         int64_t C, void* dX, void* stream) {
   // dX[T][C] = dY[T][R] * Ws: output features C, reduction over R
@@ -214,6 +234,6 @@ int sp24_pattern_table(uint16_t* out) {
   return SP24_OK;
 }
 
-int sp24_abi_version(void) { return 5; }
+int sp24_abi_version(void) { return 6; }
 
 }  // extern "C"

@@ -39,6 +39,18 @@ __device__ __forceinline__ void dma_b32(i32x4 rsrc, uint32_t lds, int voffset) {
   asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" : : "v"(voffset), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
+// GELU(x) = x * Phi(x), Phi(x) = erfc(-x / sqrt 2) / 2: the erfc form keeps
+// its relative accuracy for negative x, where 1 + erf(x / sqrt 2) cancels to
+// zero in fp32 (below about x = -5.3).  Shared by the GEGLU kernels and the
+// fused GEGLU epilogue of the forward GEMM, so that both give identical bits.
+constexpr float kInvSqrt2 = 0.70710678118654752440f;
+__device__ __forceinline__ float gelu_cdf(float x) { return 0.5f * erfcf(-x * kInvSqrt2); }
+__device__ __forceinline__ float gelu_f32(float x) { return x * gelu_cdf(x); }
+// value * GELU(gate) from fp16 inputs, rounded to nearest even in fp16
+__device__ __forceinline__ _Float16 geglu_f16(_Float16 value, _Float16 gate) {
+  return (_Float16)((float)value * gelu_f32((float)gate));
+}
+
 // Number of compute units of the current device (cached per device).
 inline int device_cu_count() {
   static int cached[64] = {0};

@@ -68,4 +68,11 @@ hipError_t launch_mvue(const uint16_t* M, const float* U, int64_t rows, int64_t 
 hipError_t launch_spmm_nt(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T,
                           int64_t N, int64_t K, uint16_t* out, hipStream_t s);
 
+// The same product with GEGLU fused into the epilogue: S's rows in blocks of
+// 32 (16 value rows, then their 16 gate rows); gout[T][N/2] = value *
+// GELU(gate) of the fp16 products.  out (the products, [T][N]) may be null
+// when the fast path applies; otherwise hipErrorNotSupported.  N % 32 == 0.
+hipError_t launch_spmm_nt_geglu(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T,
+                                int64_t N, int64_t K, uint16_t* out, uint16_t* gout, hipStream_t s);
+
 }  // namespace sp24

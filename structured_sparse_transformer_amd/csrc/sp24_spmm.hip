@@ -273,10 +273,16 @@ struct FastCfg {
   static_assert(LOADS <= 63, "vmcnt range");
 };
 
-template <int BM, int BN, int WM, int WN>
+// kGeglu: the feature rows of S come in blocks of 32, 16 value rows then the
+// 16 matching gate rows, and the epilogue also writes gout[T][ldg] columns
+// [0, N/2) = value * GELU(gate) from the fp16-rounded products, with the
+// GEGLU kernel's GELU code.  `out` may then be null (the products are not
+// stored).
+template <int BM, int BN, int WM, int WN, bool kGeglu>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ vals, const uint16_t* __restrict__ meta,
-    int64_t T, int64_t N, int64_t K, uint16_t* __restrict__ out, int64_t ldo, int tiles_m, int tiles_n) {
+    int64_t T, int64_t N, int64_t K, uint16_t* __restrict__ out, int64_t ldo, uint16_t* __restrict__ gout,
+    int64_t ldg, int tiles_m, int tiles_n) {
   using Cfg = FastCfg<BM, BN, WM, WN>;
   // one LDS block: 3 S slots, 3 B slots, 3 meta slots (the epilogue reuses
   // the start of it to stage the output tile)
@@ -501,44 +507,131 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
   static_assert(WM == 128, "epilogue assumes 16 chunks of 8 features per token row");
   __builtin_amdgcn_s_barrier();
   unsigned char* stage_base = smem + (size_t)wave * WN * WM * 2;
+  auto h2 = [](float x, float y) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x) | (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y)
+                                                                     << 16;
+  };
+  if constexpr (!kGeglu) {
 #pragma unroll
-  for (int mt = 0; mt < Cfg::TM; ++mt)
+    for (int mt = 0; mt < Cfg::TM; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < Cfg::TN; ++nt) {
-      const int t = nt * 32 + l32;                     // token within the wave tile
+      for (int nt = 0; nt < Cfg::TN; ++nt) {
+        const int t = nt * 32 + l32;                     // token within the wave tile
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f16v& a = acc[mt][nt];
-        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a[4 * i4 + 0]) |
-                            (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a[4 * i4 + 1]) << 16;
-        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a[4 * i4 + 2]) |
-                            (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a[4 * i4 + 3]) << 16;
-        const int chunk = mt * 4 + i4;                 // 8 features per chunk: mt*32 + 8*i4 + 4g
-        *reinterpret_cast<uint2*>(stage_base + t * 256 + ((chunk ^ (t & 15)) * 16) + 8 * g) = make_uint2(lo, hi);
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f16v& a = acc[mt][nt];
+          const uint32_t lo = h2(a[4 * i4 + 0], a[4 * i4 + 1]);
+          const uint32_t hi = h2(a[4 * i4 + 2], a[4 * i4 + 3]);
+          const int chunk = mt * 4 + i4;                 // 8 features per chunk: mt*32 + 8*i4 + 4g
+          *reinterpret_cast<uint2*>(stage_base + t * 256 + ((chunk ^ (t & 15)) * 16) + 8 * g) = make_uint2(lo, hi);
+        }
       }
-    }
-  // the wave reads back only what it wrote, in order, so no barrier is needed
+    // the wave reads back only what it wrote, in order, so no barrier is needed
 #pragma unroll 4
-  for (int it = 0; it < WN * 16 / 64; ++it) {
-    const int t = it * 4 + lane / 16, c = lane % 16;
-    const uint4 v = *reinterpret_cast<const uint4*>(stage_base + t * 256 + ((c ^ (t & 15)) * 16));
-    const int64_t n = n0 + wn * WN + t;
-    const int64_t m = m0 + wm * WM + c * 8;
-    if (n < T && m < N) *reinterpret_cast<uint4*>(out + n * ldo + m) = v;
+    for (int it = 0; it < WN * 16 / 64; ++it) {
+      const int t = it * 4 + lane / 16, c = lane % 16;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage_base + t * 256 + ((c ^ (t & 15)) * 16));
+      const int64_t n = n0 + wn * WN + t;
+      const int64_t m = m0 + wm * WM + c * 8;
+      if (n < T && m < N) *reinterpret_cast<uint4*>(out + n * ldo + m) = v;
+    }
+  } else {
+    // The products are rounded to fp16 first (packed in pairs, which also
+    // frees half the accumulator registers for the GELU arithmetic).
+    uint32_t pk[Cfg::TM][Cfg::TN][8];
+#pragma unroll
+    for (int mt = 0; mt < Cfg::TM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < Cfg::TN; ++nt)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pk[mt][nt][j] = h2(acc[mt][nt][2 * j], acc[mt][nt][2 * j + 1]);
+    if (out != nullptr) {
+#pragma unroll
+      for (int mt = 0; mt < Cfg::TM; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < Cfg::TN; ++nt) {
+          const int t = nt * 32 + l32;
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int chunk = mt * 4 + i4;
+            *reinterpret_cast<uint2*>(stage_base + t * 256 + ((chunk ^ (t & 15)) * 16) + 8 * g) =
+                make_uint2(pk[mt][nt][2 * i4], pk[mt][nt][2 * i4 + 1]);
+          }
+        }
+#pragma unroll 4
+      for (int it = 0; it < WN * 16 / 64; ++it) {
+        const int t = it * 4 + lane / 16, c = lane % 16;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage_base + t * 256 + ((c ^ (t & 15)) * 16));
+        const int64_t n = n0 + wn * WN + t;
+        const int64_t m = m0 + wm * WM + c * 8;
+        if (n < T && m < N) *reinterpret_cast<uint4*>(out + n * ldo + m) = v;
+      }
+      // this wave's reads of the staged products are back before the GEGLU
+      // outputs overwrite them (lgkmcnt(0))
+      __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
+    }
+    // Accumulators 4*i4 + e (i4 < 2) and 4*(i4+2) + e of a 32-feature block
+    // are features r and r + 16 of one token: a value and its gate.  The
+    // WM/2 outputs per token are staged like the products (8 per chunk, chunk
+    // index XOR-swizzled by token).
+    auto half_of = [](uint32_t w, int hi) { return __builtin_bit_cast(_Float16, (uint16_t)(hi ? w >> 16 : w)); };
+#pragma unroll
+    for (int mt = 0; mt < Cfg::TM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < Cfg::TN; ++nt) {
+        const int t = nt * 32 + l32;
+#pragma unroll
+        for (int i4 = 0; i4 < 2; ++i4) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = (float)geglu_f16(half_of(pk[mt][nt][2 * i4 + e / 2], e & 1),
+                                    half_of(pk[mt][nt][2 * (i4 + 2) + e / 2], e & 1));
+          const int chunk = mt * 2 + i4;                 // outputs mt*16 + 8*i4 + 4g + e
+          *reinterpret_cast<uint2*>(stage_base + t * 128 + ((chunk ^ (t & 7)) * 16) + 8 * g) =
+              make_uint2(h2(o[0], o[1]), h2(o[2], o[3]));
+        }
+      }
+#pragma unroll 4
+    for (int it = 0; it < WN * 8 / 64; ++it) {
+      const int t = it * 8 + lane / 8, c = lane % 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage_base + t * 128 + ((c ^ (t & 7)) * 16));
+      const int64_t n = n0 + wn * WN + t;
+      const int64_t m = (m0 + wm * WM) / 2 + c * 8;
+      if (n < T && m < N / 2) *reinterpret_cast<uint4*>(gout + n * ldg + m) = v;
+    }
   }
 }
 
-// out[T][ldo] columns [0, N) = A * S^T for the N feature rows of S given.
-template <int BM, int BN, int WM, int WN>
+// out[T][ldo] columns [0, N) = A * S^T for the N feature rows of S given;
+// with kGeglu also gout[T][ldg] columns [0, N/2).
+template <int BM, int BN, int WM, int WN, bool kGeglu = false>
 hipError_t launch_fast(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T, int64_t N,
-                       int64_t K, uint16_t* out, int64_t ldo, hipStream_t s) {
+                       int64_t K, uint16_t* out, int64_t ldo, hipStream_t s, uint16_t* gout = nullptr,
+                       int64_t ldg = 0) {
   using Cfg = FastCfg<BM, BN, WM, WN>;
   const int tiles_m = (int)((N + BM - 1) / BM), tiles_n = (int)((T + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
   const int grid = ((ntiles + 7) / 8) * 8;
-  hipLaunchKernelGGL((spmm_nt_fast_kernel<BM, BN, WM, WN>), dim3(grid), dim3(Cfg::THREADS), 0, s, A, vals, meta, T, N,
-                     K, out, ldo, tiles_m, tiles_n);
+  hipLaunchKernelGGL((spmm_nt_fast_kernel<BM, BN, WM, WN, kGeglu>), dim3(grid), dim3(Cfg::THREADS), 0, s, A, vals,
+                     meta, T, N, K, out, ldo, gout, ldg, tiles_m, tiles_n);
   return hipGetLastError();
+}
+
+bool fast_path(int64_t T, int64_t N, int64_t K) {
+  constexpr int64_t kMaxBuf = (int64_t)1 << 31;   // buffer offsets are 32-bit
+  return K % 64 == 0 && K > 0 && T * K * 2 < kMaxBuf && N * K < kMaxBuf && T * N * 2 < ((int64_t)1 << 40);
+}
+
+// The feature rows that fill whole rounds of 256 x 256 tiles on the device,
+// when the remaining 256-feature strip is better run as 256 x 64 tiles (see
+// launch_spmm_nt); 0 when no split pays.
+int64_t split_features(int64_t T, int64_t N) {
+  const int64_t cus = device_cu_count();
+  const int64_t tiles_n = (T + 255) / 256, tiles_m = (N + 255) / 256;
+  if (tiles_m > 1 && (tiles_m * tiles_n) % cus != 0 && ((tiles_m - 1) * tiles_n) % cus == 0 && (T + 63) / 64 <= cus)
+    return (tiles_m - 1) * 256;
+  return 0;
 }
 
 }  // namespace
@@ -546,19 +639,14 @@ hipError_t launch_fast(const uint16_t* A, const uint16_t* vals, const uint16_t* 
 hipError_t launch_spmm_nt(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T, int64_t N,
                           int64_t K, uint16_t* out, hipStream_t s) {
   if (T == 0 || N == 0) return hipSuccess;
-  constexpr int64_t kMaxBuf = (int64_t)1 << 31;   // buffer offsets are 32-bit
-  const bool fast = K % 64 == 0 && K > 0 && T * K * 2 < kMaxBuf && N * K < kMaxBuf && T * N * 2 < ((int64_t)1 << 40);
-  if (fast) {
+  if (fast_path(T, N, K)) {
     // 256 x 256 tiles, 8 waves (two per SIMD) of 128 features x 64 tokens.
     // When the tile count leaves a last, partly filled round of workgroups,
     // the leading feature tiles that fill whole rounds run first and the last
     // 256-feature strip runs as 256 x 64 tiles, four times as many and a
     // quarter of the work each, so the tail takes a fraction of a round.
-    const int64_t cus = device_cu_count();
-    const int64_t tiles_n = (T + 255) / 256, tiles_m = (N + 255) / 256;
-    if (tiles_m > 1 && (tiles_m * tiles_n) % cus != 0 && ((tiles_m - 1) * tiles_n) % cus == 0 &&
-        (T + 63) / 64 <= cus) {
-      const int64_t n1 = (tiles_m - 1) * 256;
+    const int64_t n1 = split_features(T, N);
+    if (n1 > 0) {
       hipError_t e = launch_fast<256, 256, 128, 64>(A, vals, meta, T, n1, K, out, N, s);
       if (e != hipSuccess) return e;
       return launch_fast<256, 64, 128, 32>(A, vals + n1 * (K / 2), meta + n1 * (K / 16), T, N - n1, K, out + n1, N, s);
@@ -566,6 +654,26 @@ hipError_t launch_spmm_nt(const uint16_t* A, const uint16_t* vals, const uint16_
     return launch_fast<256, 256, 128, 64>(A, vals, meta, T, N, K, out, N, s);
   }
   return launch_cfg<256, 128, 128, 64>(A, vals, meta, T, N, K, out, s);
+}
+
+hipError_t launch_spmm_nt_geglu(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T, int64_t N,
+                                int64_t K, uint16_t* out, uint16_t* gout, hipStream_t s) {
+  if (T == 0 || N == 0) return hipSuccess;
+  if (!fast_path(T, N, K)) {
+    // the products must be stored to apply GEGLU afterwards
+    if (out == nullptr) return hipErrorNotSupported;
+    const hipError_t e = launch_spmm_nt(A, vals, meta, T, N, K, out, s);
+    if (e != hipSuccess) return e;
+    return launch_geglu_fwd(out, T, N / 2, 16, gout, s);
+  }
+  const int64_t n1 = split_features(T, N);
+  if (n1 > 0) {
+    hipError_t e = launch_fast<256, 256, 128, 64, true>(A, vals, meta, T, n1, K, out, N, s, gout, N / 2);
+    if (e != hipSuccess) return e;
+    return launch_fast<256, 64, 128, 32, true>(A, vals + n1 * (K / 2), meta + n1 * (K / 16), T, N - n1, K,
+                                               out ? out + n1 : nullptr, N, s, gout + n1 / 2, N / 2);
+  }
+  return launch_fast<256, 256, 128, 64, true>(A, vals, meta, T, N, K, out, N, s, gout, N / 2);
 }
 
 }  // namespace sp24

@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_
                 5: "ERR_UNSUPPORTED", 6: "ERR_TOO_LARGE"}
 EXPORTS = ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
            "sp24_flip_count", "sp24_weight_grad", "sp24_geglu_fwd", "sp24_geglu_bwd", "sp24_mvue",
-           "sp24_spmm_fwd", "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table",
+           "sp24_spmm_fwd", "sp24_spmm_fwd_geglu", "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table",
            "sp24_abi_version")
 MAX_BATCH = 8
 
@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "sp24_geglu_bwd": [p, p, i64, i64, i64, p, p],
             "sp24_mvue": [p, p, i64, i64, p, p, p],
             "sp24_spmm_fwd": [p, p, p, i64, i64, i64, p, p],
+            "sp24_spmm_fwd_geglu": [p, p, p, i64, i64, i64, p, p, p],
             "sp24_spmm_bwd_input": [p, p, p, i64, i64, i64, p, p],
             "sp24_status_str": [i32],
             "sp24_pattern_table": [p],
@@ -282,6 +283,25 @@ def sp24_spmm_fwd(X, vals_row, meta_row, R, C, Y=None, stream=None):
     _check("sp24_spmm_fwd", lib().sp24_spmm_fwd(_ptr(X), _ptr(vals_row), _ptr(meta_row), T, R, C,
                                                 _ptr(Y), _stream(stream)))
     return Y
+
+
+def sp24_spmm_fwd_geglu(X, vals_row, meta_row, R, C, out=None, U=False, stream=None):
+    """out[T, R/2] = value * GELU(gate) of U = X * Ws^T, W's rows in blocks of
+    16 values then their 16 gates.  U=True also returns the products [T, R]
+    (a tensor may be passed instead); returns (out, U or None)."""
+    T = X.shape[0]
+    if X.dtype != torch.float16 or tuple(X.shape) != (T, C):
+        raise ValueError("X must be float16 [T, C]")
+    out = _out(out, (T, R // 2), torch.float16, X.device)
+    if U is True:
+        U = torch.empty(T, R, dtype=torch.float16, device=X.device)
+    elif U is False or U is None:
+        U = None
+    else:
+        U = _out(U, (T, R), torch.float16, X.device)
+    _check("sp24_spmm_fwd_geglu", lib().sp24_spmm_fwd_geglu(_ptr(X), _ptr(vals_row), _ptr(meta_row), T, R, C,
+                                                            _ptr(U), _ptr(out), _stream(stream)))
+    return out, U
 
 
 def sp24_spmm_bwd_input(dY, vals_col, meta_col, R, C, dX=None, stream=None):

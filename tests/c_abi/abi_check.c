@@ -27,7 +27,7 @@ int main(void) {
   unsigned key[90];
   int p, ones, r, c;
 
-  CHECK(sp24_abi_version() == 5);
+  CHECK(sp24_abi_version() == 6);
   CHECK(sp24_pattern_table(NULL) == SP24_ERR_NULL);
   CHECK(sp24_pattern_table(table) == SP24_OK);
   /* every pattern keeps two entries in each row and each column */
@@ -64,6 +64,7 @@ int main(void) {
   CHECK(sp24_weight_grad(fake, fake, fake, NULL, 0.5f, 8, 16, 16, (float*)fake, NULL) == SP24_ERR_NULL);
   CHECK(sp24_geglu_fwd(fake, 4, 24, 16, fake, NULL) == SP24_ERR_SHAPE);
   CHECK(sp24_geglu_bwd(fake, fake, 4, 16, 8, mis, NULL) == SP24_ERR_ALIGN);
+  CHECK(sp24_spmm_fwd_geglu(fake, fake, (uint16_t*)fake, 8, 48, 64, NULL, fake, NULL) == SP24_ERR_SHAPE);
   CHECK(sp24_mvue(fake, (const float*)fake, 4, 24, fake, (uint16_t*)fake, NULL) == SP24_ERR_SHAPE);
   {
     sp24_sc_job job;

@@ -39,7 +39,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
               "sp24_flip_count", "sp24_weight_grad", "sp24_geglu_fwd", "sp24_geglu_bwd", "sp24_mvue",
-              "sp24_spmm_fwd",
+              "sp24_spmm_fwd", "sp24_spmm_fwd_geglu",
               "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table", "sp24_abi_version"):
         assert n in names
 
@@ -59,7 +59,7 @@ def test_pattern_table_matches_oracle(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sp24_abi_version() == 5
+    assert L.sp24_abi_version() == 6
     for s in range(7):
         assert L.sp24_status_str(s)
     assert L.sp24_status_str(99) == b"unknown status"
@@ -221,3 +221,15 @@ def test_mvue_validation(L):
     assert f(FAKE, MIS, 4, 16, FAKE, FAKE, NUL) == 3
     assert f(FAKE, FAKE, 1 << 31, 16, FAKE, FAKE, NUL) == 6
     assert f(NUL, NUL, 0, 16, NUL, NUL, NUL) == 0
+
+
+def test_spmm_fwd_geglu_validation(L):
+    f = L.sp24_spmm_fwd_geglu
+    assert f(FAKE, FAKE, FAKE, 8, 48, 64, NUL, FAKE, NUL) == 2      # R % 32
+    assert f(FAKE, FAKE, FAKE, 8, 64, 20, NUL, FAKE, NUL) == 2      # C % 16
+    assert f(FAKE, FAKE, FAKE, -1, 64, 64, NUL, FAKE, NUL) == 2
+    assert f(FAKE, FAKE, FAKE, 8, 64, 64, NUL, NUL, NUL) == 1
+    assert f(NUL, FAKE, FAKE, 8, 64, 64, NUL, FAKE, NUL) == 1
+    assert f(FAKE, FAKE, FAKE, 8, 64, 64, MIS, FAKE, NUL) == 3
+    assert f(FAKE, FAKE, FAKE, 8, 64, 64, NUL, MIS, NUL) == 3
+    assert f(NUL, NUL, NUL, 0, 64, 64, NUL, NUL, NUL) == 0

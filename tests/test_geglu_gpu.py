@@ -122,3 +122,83 @@ def test_geglu_full_size_sampled(sp, group):
     ri = torch.from_numpy(rows).cuda()
     check(out[ri].cpu().numpy(), O.geglu_fwd(U[rows], group))
     check(dU[ri].cpu().numpy(), O.geglu_bwd(U[rows], d[rows], group), gate_grad_slack(U[rows], d[rows], group))
+
+
+# ----------------------------------------------------------------------------
+# GEGLU fused into the forward sparse GEMM (W's rows in blocks of 16 values
+# then their 16 gates, so U has the group-16 layout).  The fused epilogue
+# evaluates the same GELU code as the GEGLU kernel on the same fp16 products,
+# but the device library's erfc is inlined into two very different kernels
+# and may contract its fp32 arithmetic differently, so an output that lies
+# within a hair of an fp16 rounding tie may come out one ulp apart.  The
+# tests therefore ask for the same fp16 products, outputs at most one fp16
+# ulp from the two-kernel path, and the GEGLU tolerance against the oracle
+# applied to those products.
+
+def _ordered(t):
+    """fp16 bit patterns mapped to integers in value order (+0 and -0 meet)."""
+    bits = t.cpu().numpy().view(np.uint16).astype(np.int32)
+    mag = bits & 0x7FFF
+    return np.where(bits & 0x8000, -mag, mag)
+
+
+def assert_within_one_ulp(a, b):
+    d = np.abs(_ordered(a) - _ordered(b))
+    assert (d <= 1).all(), int(d.max())
+
+def _fused_case(sp, T, R, C, seed):
+    W = WL.normal_f16(seed, 1, (R, C), 0.02)
+    X = WL.normal_f16(seed, 2, (T, C))
+    f = sp.sp24_search_compress(dev(W))
+    return W, X, f
+
+
+@pytest.mark.parametrize("T,R,C", [(1, 32, 64), (100, 96, 128), (300, 544, 320), (257, 256, 1024)])
+def test_fused_geglu_matches_gemm_then_geglu_bit_for_bit(sp, T, R, C):
+    W, X, f = _fused_case(sp, T, R, C, T + R)
+    out, U = sp.sp24_spmm_fwd_geglu(dev(X), f["vals_row"], f["meta_row"], R, C, U=True)
+    Y = sp.sp24_spmm_fwd(dev(X), f["vals_row"], f["meta_row"], R, C)
+    assert torch.equal(U, Y)
+    assert_within_one_ulp(out, sp.sp24_geglu_fwd(Y, 16))
+    check(out.cpu().numpy(), O.geglu_fwd(U.cpu().numpy(), 16))
+    out2, none = sp.sp24_spmm_fwd_geglu(dev(X), f["vals_row"], f["meta_row"], R, C)
+    assert none is None and torch.equal(out2, out)
+    # against the oracle: GEGLU of the float64 product, to the GEMM tolerance
+    c = O.compress(W, O.mask_search(W))
+    want = O.geglu_fwd(O.spmm_fwd(X, c["vals_row"], c["meta_row"], R, C), 16)
+    mr, ma = O.gemm_errors(out.cpu().numpy().astype(np.float64), want)
+    assert mr <= 1e-2 and ma <= 1e-3, (mr, ma)
+
+
+def test_fused_geglu_fallback_needs_products(sp):
+    """K (= C) not a multiple of 64: the library stores U and runs the GEGLU
+    kernel on it; without a U buffer it reports UNSUPPORTED."""
+    T, R, C = 40, 64, 80
+    W, X, f = _fused_case(sp, T, R, C, 5)
+    out, U = sp.sp24_spmm_fwd_geglu(dev(X), f["vals_row"], f["meta_row"], R, C, U=True)
+    assert torch.equal(out, sp.sp24_geglu_fwd(U, 16))       # this path runs the GEGLU kernel itself
+    with pytest.raises(sp.Sp24Error) as e:
+        sp.sp24_spmm_fwd_geglu(dev(X), f["vals_row"], f["meta_row"], R, C)
+    assert e.value.status == 5
+
+
+def test_fused_geglu_gpt2_1p5b_shape(sp):
+    """W1's shape of the 1.5B FFN (6400 x 1600, read as a gated layer with
+    h = 3200) over 16384 tokens: the 256-feature tail split is taken.  Same
+    products, and outputs within one ulp of the two-kernel path, everywhere;
+    the oracle on sampled rows."""
+    cfg = WL.GPT2_1P5B
+    inp = WL.ffn_inputs(cfg)
+    R, C = inp.w1.shape
+    f = sp.sp24_search_compress(dev(inp.w1))
+    dX = dev(inp.x)
+    out, U = sp.sp24_spmm_fwd_geglu(dX, f["vals_row"], f["meta_row"], R, C, U=True)
+    Y = sp.sp24_spmm_fwd(dX, f["vals_row"], f["meta_row"], R, C)
+    assert torch.equal(U, Y)
+    assert_within_one_ulp(out, sp.sp24_geglu_fwd(Y, 16))
+    rows = np.sort(np.random.default_rng(4).choice(inp.x.shape[0], size=32, replace=False))
+    c = O.compress(inp.w1, O.mask_search(inp.w1))
+    want = O.geglu_fwd(O.spmm_fwd(inp.x[rows], c["vals_row"], c["meta_row"], R, C), 16)
+    got = out[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    mr, ma = O.gemm_errors(got, want)
+    assert mr <= 1e-2 and ma <= 1e-3, (mr, ma)
