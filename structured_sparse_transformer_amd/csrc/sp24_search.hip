@@ -271,21 +271,20 @@ struct TileData {
   uint32_t prev4;   // four previous indices: block row tid/8, block columns 4*(tid%8) .. +3
 };
 
-// Previous indices of a tile, one dword (four blocks) per thread, issued
-// before the tile's W loads so that only they need to have arrived when the
-// dword is parked in LDS.
+// Previous indices of a tile, one dword (four blocks) per thread.  The loads
+// here and in load_tile are branch-free (indices past a partial tile are
+// clamped to its last block and the values never used), so the compiler can
+// count them exactly and wait for just the ones it needs.
 __device__ __forceinline__ void load_prev(const TileRef& tr, int tid, TileData& d) {
-  const int bi = tid / 8, bj4 = 4 * (tid % 8);
-  if (bi < tr.rows / 4 && bj4 < tr.cols / 4)
-    d.prev4 = *reinterpret_cast<const uint32_t*>(tr.jb.idx_prev + (tr.r0 / 4 + bi) * (tr.jb.C / 4) + tr.c0 / 4 + bj4);
+  const int bi = min(tid / 8, tr.rows / 4 - 1), bj4 = min(4 * (tid % 8), tr.cols / 4 - 4);
+  d.prev4 = *reinterpret_cast<const uint32_t*>(tr.jb.idx_prev + (tr.r0 / 4 + bi) * (tr.jb.C / 4) + tr.c0 / 4 + bj4);
 }
 
 __device__ __forceinline__ void load_tile(const TileRef& tr, int tid, TileData& d) {
-  const int bj = tid % kTB;
+  const int bj = min(tid % kTB, tr.cols / 4 - 1);
 #pragma unroll
   for (int q = 0; q < kBlocksPerThread; ++q) {
-    const int bi = tid / kTB + q * (kCompressThreads / kTB);
-    if (bi >= tr.rows / 4 || bj >= tr.cols / 4) continue;
+    const int bi = min(tid / kTB + q * (kCompressThreads / kTB), tr.rows / 4 - 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint2 v = *reinterpret_cast<const uint2*>(tr.jb.W + (tr.r0 + 4 * bi + r) * tr.jb.C + tr.c0 + 4 * bj);
@@ -392,11 +391,21 @@ __device__ __forceinline__ void write_tile(const TileRef& tr, int tid, const Com
   }
 }
 
+// Workgroup barrier for LDS hand-offs only: this wave's LDS accesses have
+// completed (lgkmcnt(0)) when it arrives.  __syncthreads() would also wait for
+// every outstanding global load and store (vmcnt(0)): tile 0's search would
+// wait for tile 1's loads, and tile 1's staging for tile 0's stores to be
+// acknowledged.  Register results of global loads are waited for where they
+// are used, as usual.  The memory clobber keeps the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Each workgroup handles kTilesPerWg tiles.  All of their loads are issued
-// first; tile k+1 is searched while the global stores of tile k drain, so
-// loading, searching and storing overlap within the workgroup instead of
-// running as three GPU-wide phases.  A job that counts flips gets one atomic
-// add per tile, after the tile's waves have pooled their counts in LDS.
+// first; tile 0 is searched as soon as its own loads land, and tile k+1 is
+// searched while the global stores of tile k drain, so loading, searching
+// and storing overlap within the workgroup instead of running as three
+// GPU-wide phases.  A job that counts flips gets one atomic add per
+// counter, after the tile's waves have pooled their counts in LDS.
 
 template <bool kSearch>
 __global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(ScJobs jobs) {
@@ -419,18 +428,21 @@ __global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(ScJob
   for (int k = 0; k < kTilesPerWg; ++k) {
     const int64_t t = grp * kTilesPerWg + k;
     have[k] = t < jobs.total_tiles;
-    if (have[k]) {
-      tr[k] = tile_ref(jobs, t);
-      if (kSearch && tr[k].jb.idx_prev) load_prev(tr[k], tid, td[k]);
-      load_tile(tr[k], tid, td[k]);
-    }
+    // a missing last tile loads the first one again (never staged), which
+    // keeps the load sequence the same for every workgroup
+    tr[k] = tile_ref(jobs, have[k] ? t : grp * kTilesPerWg);
   }
+#pragma unroll
+  for (int k = 0; k < kTilesPerWg; ++k)
+    if (kSearch && tr[k].jb.idx_prev) load_prev(tr[k], tid, td[k]);
+#pragma unroll
+  for (int k = 0; k < kTilesPerWg; ++k) load_tile(tr[k], tid, td[k]);
 #pragma unroll
   for (int k = 0; k < kTilesPerWg; ++k) {
     if (kSearch && have[k] && tr[k].jb.idx_prev && tid / 8 < tr[k].rows / 4 && 4 * (tid % 8) < tr[k].cols / 4)
       *reinterpret_cast<uint32_t*>(&sm.prev[k][tid / 8][4 * (tid % 8)]) = td[k].prev4;
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int k = 0; k < kTilesPerWg; ++k) {
     if (!have[k]) continue;
@@ -439,9 +451,9 @@ __global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(ScJob
       const uint32_t w = wave_sum(f);
       if (tid % 64 == 0) sm.flips[k][tid / 64] = w;
     }
-    __syncthreads();
+    lds_barrier();
     write_tile(tr[k], tid, sm);
-    __syncthreads();    // the staging buffer is read out before the next tile overwrites it
+    lds_barrier();    // the staging buffer is read out before the next tile overwrites it
   }
   if (kSearch && tid == 0) {
     // one atomic per counter: same-address device atomics serialise, and all
