@@ -77,7 +77,10 @@ What the method computes, and the readings taken where the pages are silent:
    makes the estimate unbiased.  A group with fewer than two non-zero entries
    is kept as it is.  The output is the library's 2:4 row form.  Every
    decision is taken in fp32 in the order written in ``mvue_group``, so that
-   an implementation with the same fp32 operations reproduces it bit for bit.
+   an implementation with the same fp32 operations reproduces it bit for bit;
+   that order compares cumulative masses with u times a scale instead of
+   dividing (the same decisions in exact arithmetic), and a kept value is
+   sign(a_i) times that scale, so no step divides.
 """
 from __future__ import annotations
 
@@ -342,6 +345,17 @@ def mvue_group(a: np.ndarray, u: np.float32) -> tuple:
 
     Returns (i, k, value_i, value_k) with i < k, values as fp32.  All
     arithmetic is fp32 (numpy float32 scalars round every operation).
+
+    The probabilities are carried as masses w_j over a common scale D, with
+    p_j = w_j / D and sum p_j = 2 (so sum w_j = 2 D):
+      uncapped  w_j = |a_j|, D = S / 2;
+      capped k  w_j = |a_j| for j != k, w_k = D = S - |a_k| (so p_k = 1).
+    A cumulative sum C_j = W_j / D (W_j = w_0 + .. + w_j) is compared with u
+    as W_j <= u D, and with u + 1 as W_j <= u D + D.  A kept entry's value
+    a_j / p_j is then a_j itself for the capped entry and sign(a_j) D for
+    any other entry with a_j != 0.  In exact arithmetic this is the
+    definition; in fp32 it has no division, and every sum of fp16
+    magnitudes in it is exact unless they span more than 11 binades.
     """
     f = np.float32
     m = [f(abs(f(x))) for x in a]
@@ -354,29 +368,37 @@ def mvue_group(a: np.ndarray, u: np.float32) -> tuple:
         i, k = min(i, k), max(i, k)
         return i, k, f(a[i]), f(a[k])
     S = f(f(f(m[0] + m[1]) + m[2]) + m[3])
-    p = [f(f(2) * m[i]) / S for i in range(4)]
-    over = [i for i in range(4) if p[i] > f(1)]
-    if over:
-        kc = over[0]
-        rest = f(0)
+    # p_k > 1  <=>  2 |a_k| > S; at most one entry can satisfy it
+    over = [i for i in range(4) if f(2) * m[i] > S]
+    kc = over[0] if over else -1
+    if kc >= 0:
+        D = f(0)
         for j in range(4):
             if j != kc:
-                rest = f(rest + m[j])
-        p = [f(1) if j == kc else m[j] / rest for j in range(4)]
-    C0 = p[0]
-    C1 = f(C0 + p[1])
-    C2 = f(C1 + p[2])
-    u = f(u)
-    u1 = f(u + f(1))
-    i = int(C0 <= u) + int(C1 <= u) + int(C2 <= u)
-    k = int(C0 <= u1) + int(C1 <= u1) + int(C2 <= u1)
+                D = f(D + m[j])
+        w = [D if j == kc else m[j] for j in range(4)]
+    else:
+        D = f(S * f(0.5))
+        w = m
+    W0 = w[0]
+    W1 = f(W0 + w[1])
+    W2 = f(W1 + w[2])
+    uD = f(f(u) * D)
+    uD1 = f(uD + D)
+    i = int(W0 <= uD) + int(W1 <= uD) + int(W2 <= uD)
+    k = int(W0 <= uD1) + int(W1 <= uD1) + int(W2 <= uD1)
     if k == i:
         if i < 3:
             k = i + 1
         else:
             i, k = 2, 3
-    val = lambda j: f(a[j]) / p[j] if p[j] > 0 else f(0)  # noqa: E731
-    return i, k, f(val(i)), f(val(k))
+
+    def val(j):
+        if j == kc:
+            return f(a[j])
+        return f(np.copysign(D, f(a[j]))) if m[j] != 0 else f(0)
+
+    return i, k, val(i), val(k)
 
 
 def mvue(M: np.ndarray, U: np.ndarray) -> dict:

@@ -504,6 +504,9 @@ def test_mvue_worked_examples():
     one = np.array([1, 1, 1, 1], np.float16)
     assert O.mvue_group(one, np.float32(0.25)) == (0, 2, 2.0, 2.0)      # C = 0.5, 1, 1.5
     assert O.mvue_group(one, np.float32(0.75)) == (1, 3, 2.0, 2.0)
+    # u on a cumulative sum: the intervals are half-open, [C_(j-1), C_j)
+    assert O.mvue_group(one, np.float32(0.5)) == (1, 3, 2.0, 2.0)       # u = C0, u + 1 = C2
+    assert O.mvue_group(one, np.float32(0.0)) == (0, 2, 2.0, 2.0)       # u + 1 = C1
     dom = np.array([8, 1, 1, 0], np.float16)                          # p = 1 (capped), 1/2, 1/2, 0
     assert O.mvue_group(dom, np.float32(0.1)) == (0, 1, 8.0, 2.0)
     assert O.mvue_group(dom, np.float32(0.6)) == (0, 2, 8.0, 2.0)
@@ -536,6 +539,47 @@ def test_mvue_unbiased_with_minimum_variance():
         var = sq - a.astype(np.float64) ** 2
         want = np.where(p > 0, a.astype(np.float64) ** 2 * (1 / np.where(p > 0, p, 1) - 1), 0)
         assert np.allclose(var, want, rtol=0, atol=5e-3 * (a.astype(np.float64) ** 2).max() + 1e-9)
+
+
+def test_mvue_matches_exact_rational_definition():
+    """Picks and kept values against the estimator's definition evaluated in
+    exact rational arithmetic: p_i = 2|a_i|/S, the cap at 1 with the others
+    rescaled by S - |a_k|, the cumulative sums, the intervals holding u and
+    u + 1, and a_i / p_i.  Magnitudes span under 11 binades, so the fp32 sums
+    are exact; draws with u within 1e-6 of a cumulative sum are skipped."""
+    from fractions import Fraction as Fr
+    rng = np.random.default_rng(62)
+    checked = capped = 0
+    for _ in range(4000):
+        mag = rng.uniform(0.25, 8.0, 4)
+        mag[rng.random(4) < 0.1] *= 16.0            # some groups get a capped entry
+        a = (rng.choice([-1.0, 1.0], 4) * mag).astype(np.float16)
+        a[rng.random(4) < 0.15] = 0
+        u = np.float32(rng.random())
+        m = [abs(Fr(float(x))) for x in a]
+        if sum(1 for x in m if x) < 2:
+            continue
+        S = sum(m)
+        p = [2 * x / S for x in m]
+        over = [j for j in range(4) if p[j] > 1]
+        if over:
+            kc = over[0]
+            p = [Fr(1) if j == kc else m[j] / (S - m[kc]) for j in range(4)]
+        assert sum(p) == 2
+        C = [p[0], p[0] + p[1], p[0] + p[1] + p[2]]
+        uf = Fr(float(u))
+        if any(abs(c - uf) < Fr(1, 10**6) or abs(c - uf - 1) < Fr(1, 10**6) for c in C):
+            continue
+        i = sum(c <= uf for c in C)
+        k = sum(c <= uf + 1 for c in C)
+        got = O.mvue_group(a, u)
+        assert got[:2] == (i, k), (a, u)
+        for j, v in ((i, got[2]), (k, got[3])):
+            want = Fr(float(a[j])) / p[j] if p[j] else Fr(0)
+            assert Fr(float(v)) == want, (a, u, j)
+        checked += 1
+        capped += bool(over)
+    assert checked > 3000 and capped > 300
 
 
 def test_mvue_matrix_form():
