@@ -306,8 +306,14 @@ int sp24_geglu_bwd(const void* U, const void* dout, int64_t T, int64_t h, int64_
  *   - Kept values are a_i / p_i (0 where p_i == 0).  A group with fewer than
  *     two non-zero entries keeps its non-zero entry (if any) and the lowest
  *     other index, unchanged.
- * All arithmetic is fp32 in the order above, with IEEE division.  Values are
- * rounded to nearest even in fp16, so results are reproducible bit for bit.
+ * Evaluation, all fp32, in this order, without division: with D = S/2
+ * (uncapped) or D = S - |a_k| (capped k, the first with 2|a_k| > S; the sum of
+ * the other three left to right), masses w_j = |a_j| (w_k = D) and their
+ * running sums W_0..W_2, the test C_j <= u is W_j <= u*D and C_j <= u + 1 is
+ * W_j <= u*D + D.  A kept value is a_k for the capped entry and +-D (the sign
+ * of a_j) for any other non-zero entry: a_j / p_j in exact arithmetic.
+ * Values are rounded to nearest even in fp16, so results are reproducible bit
+ * for bit.  An estimate beyond the fp16 range (|D| > 65504) becomes +-inf.
  *
  *   M      in   fp16 [rows, cols], the gradient (finite)
  *   U      in   fp32 [rows, cols/4], one uniform u in [0, 1) per group,

@@ -12,14 +12,18 @@
 // so the estimate is unbiased.  A group with fewer than two non-zero entries
 // is kept as it is.
 //
-// Every step is fp32, in a fixed order, with IEEE division and no contraction,
-// so the picks and values are reproducible bit for bit.  Output: the
+// Every step is fp32, in a fixed order and without contraction, so the picks
+// and values are reproducible bit for bit; the order (mvue_group) compares
+// cumulative masses instead of dividing, the same decisions in exact
+// arithmetic.  Output: the
 // library's 2:4 row form (vals fp16 [rows][cols/2], meta [rows][cols/16], one
 // nibble i0 | i1 << 2 per group), which the sparse GEMM consumes directly.
 //
 // Bound by HBM: per entry it reads 2 bytes of the gradient and 1 of u (4 bytes
-// per group) and writes 1.125 bytes.  One lane handles 16 entries (one meta
-// word) with 16-byte accesses.
+// per group) and writes 1.125 bytes, against about 50 VALU operations per
+// group.  One lane handles 16 entries (one meta word) with 16-byte accesses;
+// splitting a lane's entries into two wave-contiguous halves, or giving each
+// lane 8, measured slower.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -39,62 +43,72 @@ struct Pick {
   float vi, vk;
 };
 
+// v[j] for j in 0..3 as two levels of selects on j's bits (a compare chain
+// would become a switch, lowered to branches)
+__device__ __forceinline__ float sel4(const float (&v)[4], int j) {
+  const float lo = (j & 1) ? v[1] : v[0];
+  const float hi = (j & 1) ? v[3] : v[2];
+  return (j & 2) ? hi : lo;
+}
+
+// The probabilities are carried as masses w_j over a scale D (p_j = w_j / D,
+// sum w_j = 2D): uncapped, w_j = |a_j| and D = S/2; with entry c capped,
+// w_j = |a_j| for j != c and w_c = D = S - |a_c|.  C_j <= u then reads
+// W_j <= u D on the cumulative masses W_j, and a kept value a_j / p_j is a_c
+// for the capped entry and sign(a_j) D for any other non-zero entry.  No step
+// divides, and every choice is a select, so a wave never splits.
 __device__ __forceinline__ Pick mvue_group(const float (&a)[4], float u) {
   float m[4];
-  int nz = 0, first_nz = -1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = __builtin_fabsf(a[i]);
-    if (m[i] != 0.0f) {
-      if (first_nz < 0) first_nz = i;
-      ++nz;
-    }
-  }
-  Pick r;
-  if (nz < 2) {
-    int i = first_nz < 0 ? 0 : first_nz;
-    int k = i == 0 ? 1 : 0;
-    if (k < i) {
-      const int t = i;
-      i = k;
-      k = t;
-    }
-    r.nib = (uint32_t)(i | (k << 2));
-    r.vi = a[i];
-    r.vk = a[k];
-    return r;
-  }
+  for (int j = 0; j < 4; ++j) m[j] = __builtin_fabsf(a[j]);
   const float S = ((m[0] + m[1]) + m[2]) + m[3];
-  float p[4];
+  // p_c > 1 <=> 2|a_c| > S.  At most one entry can satisfy it: the rounded
+  // running sum S is at least the rounded sum of any two entries, which is
+  // at least twice the smaller one.
+  bool cap[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = (2.0f * m[i]) / S;
-  int kc = -1;
+  for (int j = 0; j < 4; ++j) cap[j] = 2.0f * m[j] > S;
+  const bool capped = (cap[0] | cap[1]) | (cap[2] | cap[3]);
+  // the ordered sum of the other three: a zero in the capped slot adds nothing
+  float o[4];
 #pragma unroll
-  for (int i = 3; i >= 0; --i)
-    if (p[i] > 1.0f) kc = i;
-  if (kc >= 0) {
-    float rest = 0.0f;
+  for (int j = 0; j < 4; ++j) o[j] = cap[j] ? 0.0f : m[j];
+  const float rest = ((o[0] + o[1]) + o[2]) + o[3];
+  const float D = capped ? rest : S * 0.5f;
+  float w[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (j != kc) rest = rest + m[j];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = j == kc ? 1.0f : m[j] / rest;
-  }
-  const float C0 = p[0], C1 = C0 + p[1], C2 = C1 + p[2];
-  const float u1 = u + 1.0f;
-  int i = (C0 <= u) + (C1 <= u) + (C2 <= u);
-  int k = (C0 <= u1) + (C1 <= u1) + (C2 <= u1);
-  if (k == i) {
-    if (i < 3) {
-      k = i + 1;
-    } else {
-      i = 2;
-      k = 3;
-    }
-  }
+  for (int j = 0; j < 4; ++j) w[j] = cap[j] ? D : m[j];
+  const float W0 = w[0], W1 = W0 + w[1], W2 = W1 + w[2];
+  const float uD = u * D, uD1 = uD + D;
+  int i = (int)(W0 <= uD) + (int)(W1 <= uD) + (int)(W2 <= uD);
+  int k = (int)(W0 <= uD1) + (int)(W1 <= uD1) + (int)(W2 <= uD1);
+  // rounding can put u and u + 1 in one interval: take the next one, or
+  // (2, 3) from the last
+  const bool same = k == i;
+  k = same ? (i < 3 ? i + 1 : 3) : k;
+  i = same && i == 3 ? 2 : i;
+  // fewer than two non-zero entries: keep the non-zero one (if any) and the
+  // lowest other index, both exactly
+  const int nz = (int)(m[0] != 0.0f) + (int)(m[1] != 0.0f) + (int)(m[2] != 0.0f) + (int)(m[3] != 0.0f);
+  const bool few = nz < 2;
+  const int only = m[1] != 0.0f ? 1 : m[2] != 0.0f ? 2 : m[3] != 0.0f ? 3 : 1;
+  i = few ? 0 : i;
+  k = few ? (m[0] != 0.0f ? 1 : only) : k;
+  const uint32_t capbits = (uint32_t)cap[0] | (uint32_t)cap[1] << 1 | (uint32_t)cap[2] << 2 | (uint32_t)cap[3] << 3;
+  // the kept values, computed for the two picks only
+  // (sign(a_j) D, or +0 for a zero a_j, built from the bits)
+  const uint32_t dbits = __builtin_bit_cast(uint32_t, D);
+  auto value = [&](int j) {
+    const uint32_t ab = __builtin_bit_cast(uint32_t, sel4(a, j));
+    const bool exact = few | (((capbits >> j) & 1u) != 0);
+    const uint32_t nonzero = 0u - (uint32_t)((ab << 1) != 0u);
+    const uint32_t est = (dbits | (ab & 0x80000000u)) & nonzero;
+    return __builtin_bit_cast(float, exact ? ab : est);
+  };
+  Pick r;
   r.nib = (uint32_t)(i | (k << 2));
-  r.vi = p[i] > 0.0f ? a[i] / p[i] : 0.0f;
-  r.vk = p[k] > 0.0f ? a[k] / p[k] : 0.0f;
+  r.vi = value(i);
+  r.vk = value(k);
   return r;
 }
 
