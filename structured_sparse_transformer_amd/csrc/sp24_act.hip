@@ -13,10 +13,11 @@
 // Per hidden unit and token the forward moves 6 bytes (read value and gate,
 // write out) and the backward 10 (read value, gate and dOut, write both
 // gradients).  At these rates the kernels sit between the HBM roof and the
-// fp32 vector roof: each erfcf costs a few dozen VALU operations.  Each lane
+// fp32 vector roof.  Each lane
 // handles 8 consecutive hidden units of one token with 16-byte loads and
 // stores; arithmetic is fp32, with results rounded to nearest even in fp16.
-// Phi is evaluated as erfc(-x / sqrt 2) / 2 (gelu_cdf in sp24_device.hpp).
+// Phi and phi come from gelu_cdf / gelu_cdf_pdf (sp24_device.hpp): a fitted
+// erfc with one reciprocal and one exponential, about 35 VALU operations.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -27,7 +28,6 @@ namespace sp24 {
 namespace {
 
 constexpr int kActThreads = 256;
-constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -86,8 +86,8 @@ __global__ __launch_bounds__(kActThreads) void geglu_bwd_kernel(const uint16_t* 
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float x = (float)g[e], dy = (float)d[e];
-    const float cdf = gelu_cdf(x);
-    const float pdf = kInvSqrt2Pi * expf(-0.5f * x * x);
+    float cdf, pdf;
+    gelu_cdf_pdf(x, cdf, pdf);
     dv[e] = (_Float16)(dy * (x * cdf));
     dg[e] = (_Float16)(dy * (float)v[e] * (cdf + x * pdf));
   }

@@ -42,9 +42,65 @@ __device__ __forceinline__ void dma_b32(i32x4 rsrc, uint32_t lds, int voffset) {
 // GELU(x) = x * Phi(x), Phi(x) = erfc(-x / sqrt 2) / 2: the erfc form keeps
 // its relative accuracy for negative x, where 1 + erf(x / sqrt 2) cancels to
 // zero in fp32 (below about x = -5.3).  Shared by the GEGLU kernels and the
-// fused GEGLU epilogue of the forward GEMM, so that both give identical bits.
+// fused GEGLU epilogue of the forward GEMM.
+//
+// erfc(z), z = |x| / sqrt 2 >= 0, is evaluated as t * exp(-z^2 + P(t)) with
+// t = 1 / (1 + z/2), the form of the Chebyshev erfc in Numerical Recipes
+// (section 6.2).  P is a degree-9 polynomial fitted here (weighted least
+// squares, gen_erfc_fit.py) to log(erfcx(z) / t) over t in [0, 1]; its largest
+// error, with the coefficients rounded to fp32, is 1.2e-7.
+//
+// The exponent reaches -z^2 = -x^2/2 (about -18 at x = -6), where its fp32
+// rounding alone would cost about 1e-6 relative.  So it is carried as s + e:
+// x^2 is split exactly by an FMA, and s = -x^2/2 + P comes with its rounding
+// error (Fast2Sum, exact once |x^2/2| >= |P|, which is where it matters).
+// exp(s + e) = 2^(s log2 e) * (1 + e'), where the hardware 2^y takes the
+// rounded product and e' gathers e and the product's error.  Emulated in fp32
+// over every fp16 x, with 2^y off by up to 2 ulp, Phi is within 6e-7
+// relative.
 constexpr float kInvSqrt2 = 0.70710678118654752440f;
-__device__ __forceinline__ float gelu_cdf(float x) { return 0.5f * erfcf(-x * kInvSqrt2); }
+constexpr float kErfcP[10] = {-1.2655122f, 1.0000226f, 0.37412503f,  0.096388236f, -0.18396664f,
+                              0.27135256f, -1.1211007f, 1.473255f, -0.8133247f,  0.1687606f};
+constexpr float kLog2E = 1.442695f, kLog2ELo = 1.925963e-08f, kLn2 = 0.6931472f;
+constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
+struct ErfcParts {
+  float half;   // erfc(|x| / sqrt 2) / 2
+  float p;      // P(t)
+  float ex;     // exp(-x^2/2 + P(t))
+};
+__device__ __forceinline__ ErfcParts erfc_parts(float x) {
+  const float z = __builtin_fabsf(x) * kInvSqrt2;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
+  float p = kErfcP[9];
+#pragma unroll
+  for (int k = 8; k >= 0; --k) p = __builtin_fmaf(p, t, kErfcP[k]);
+  const float hi = x * x;
+  const float lo = __builtin_fmaf(x, x, -hi);
+  const float a = -0.5f * hi;
+  const float s = a + p;
+  const float e = __builtin_fmaf(-0.5f, lo, p - (s - a));
+  const float yh = s * kLog2E;
+  const float yl = __builtin_fmaf(s, kLog2ELo, __builtin_fmaf(s, kLog2E, -yh));
+  const float E = __builtin_amdgcn_exp2f(yh);
+  ErfcParts r;
+  r.ex = __builtin_fmaf(E, __builtin_fmaf(yl, kLn2, e), E);
+  r.half = (0.5f * t) * r.ex;
+  r.p = p;
+  return r;
+}
+__device__ __forceinline__ float gelu_cdf(float x) {
+  const ErfcParts r = erfc_parts(x);
+  return x < 0.0f ? r.half : 1.0f - r.half;
+}
+// Phi(x) and phi(x) = exp(-x^2/2) / sqrt(2 pi) together.  phi reuses the
+// exponential above, exp(-x^2/2) = exp(-x^2/2 + P) * exp(-P); P lies in
+// [-1.27, 0], so exp(-P) needs no extra care (within 7e-7 relative in the
+// same emulation).
+__device__ __forceinline__ void gelu_cdf_pdf(float x, float& cdf, float& pdf) {
+  const ErfcParts r = erfc_parts(x);
+  cdf = x < 0.0f ? r.half : 1.0f - r.half;
+  pdf = (r.ex * __builtin_amdgcn_exp2f(-r.p * kLog2E)) * kInvSqrt2Pi;
+}
 __device__ __forceinline__ float gelu_f32(float x) { return x * gelu_cdf(x); }
 // value * GELU(gate) from fp16 inputs, rounded to nearest even in fp16
 __device__ __forceinline__ _Float16 geglu_f16(_Float16 value, _Float16 gate) {
