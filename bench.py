@@ -18,7 +18,7 @@ search+compress GB/s (4.375 algorithmic bytes per weight element), the GEMM
 kernel's roofline fraction, the per-step flip rates and the CPU oracle
 baseline.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 20] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -193,7 +193,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy context numbers")
