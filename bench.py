@@ -103,7 +103,7 @@ def cpu_baseline(cfg, inp, sample_tokens: int):
         O.flip_count(p, idx)
         forms.append(O.compress(W, idx))
     t_sc = time.perf_counter() - t0
-    Ts = sample_tokens
+    Ts = sample_tokens if 0 < sample_tokens < cfg.tokens else cfg.tokens
     t0 = time.perf_counter()
     (f1, f2) = forms
     d, f = cfg.d, cfg.dff
@@ -118,10 +118,11 @@ def cpu_baseline(cfg, inp, sample_tokens: int):
         "unit": "TFLOP/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": (f"mask search + flip count + compress of W1 and W2 in full (NumPy, single thread, "
-                   f"{t_sc:.1f} s) and the "
-                   f"four float64 GEMMs on the first {Ts} of {cfg.tokens} tokens (BLAS, {blas_threads} threads, "
-                   f"{t_gemm:.1f} s), GEMM time scaled linearly to all tokens; one step of the 1.5B loop"),
+        "sample": (f"one step of the 1.5B loop: mask search + flip count + compress of W1 and W2 in full "
+                   f"(NumPy, single thread, {t_sc:.1f} s) and the four float64 GEMMs "
+                   + (f"on all {cfg.tokens} tokens" if Ts == cfg.tokens else
+                      f"on the first {Ts} of {cfg.tokens} tokens, time scaled linearly to all tokens")
+                   + f" (BLAS, {blas_threads} threads, {t_gemm:.1f} s)"),
         "search_compress_GBps": round(SC_BYTES_PER_ELEM * (inp.w1.size + inp.w2.size) / t_sc / 1e9, 4),
     }
 
@@ -195,7 +196,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens of the oracle's GEMMs in the CPU baseline, scaled to all tokens (0: all of them)")
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy context numbers")
     ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "flip_count", "weight_grad", "geglu",
                                                  "mvue", "copy"],

@@ -219,9 +219,9 @@ int sp24_spmm_fwd(const void* X, const void* vals_row, const uint16_t* meta_row,
  *   T, R, C        as sp24_spmm_fwd, and R a multiple of 32
  *   U         out  fp16 [T, R], the products (for the backward), or NULL
  *   out       out  fp16 [T, R/2]
- * When C is not a multiple of 64 (or an operand exceeds 2 GiB) the library
- * stores U and runs the GEGLU kernel on it; U must then be given, else
- * SP24_ERR_UNSUPPORTED.
+ * When C is not a multiple of 64, C is 4M or more, or an operand exceeds
+ * 2 GiB, the library stores U and runs the GEGLU kernel on it; U must then be
+ * given, else SP24_ERR_UNSUPPORTED.
  * Errors: NULL, SHAPE, ALIGN, TOO_LARGE, UNSUPPORTED, LAUNCH.
  */
 int sp24_spmm_fwd_geglu(const void* X, const void* vals_row, const uint16_t* meta_row,

@@ -619,8 +619,12 @@ hipError_t launch_fast(const uint16_t* A, const uint16_t* vals, const uint16_t* 
 }
 
 bool fast_path(int64_t T, int64_t N, int64_t K) {
-  constexpr int64_t kMaxBuf = (int64_t)1 << 31;   // buffer offsets are 32-bit
-  return K % 64 == 0 && K > 0 && T * K * 2 < kMaxBuf && N * K < kMaxBuf && T * N * 2 < ((int64_t)1 << 40);
+  // Buffer offsets are 32-bit.  A tile computes r * K * 2 for each of its
+  // 256 rows, also rows past T or N (whose loads are out of range), so the
+  // bound is on 256 rows of K, not only on the matrices.
+  constexpr int64_t kMaxBuf = (int64_t)1 << 31;
+  return K % 64 == 0 && K > 0 && K * 512 < kMaxBuf && T * K * 2 < kMaxBuf && N * K < kMaxBuf &&
+         T * N * 2 < ((int64_t)1 << 40);
 }
 
 // The feature rows that fill whole rounds of 256 x 256 tiles on the device,
