@@ -196,7 +196,14 @@ constexpr int kCompressThreads = 256;
 constexpr int kBlocksPerThread = kTB * kTB / kCompressThreads;  // 4
 constexpr int kCompressWaves = kCompressThreads / 64;
 // Each workgroup handles kTilesPerWg tiles (see search_compress_kernel).
-constexpr int kTilesPerWg = 2;
+// One is fastest at the 1.5B shapes (both weights from HBM: 46.2 us against
+// 50.2 us with two; cache-resident: 29.6 us against 34.8 us with two and
+// 38.7 us with three): with about three workgroups resident per
+// CU, later workgroups start as earlier ones finish, so loads, searches and
+// stores of different tiles overlap on each CU.  Smaller 64 x 64 tiles are
+// slower (44-68 us): each workgroup adds its flip count with one same-address
+// atomic, and those serialise.
+constexpr int kTilesPerWg = 1;
 
 // v_perm_b32 byte selector that gathers halves i0 and i1 of a 4-half group
 // held in two dwords (bytes 2*i0, 2*i0+1, 2*i1, 2*i1+1), from the nibble
@@ -393,19 +400,18 @@ __device__ __forceinline__ void write_tile(const TileRef& tr, int tid, const Com
 
 // Workgroup barrier for LDS hand-offs only: this wave's LDS accesses have
 // completed (lgkmcnt(0)) when it arrives.  __syncthreads() would also wait for
-// every outstanding global load and store (vmcnt(0)): tile 0's search would
-// wait for tile 1's loads, and tile 1's staging for tile 0's stores to be
-// acknowledged.  Register results of global loads are waited for where they
-// are used, as usual.  The memory clobber keeps the compiler from moving
+// every outstanding global load and store (vmcnt(0)): with several tiles per
+// workgroup, tile 0's search would wait for tile 1's loads, and tile 1's
+// staging for tile 0's stores to be acknowledged.  Register results of global
+// loads are waited for where they are used, as usual.  The memory clobber keeps the compiler from moving
 // memory accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Each workgroup handles kTilesPerWg tiles.  All of their loads are issued
 // first; tile 0 is searched as soon as its own loads land, and tile k+1 is
-// searched while the global stores of tile k drain, so loading, searching
-// and storing overlap within the workgroup instead of running as three
-// GPU-wide phases.  A job that counts flips gets one atomic add per
-// counter, after the tile's waves have pooled their counts in LDS.
+// searched while the global stores of tile k drain.  A job that counts flips
+// gets one atomic add per counter and workgroup, after the tile's waves have
+// pooled their counts in LDS.
 
 template <bool kSearch>
 __global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(ScJobs jobs) {
