@@ -16,6 +16,8 @@
 // fp32 vector roof.  Each lane
 // handles 8 consecutive hidden units of one token with 16-byte loads and
 // stores; arithmetic is fp32, with results rounded to nearest even in fp16.
+// The token and block of a lane come from multiply-shift divisions by
+// divisors fixed on the host (make_div).
 // Phi and phi come from gelu_cdf / gelu_cdf_pdf (sp24_device.hpp): a fitted
 // erfc with one reciprocal and one exponential, about 35 VALU operations.
 #include <hip/hip_runtime.h>
@@ -40,30 +42,65 @@ __device__ __forceinline__ void st16(uint16_t* p, h8 v) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
 }
 
+// Division by a divisor d fixed for the launch (1 <= d < 2^31), for
+// dividends n < 2^31: floor(n / d) = floor(n * m / 2^(31 + s)) with
+// s = ceil(log2 d) and m = ceil(2^(31 + s) / d) < 2^32 (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994,
+// Theorem 4.2: m d - 2^(31+s) < d <= 2^s).  One 32x32 -> 64-bit multiply and
+// a shift, where a division by a kernel argument costs a float reciprocal
+// sequence of a dozen VALU operations.
+struct DivU31 {
+  uint32_t m;
+  uint32_t shift;   // 31 + s
+};
+DivU31 make_div(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  return {(uint32_t)((((uint64_t)1 << (31 + s)) + d - 1) / d), 31 + s};
+}
+__device__ __forceinline__ uint32_t div_u31(uint32_t n, DivU31 d) {
+  return (uint32_t)(((uint64_t)n * d.m) >> d.shift);
+}
+
 // One lane per vector of 8 hidden units of one token: vector i is token
-// i / (h/8), units 8*(i % (h/8)) ..; Index is uint32_t when the vector count
-// fits, so the divisions stay 32-bit.  Offsets into U and out:
-template <typename Index>
+// i / (h/8), units 8*(i % (h/8)) ..  Offsets into U and out:
 struct Pos {
   int64_t u_val, u_gate, o;
 };
-template <typename Index>
-__device__ __forceinline__ Pos<Index> position(Index i, Index hv, Index group) {
-  const Index t = i / hv, unit = (i - t * hv) * 8;
-  const Index b = unit / group, w = unit - b * group;
-  Pos<Index> p;
-  p.u_val = (int64_t)t * 2 * (int64_t)hv * 8 + (int64_t)(2 * group * b + w);
-  p.u_gate = p.u_val + (int64_t)group;
-  p.o = (int64_t)t * (int64_t)hv * 8 + (int64_t)unit;
+// Index is uint32_t (with the multiply-shift divisions) when the vector count
+// is below 2^31, else uint64_t with plain divisions.
+struct Geom32 {
+  uint32_t hv, group;
+  DivU31 by_hv, by_group;
+};
+struct Geom64 {
+  uint64_t hv, group;
+};
+__device__ __forceinline__ Pos position(uint32_t i, const Geom32& g) {
+  const uint32_t t = div_u31(i, g.by_hv), unit = (i - t * g.hv) * 8;
+  const uint32_t b = div_u31(unit, g.by_group), w = unit - b * g.group;
+  Pos p;
+  p.u_val = (int64_t)t * 2 * (int64_t)g.hv * 8 + (int64_t)(2 * g.group * b + w);
+  p.u_gate = p.u_val + (int64_t)g.group;
+  p.o = (int64_t)t * (int64_t)g.hv * 8 + (int64_t)unit;
+  return p;
+}
+__device__ __forceinline__ Pos position(uint64_t i, const Geom64& g) {
+  const uint64_t t = i / g.hv, unit = (i - t * g.hv) * 8;
+  const uint64_t b = unit / g.group, w = unit - b * g.group;
+  Pos p;
+  p.u_val = (int64_t)t * 2 * (int64_t)g.hv * 8 + (int64_t)(2 * g.group * b + w);
+  p.u_gate = p.u_val + (int64_t)g.group;
+  p.o = (int64_t)t * (int64_t)g.hv * 8 + (int64_t)unit;
   return p;
 }
 
-template <typename Index>
-__global__ __launch_bounds__(kActThreads) void geglu_fwd_kernel(const uint16_t* __restrict__ U, Index n, Index hv,
-                                                               Index group, uint16_t* __restrict__ out) {
+template <typename Index, typename Geom>
+__global__ __launch_bounds__(kActThreads) void geglu_fwd_kernel(const uint16_t* __restrict__ U, Index n, Geom geom,
+                                                               uint16_t* __restrict__ out) {
   const Index i = (Index)blockIdx.x * kActThreads + threadIdx.x;
   if (i >= n) return;
-  const Pos<Index> p = position<Index>(i, hv, group);
+  const Pos p = position(i, geom);
   const h8 v = ld16(U + p.u_val);
   const h8 g = ld16(U + p.u_gate);
   h8 o;
@@ -72,13 +109,13 @@ __global__ __launch_bounds__(kActThreads) void geglu_fwd_kernel(const uint16_t* 
   st16(out + p.o, o);
 }
 
-template <typename Index>
+template <typename Index, typename Geom>
 __global__ __launch_bounds__(kActThreads) void geglu_bwd_kernel(const uint16_t* __restrict__ U,
-                                                               const uint16_t* __restrict__ dout, Index n, Index hv,
-                                                               Index group, uint16_t* __restrict__ dU) {
+                                                               const uint16_t* __restrict__ dout, Index n, Geom geom,
+                                                               uint16_t* __restrict__ dU) {
   const Index i = (Index)blockIdx.x * kActThreads + threadIdx.x;
   if (i >= n) return;
-  const Pos<Index> p = position<Index>(i, hv, group);
+  const Pos p = position(i, geom);
   const h8 v = ld16(U + p.u_val);
   const h8 g = ld16(U + p.u_gate);
   const h8 d = ld16(dout + p.o);
@@ -97,16 +134,25 @@ __global__ __launch_bounds__(kActThreads) void geglu_bwd_kernel(const uint16_t* 
 
 }  // namespace
 
+namespace {
+// 32-bit geometry when every index fits below 2^31: the vector index (lanes
+// past n included, up to the grid's end) and the unit offset below h.
+bool fits31(int64_t n, int64_t h) { return n + kActThreads < ((int64_t)1 << 31) && h < ((int64_t)1 << 31); }
+Geom32 geom32(int64_t h, int64_t group) {
+  return {(uint32_t)(h / 8), (uint32_t)group, make_div((uint32_t)(h / 8)), make_div((uint32_t)group)};
+}
+}  // namespace
+
 hipError_t launch_geglu_fwd(const uint16_t* U, int64_t T, int64_t h, int64_t group, uint16_t* out, hipStream_t s) {
   const int64_t n = T * (h / 8);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + kActThreads - 1) / kActThreads));
-  if (n < ((int64_t)1 << 32) - kActThreads)
-    hipLaunchKernelGGL(geglu_fwd_kernel<uint32_t>, grid, dim3(kActThreads), 0, s, U, (uint32_t)n, (uint32_t)(h / 8),
-                       (uint32_t)group, out);
+  if (fits31(n, h))
+    hipLaunchKernelGGL((geglu_fwd_kernel<uint32_t, Geom32>), grid, dim3(kActThreads), 0, s, U, (uint32_t)n,
+                       geom32(h, group), out);
   else
-    hipLaunchKernelGGL(geglu_fwd_kernel<uint64_t>, grid, dim3(kActThreads), 0, s, U, (uint64_t)n, (uint64_t)(h / 8),
-                       (uint64_t)group, out);
+    hipLaunchKernelGGL((geglu_fwd_kernel<uint64_t, Geom64>), grid, dim3(kActThreads), 0, s, U, (uint64_t)n,
+                       Geom64{(uint64_t)(h / 8), (uint64_t)group}, out);
   return hipGetLastError();
 }
 
@@ -115,12 +161,12 @@ hipError_t launch_geglu_bwd(const uint16_t* U, const uint16_t* dout, int64_t T, 
   const int64_t n = T * (h / 8);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + kActThreads - 1) / kActThreads));
-  if (n < ((int64_t)1 << 32) - kActThreads)
-    hipLaunchKernelGGL(geglu_bwd_kernel<uint32_t>, grid, dim3(kActThreads), 0, s, U, dout, (uint32_t)n,
-                       (uint32_t)(h / 8), (uint32_t)group, dU);
+  if (fits31(n, h))
+    hipLaunchKernelGGL((geglu_bwd_kernel<uint32_t, Geom32>), grid, dim3(kActThreads), 0, s, U, dout, (uint32_t)n,
+                       geom32(h, group), dU);
   else
-    hipLaunchKernelGGL(geglu_bwd_kernel<uint64_t>, grid, dim3(kActThreads), 0, s, U, dout, (uint64_t)n,
-                       (uint64_t)(h / 8), (uint64_t)group, dU);
+    hipLaunchKernelGGL((geglu_bwd_kernel<uint64_t, Geom64>), grid, dim3(kActThreads), 0, s, U, dout, (uint64_t)n,
+                       Geom64{(uint64_t)(h / 8), (uint64_t)group}, dU);
   return hipGetLastError();
 }
 

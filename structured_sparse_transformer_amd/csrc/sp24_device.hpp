@@ -63,17 +63,21 @@ constexpr float kErfcP[10] = {-1.2655122f, 1.0000226f, 0.37412503f,  0.096388236
                               0.27135256f, -1.1211007f, 1.473255f, -0.8133247f,  0.1687606f};
 constexpr float kLog2E = 1.442695f, kLog2ELo = 1.925963e-08f, kLn2 = 0.6931472f;
 constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
+// erfc / 2 = t exp(-z^2 + P(t) - ln 2): the halving rides in the constant
+// term (its fp32 rounding adds at most 6e-8 to the exponent).
+constexpr float kErfcP0Half = kErfcP[0] - kLn2;
 struct ErfcParts {
   float half;   // erfc(|x| / sqrt 2) / 2
-  float p;      // P(t)
-  float ex;     // exp(-x^2/2 + P(t))
+  float p;      // P(t) - ln 2
+  float ex;     // exp(-x^2/2 + P(t) - ln 2)
 };
 __device__ __forceinline__ ErfcParts erfc_parts(float x) {
   const float z = __builtin_fabsf(x) * kInvSqrt2;
   const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
   float p = kErfcP[9];
 #pragma unroll
-  for (int k = 8; k >= 0; --k) p = __builtin_fmaf(p, t, kErfcP[k]);
+  for (int k = 8; k >= 1; --k) p = __builtin_fmaf(p, t, kErfcP[k]);
+  p = __builtin_fmaf(p, t, kErfcP0Half);
   const float hi = x * x;
   const float lo = __builtin_fmaf(x, x, -hi);
   const float a = -0.5f * hi;
@@ -84,7 +88,7 @@ __device__ __forceinline__ ErfcParts erfc_parts(float x) {
   const float E = __builtin_amdgcn_exp2f(yh);
   ErfcParts r;
   r.ex = __builtin_fmaf(E, __builtin_fmaf(yl, kLn2, e), E);
-  r.half = (0.5f * t) * r.ex;
+  r.half = t * r.ex;
   r.p = p;
   return r;
 }
@@ -93,9 +97,9 @@ __device__ __forceinline__ float gelu_cdf(float x) {
   return x < 0.0f ? r.half : 1.0f - r.half;
 }
 // Phi(x) and phi(x) = exp(-x^2/2) / sqrt(2 pi) together.  phi reuses the
-// exponential above, exp(-x^2/2) = exp(-x^2/2 + P) * exp(-P); P lies in
-// [-1.27, 0], so exp(-P) needs no extra care (within 7.5e-7 relative in the
-// same emulation).
+// exponential above, exp(-x^2/2) = ex * exp(-p); p lies in [-1.96, -0.69],
+// so exp(-p) needs no extra care (within 7.5e-7 relative in the same
+// emulation).
 __device__ __forceinline__ void gelu_cdf_pdf(float x, float& cdf, float& pdf) {
   const ErfcParts r = erfc_parts(x);
   cdf = x < 0.0f ? r.half : 1.0f - r.half;

@@ -46,8 +46,9 @@ def model(x, ulps):
     z = (np.abs(x) * k["kInvSqrt2"]).astype(f32)
     t = (1.0 / fma(f32(0.5), z, f32(1)).astype(np.float64)).astype(f32)
     p = np.full_like(t, coef[9])
-    for c in coef[8::-1]:
+    for c in coef[8:0:-1]:
         p = fma(p, t, c)
+    p = fma(p, t, f32(coef[0] - k["kLn2"]))      # the halving folded into the constant term
     hi = (x * x).astype(f32)
     lo = fma(x, x, -hi)
     a = (f32(-0.5) * hi).astype(f32)
@@ -57,7 +58,7 @@ def model(x, ulps):
     yl = fma(s, k["kLog2ELo"], fma(s, k["kLog2E"], -yh))
     E = exp2_hw(yh, ulps)
     ex = fma(E, fma(yl, k["kLn2"], e), E)
-    half = ((f32(0.5) * t).astype(f32) * ex).astype(f32)
+    half = (t * ex).astype(f32)
     cdf = np.where(x < 0, half, (f32(1) - half).astype(f32))
     pdf = ((ex * exp2_hw((-p * k["kLog2E"]).astype(f32), ulps)).astype(f32) * k["kInvSqrt2Pi"]).astype(f32)
     return cdf, pdf
