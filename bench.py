@@ -320,23 +320,24 @@ def main():
     fl_us = e0.elapsed_time(e1) * 1e3 / fl_calls
     fl_bytes = 2 * F1["idx"].numel()
 
+    def timed_ms(fn, reps):
+        """Average ms per call over `reps` back-to-back calls between two events.
+        One untimed call goes first, so the GPU is busy while the timed calls
+        are enqueued and host launch latency stays outside the events."""
+        fn()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
     # next row: GEGLU forward and backward at the FFN width (HBM-bound)
     U, gd = geglu_inputs(torch, dev, cfg)
     g_out, g_dU = torch.empty_like(gd), torch.empty_like(U)
-    sp24.sp24_geglu_fwd(U, GEGLU_GROUP, out=g_out)
-    sp24.sp24_geglu_bwd(U, gd, GEGLU_GROUP, dU=g_dU)
-    torch.cuda.synchronize()
-    gev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    geglu_ms = np.zeros(2)
-    for _ in range(5):
-        gev[0].record()
-        sp24.sp24_geglu_fwd(U, GEGLU_GROUP, out=g_out)
-        gev[1].record()
-        sp24.sp24_geglu_bwd(U, gd, GEGLU_GROUP, dU=g_dU)
-        gev[2].record()
-        torch.cuda.synchronize()
-        geglu_ms += [gev[0].elapsed_time(gev[1]), gev[1].elapsed_time(gev[2])]
-    geglu_ms /= 5
+    geglu_ms = np.array([timed_ms(lambda: sp24.sp24_geglu_fwd(U, GEGLU_GROUP, out=g_out), 10),
+                         timed_ms(lambda: sp24.sp24_geglu_bwd(U, gd, GEGLU_GROUP, dU=g_dU), 10)])
     units = T * f
     geglu_gbps = [6 * units / (geglu_ms[0] * 1e-3) / 1e9, 10 * units / (geglu_ms[1] * 1e-3) / 1e9]
     del U, gd, g_out, g_dU
@@ -352,30 +353,13 @@ def main():
         "fused_storing_U": lambda: sp24.sp24_spmm_fwd_geglu(X, F1["vals_row"], F1["meta_row"], f, d, out=gf, U=Uf),
         "fused_without_U": lambda: sp24.sp24_spmm_fwd_geglu(X, F1["vals_row"], F1["meta_row"], f, d, out=gf),
     }
-    fused_us = {}
-    for name, fn in fused_variants.items():
-        fn()
-        torch.cuda.synchronize()
-        e0f, e1f = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0f.record()
-        for _ in range(5):
-            fn()
-        e1f.record()
-        torch.cuda.synchronize()
-        fused_us[name] = round(e0f.elapsed_time(e1f) / 5 * 1e3, 1)
+    fused_us = {name: round(timed_ms(fn, 5) * 1e3, 1) for name, fn in fused_variants.items()}
     del Uf, gf
 
     # next row: MVUE 2:4 estimate of the output gradient dY1 [T, 4d] (HBM-bound)
     Um = mvue_uniforms(torch, dev, cfg)
     mv_out = sp24.sp24_mvue(dY1, Um)
-    torch.cuda.synchronize()
-    e0m, e1m = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0m.record()
-    for _ in range(10):
-        sp24.sp24_mvue(dY1, Um, out=mv_out)
-    e1m.record()
-    torch.cuda.synchronize()
-    mvue_ms = e0m.elapsed_time(e1m) / 10
+    mvue_ms = timed_ms(lambda: sp24.sp24_mvue(dY1, Um, out=mv_out), 10)
     mvue_gbps = 4.125 * T * f / (mvue_ms * 1e-3) / 1e9
     del Um, mv_out
 
@@ -383,22 +367,8 @@ def main():
     # term (dense fp16 MFMA, fp32 out), timed back to back after the step
     dW1 = torch.empty(f, d, dtype=torch.float32, device=dev)
     dW2 = torch.empty(d, f, dtype=torch.float32, device=dev)
-    wg = lambda: (sp24.sp24_weight_grad(dY1, X, W1s[-1], F1["idx"], DECAY, dW=dW1),  # noqa: E731
-                  sp24.sp24_weight_grad(dY2, H, W2s[-1], F2["idx"], DECAY, dW=dW2))
-    wg()
-    torch.cuda.synchronize()
-    wev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    wg_ms = np.zeros(2)
-    wg_reps = 5
-    for _ in range(wg_reps):
-        wev[0].record()
-        sp24.sp24_weight_grad(dY1, X, W1s[-1], F1["idx"], DECAY, dW=dW1)
-        wev[1].record()
-        sp24.sp24_weight_grad(dY2, H, W2s[-1], F2["idx"], DECAY, dW=dW2)
-        wev[2].record()
-        torch.cuda.synchronize()
-        wg_ms += [wev[0].elapsed_time(wev[1]), wev[1].elapsed_time(wev[2])]
-    wg_ms /= wg_reps
+    wg_ms = np.array([timed_ms(lambda: sp24.sp24_weight_grad(dY1, X, W1s[-1], F1["idx"], DECAY, dW=dW1), 5),
+                      timed_ms(lambda: sp24.sp24_weight_grad(dY2, H, W2s[-1], F2["idx"], DECAY, dW=dW2), 5)])
     wg_flops = 2 * T * f * d
     wg_tflops = [wg_flops / (ms * 1e-3) / 1e12 for ms in wg_ms]
     wg_achieved = wg_flops / (float(np.mean(wg_ms)) * 1e-3) / 1e12

@@ -253,7 +253,7 @@ def test_spmm_tiny(sp):
 
 
 @pytest.mark.parametrize("T,R,C", [(1, 16, 16), (7, 48, 80), (100, 272, 144), (129, 256, 512), (300, 528, 336),
-                                   (256, 64, 4112)])
+                                   (256, 64, 4112), (300, 320, 192)])
 def test_spmm_ragged(sp, T, R, C):
     rng = np.random.default_rng(T * 131 + R * 7 + C)
     W = (rng.standard_normal((R, C)) * 0.02).astype(np.float16)
