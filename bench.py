@@ -242,9 +242,11 @@ def main():
     Y2 = torch.empty(T, d, dtype=torch.float16, device=dev)
     dX2 = torch.empty(T, f, dtype=torch.float16, device=dev)
 
-    def step(s, ev=None, fl=FL):
+    def step(s, ev=None, fl=FL, marks=(0, 1, 2, 3, 4, 5)):
+        # ev[i] is recorded at mark i when i is in `marks`: 0 before the search,
+        # 1 after it, 2..4 between the GEMMs, 5 after the last one
         def mark(i):
-            if ev is not None:
+            if ev is not None and i in marks:
                 ev[i].record()
         mark(0)
         sp24.sp24_search_compress_batch([W1s[s], W2s[s]], outs=[F1, F2], prev=[F1["idx"], F2["idx"]],
@@ -267,22 +269,29 @@ def main():
         step(s)
     torch.cuda.synchronize()
 
-    # timed region: exactly --steps steps, synchronised on both sides
+    # timed region: exactly --steps steps, synchronised on both sides.  Two
+    # events per step (after the search and after the four GEMMs; about 5 us
+    # of the step) time the GEMM launches and the search within this region.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start.record()
-    for s in range(args.warmup, nsteps):
-        step(s)
+    for k, s in enumerate(range(args.warmup, nsteps)):
+        step(s, tev[k], marks=(1, 5))
     end.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - w0) * 1e3
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
     log(f"timed {args.steps} steps: {ms_total:.3f} ms on events, {wall_ms:.3f} ms wall")
+    # search: from the previous step's last GEMM (or the start) to the end of
+    # the search; GEMMs: the four calls of each step
+    sc_ms = float(np.mean([(start if k == 0 else tev[k - 1][5]).elapsed_time(tev[k][1]) for k in range(args.steps)]))
+    gemm_call_ms = float(np.mean([tev[k][1].elapsed_time(tev[k][5]) for k in range(args.steps)])) / 4
 
-    # per-kernel breakdown: the same steps again with events between the
-    # calls, all enqueued before a single synchronisation so that host-side
+    # per-GEMM breakdown: the same steps again with events between every
+    # call, all enqueued before a single synchronisation so that host-side
     # call overhead never sits between two events of an idle GPU
     evs = []
     for s in range(args.warmup, nsteps):
@@ -294,14 +303,14 @@ def main():
     for ev in evs:
         seg += [ev[i].elapsed_time(ev[i + 1]) for i in range(5)]
     seg /= args.steps
-    sc_ms, gemm_ms = seg[0], seg[1:]
+    gemm_ms = seg[1:]
     gemm_shapes = cfg.gemm_shapes()
     sc_bytes = SC_BYTES_PER_ELEM * 2 * d * f
     sc_gbps = sc_bytes / (sc_ms * 1e-3) / 1e9
     gemm_dense_tflops = [2 * Tt * N * K / (ms * 1e-3) / 1e12 for (_, Tt, N, K), ms in zip(gemm_shapes, gemm_ms)]
     # roofline of the GEMM kernel: executed (non-zero) flops T*N*K per launch
     launch_flops = [Tt * N * K for (_, Tt, N, K) in gemm_shapes]
-    avg_launch_ms = float(np.mean(gemm_ms))
+    avg_launch_ms = gemm_call_ms
     achieved = float(np.mean(launch_flops)) / (avg_launch_ms * 1e-3) / 1e12
     traffic = traffic_from_counters()
 
@@ -449,7 +458,11 @@ def main():
                       "standalone_GBps": round(fl_bytes / (fl_us * 1e-6) / 1e9, 1)},
         "gemm_TFLOPs_dense_equiv": {n: round(v, 1) for (n, *_), v in zip(gemm_shapes, gemm_dense_tflops)},
         "gemm_us": {n: round(ms * 1e3, 1) for (n, *_), ms in zip(gemm_shapes, gemm_ms)},
+        "gemm_breakdown_note": "gemm_us and gemm_TFLOPs_dense_equiv come from a second pass of the same steps with "
+                               "events between every call; roofline and search_compress from events in the timed "
+                               "region (after each search and after each step's four GEMMs)",
         "roofline": {"kernel": "spmm_nt (one sp24_spmm_* call)", "bound": "mfma", "achieved": round(achieved, 1),
+                     "launch_us": round(avg_launch_ms * 1e3, 1),
                      "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic,
                      "note": "executed non-zero flops T*N*K per launch (half the dense-equivalent 2*T*N*K) over the "
