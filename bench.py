@@ -113,10 +113,18 @@ def cpu_baseline(cfg, inp, sample_tokens: int):
     O.spmm_bwd_input(inp.dy2[:Ts], f2["vals_col"], f2["meta_col"], d, f)
     t_gemm = time.perf_counter() - t0
     step_s = t_sc + t_gemm * cfg.tokens / Ts
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     return {
         "value": round(cfg.dense_equiv_flops() / step_s / 1e12, 4),
         "unit": "TFLOP/s",
         "cores": int(blas_threads),
+        "cpu_model": cpu_model,
+        "affinity_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": (f"one step of the 1.5B loop: mask search + flip count + compress of W1 and W2 in full "
                    f"(NumPy, single thread, {t_sc:.1f} s) and the four float64 GEMMs "
@@ -316,6 +324,23 @@ def main():
 
     flips = FL[args.warmup:].cpu().numpy().astype(np.float64) / np.array([f * d, d * f], dtype=np.float64)
 
+    # search+compress per weight: single-weight launches over every weight
+    # version of the run (2 x 40 x 20.5 MB, more than L2 and the 256 MB
+    # last-level cache hold), back to back, each counting its flips as in the
+    # step
+    pw_ctr = FLb[0, 1:2]
+    def per_weight_us(Ws, F):
+        sp24.sp24_search_compress_batch([Ws[0]], outs=[F], prev=[F["idx"]], flips=[pw_ctr])
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for Wk in Ws:
+            sp24.sp24_search_compress_batch([Wk], outs=[F], prev=[F["idx"]], flips=[pw_ctr])
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / len(Ws)
+    pw_us = [per_weight_us(W1s, F1), per_weight_us(W2s, F2)]
+    pw_gbps = [SC_BYTES_PER_ELEM * d * f / (us * 1e-6) / 1e9 for us in pw_us]
+
     # the standalone flip count (two index arrays of W1, 640000 blocks each),
     # back-to-back calls: launch-bound at this size
     fl_prev, fl_ctr, fl_calls = torch.roll(F1["idx"], 1, 0).contiguous(), FLb[0, 0:1], 50
@@ -450,6 +475,10 @@ def main():
         "search_compress_GBps": round(sc_gbps, 1),
         "search_compress_frac_hbm": round(sc_gbps / HBM_PEAK_GBPS, 4),
         "search_compress_us_both_weights": round(sc_ms * 1e3, 2),
+        "search_compress_per_weight": {"W1_us": round(pw_us[0], 2), "W2_us": round(pw_us[1], 2),
+                                       "W1_GBps": round(pw_gbps[0], 1), "W2_GBps": round(pw_gbps[1], 1),
+                                       "note": "one launch per weight over all weight versions of the run "
+                                               "(distinct buffers, 4.375 B per element with the flip count)"},
         "flip_rate": {"definition": "mask entries changed since the previous step's search / entries",
                       "w1_mean": float(f"{flips[:, 0].mean():.4g}"), "w2_mean": float(f"{flips[:, 1].mean():.4g}"),
                       "w1_first_last": [float(f"{flips[0, 0]:.4g}"), float(f"{flips[-1, 0]:.4g}")],
