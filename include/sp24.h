@@ -268,7 +268,9 @@ int sp24_weight_grad(const void* dY, const void* X, const void* W, const uint8_t
 /*
  * GEGLU forward [GEGLU]: out[t][j] = value[t][j] * GELU(gate[t][j]), GELU the
  * exact x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), fp32 arithmetic, fp16
- * result rounded to nearest even.
+ * result rounded to nearest even.  Phi is evaluated within 7e-7 relative of
+ * its exact value; gates of +-inf give what x * Phi(x) gives in IEEE
+ * arithmetic (+inf, and NaN for -inf).
  *
  *   U      in   fp16 [T, 2h], the first linear's output.  Its columns come in
  *               blocks of `group` value columns followed by the `group`

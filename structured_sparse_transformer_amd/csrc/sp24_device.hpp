@@ -71,7 +71,12 @@ struct ErfcParts {
   float p;      // P(t) - ln 2
   float ex;     // exp(-x^2/2 + P(t) - ln 2)
 };
-__device__ __forceinline__ ErfcParts erfc_parts(float x) {
+// The argument is clamped to [-64, 64]: beyond it erfc(|x| / sqrt 2) / 2 is
+// 0 in fp32 either way, and x = +-inf would otherwise turn x^2's split into
+// inf - inf.  GELU's final multiply by the unclamped x keeps +inf -> +inf and
+// -inf -> NaN (x Phi(x) = -inf * 0), as in exact arithmetic in IEEE.
+__device__ __forceinline__ ErfcParts erfc_parts(float xin) {
+  const float x = __builtin_amdgcn_fmed3f(xin, -64.0f, 64.0f);
   const float z = __builtin_fabsf(x) * kInvSqrt2;
   const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
   float p = kErfcP[9];

@@ -111,6 +111,30 @@ def test_geglu_every_fp16_gate(sp, value, limit):
     check(dU, O.geglu_bwd(U, d, 16), gate_grad_slack(U, d, 16))
 
 
+def test_geglu_infinite_gates(sp):
+    """Gates of +-inf (an fp16 overflow upstream) give what x * Phi(x) gives in
+    IEEE arithmetic: GELU(+inf) = +inf, GELU(-inf) = -inf * 0 = NaN; and the
+    gate gradient Phi + x phi is NaN at both (inf * 0)."""
+    T, h = 4, 16
+    U = WL.normal_f16(92, 1, (T, 2 * h))
+    U[:, h:] = np.float16(0.5)
+    U[0, h:h + 4] = np.float16(np.inf)
+    U[1, h:h + 4] = np.float16(-np.inf)
+    U[2, h] = np.float16(64.0)
+    U[2, h + 1] = np.float16(-64.0)
+    d = WL.normal_f16(92, 2, (T, h))
+    with np.errstate(invalid="ignore", over="ignore"):
+        want_out = O.geglu_fwd(U, h)
+        want_dU = O.geglu_bwd(U, d, h)
+    got_out = sp.sp24_geglu_fwd(dev(U), h).cpu().numpy().astype(np.float64)
+    got_dU = sp.sp24_geglu_bwd(dev(U), dev(d), h).cpu().numpy().astype(np.float64)
+    for got, want in ((got_out, want_out), (got_dU, want_dU)):
+        assert (np.isnan(got) == np.isnan(want)).all()
+        fin = np.isfinite(want)
+        assert (got[~fin & ~np.isnan(want)] == want[~fin & ~np.isnan(want)]).all()
+        check(got[fin], want[fin])
+
+
 def test_geglu_layout_group_does_not_change_results(sp):
     T, h = 40, 256
     U, d = draw(3, T, h)

@@ -43,6 +43,8 @@ def exp2_hw(y, ulps):
 
 def model(x, ulps):
     coef, k = header_constants()
+    xs = x
+    x = np.clip(x, f32(-64), f32(64)).astype(f32)      # the kernel clamps the erfc argument
     z = (np.abs(x) * k["kInvSqrt2"]).astype(f32)
     t = (1.0 / fma(f32(0.5), z, f32(1)).astype(np.float64)).astype(f32)
     p = np.full_like(t, coef[9])
@@ -59,7 +61,7 @@ def model(x, ulps):
     E = exp2_hw(yh, ulps)
     ex = fma(E, fma(yl, k["kLn2"], e), E)
     half = (t * ex).astype(f32)
-    cdf = np.where(x < 0, half, (f32(1) - half).astype(f32))
+    cdf = np.where(xs < 0, half, (f32(1) - half).astype(f32))
     pdf = ((ex * exp2_hw((-p * k["kLog2E"]).astype(f32), ulps)).astype(f32) * k["kInvSqrt2Pi"]).astype(f32)
     return cdf, pdf
 
