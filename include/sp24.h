@@ -36,7 +36,9 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls enqueue their kernels on that stream and return at once; nothing
  *     is synchronised.  A fault inside a kernel surfaces at the caller's next
- *     synchronisation of that stream.
+ *     synchronisation of that stream.  The stream and every buffer belong to
+ *     the calling thread's current device (hipSetDevice), whose CU count
+ *     picks the tiling.
  *   - Arguments are checked on the host before any HIP call, so every
  *     validation error is returned without touching the device.  A zero-sized
  *     problem (R, C or T equal to 0) is valid, launches nothing and may pass

@@ -2,6 +2,8 @@
 // direct global->LDS loads for gfx950, and the device's CU count.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <cstdint>
 
 namespace sp24 {
@@ -116,17 +118,18 @@ __device__ __forceinline__ _Float16 geglu_f16(_Float16 value, _Float16 gate) {
   return (_Float16)((float)value * gelu_f32((float)gate));
 }
 
-// Number of compute units of the current device (cached per device).
+// Number of compute units of the current device (cached per device; host
+// threads may race to fill an entry, and all of them store the same value).
 inline int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 }  // namespace sp24

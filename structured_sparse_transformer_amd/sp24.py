@@ -91,6 +91,9 @@ def _ptr(t):
         return None
     if not t.is_cuda:
         raise ValueError("tensor must be on the GPU")
+    # the library launches on the current device (and its current stream)
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensor is on {t.device} but the current device is cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
@@ -98,6 +101,8 @@ def _ptr(t):
 
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
+    if s.device.index != torch.cuda.current_device():
+        raise ValueError(f"stream is on {s.device} but the current device is cuda:{torch.cuda.current_device()}")
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -164,9 +169,7 @@ def _flip_counter(f):
         return None
     if f.dtype != torch.int64 or f.numel() != 1:
         raise ValueError("a flip counter is a one-element int64 tensor (or a view of one)")
-    if not f.is_cuda:
-        raise ValueError("tensor must be on the GPU")
-    return f.data_ptr()
+    return _ptr(f).value
 
 
 def sp24_search_compress_batch(Ws, outs=None, want_idx=True, row=True, col=True, prev=None, flips=None,
