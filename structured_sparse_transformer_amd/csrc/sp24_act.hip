@@ -109,11 +109,23 @@ __global__ __launch_bounds__(kActThreads) void geglu_fwd_kernel(const uint16_t* 
   st16(out + p.o, o);
 }
 
+// The backward's two output vectors of a lane sit `group` columns apart, so
+// with groups below 64 columns each store instruction covers only part of
+// every 128-byte line it touches.  Streamed out as such (non-temporal) those
+// partial lines cost a quarter of the kernel's time.  When the group divides
+// 512, a full wave's 64 vectors are 512 consecutive hidden units whose value
+// and gate gradients fill one exclusive 2 KB span of dU, so the wave stages
+// them in LDS and writes the span as two contiguous 1 KB stores.  Otherwise
+// (and for a last, partial wave) each lane stores its own vectors, as
+// ordinary stores that L2 merges into whole lines.
 template <typename Index, typename Geom>
 __global__ __launch_bounds__(kActThreads) void geglu_bwd_kernel(const uint16_t* __restrict__ U,
                                                                const uint16_t* __restrict__ dout, Index n, Geom geom,
-                                                               uint16_t* __restrict__ dU) {
+                                                               uint16_t* __restrict__ dU, bool staged) {
+  __shared__ __align__(16) unsigned char stage[kActThreads / 64][2048];
   const Index i = (Index)blockIdx.x * kActThreads + threadIdx.x;
+  const Index w0 = i - (Index)(threadIdx.x & 63);   // the wave's first vector
+  const bool whole = staged && w0 + 64 <= n;          // uniform across the wave
   if (i >= n) return;
   const Pos p = position(i, geom);
   const h8 v = ld16(U + p.u_val);
@@ -128,8 +140,24 @@ __global__ __launch_bounds__(kActThreads) void geglu_bwd_kernel(const uint16_t* 
     dv[e] = (_Float16)(dy * (x * cdf));
     dg[e] = (_Float16)(dy * (float)v[e] * (cdf + x * pdf));
   }
-  st16(dU + p.u_val, dv);
-  st16(dU + p.u_gate, dg);
+  if (whole) {
+    // vector j covers flattened hidden units 8j .. 8j+7, and a block of
+    // `group` such units occupies 2 * group columns of dU, so the wave's
+    // units [8 w0, 8 w0 + 512) are dU's [16 w0, 16 w0 + 1024)
+    unsigned char* st = stage[threadIdx.x >> 6];
+    const int64_t base = (int64_t)w0 * 16;
+    *reinterpret_cast<h8*>(st + (p.u_val - base) * 2) = dv;
+    *reinterpret_cast<h8*>(st + (p.u_gate - base) * 2) = dg;
+    __builtin_amdgcn_wave_barrier();
+    const int lane = threadIdx.x & 63;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(st + lane * 16);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(st + 1024 + lane * 16);
+    st16(dU + base + lane * 8, __builtin_bit_cast(h8, a));
+    st16(dU + base + 512 + lane * 8, __builtin_bit_cast(h8, b));
+  } else {
+    *reinterpret_cast<u32x4*>(dU + p.u_val) = __builtin_bit_cast(u32x4, dv);
+    *reinterpret_cast<u32x4*>(dU + p.u_gate) = __builtin_bit_cast(u32x4, dg);
+  }
 }
 
 }  // namespace
@@ -161,12 +189,14 @@ hipError_t launch_geglu_bwd(const uint16_t* U, const uint16_t* dout, int64_t T, 
   const int64_t n = T * (h / 8);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + kActThreads - 1) / kActThreads));
+  // groups of 64 columns or more already fill whole lines per instruction
+  const bool staged = group < 64 && 512 % group == 0;
   if (fits31(n, h))
     hipLaunchKernelGGL((geglu_bwd_kernel<uint32_t, Geom32>), grid, dim3(kActThreads), 0, s, U, dout, (uint32_t)n,
-                       geom32(h, group), dU);
+                       geom32(h, group), dU, staged);
   else
     hipLaunchKernelGGL((geglu_bwd_kernel<uint64_t, Geom64>), grid, dim3(kActThreads), 0, s, U, dout, (uint64_t)n,
-                       Geom64{(uint64_t)(h / 8), (uint64_t)group}, dU);
+                       Geom64{(uint64_t)(h / 8), (uint64_t)group}, dU, staged);
   return hipGetLastError();
 }
 

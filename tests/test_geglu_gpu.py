@@ -79,8 +79,11 @@ def draw(seed, T, h):
     return U, d
 
 
+# Groups of 8, 16 and 32 columns stage a whole wave's backward outputs in LDS
+# (64 vectors of 8 units); (40, 256, 8) and (9, 800, 32) have whole waves, and
+# the latter a partial last wave as well, like (33, 6400, 16).
 @pytest.mark.parametrize("T,h,group", [(1, 8, 8), (3, 64, 16), (7, 48, 48), (5, 96, 32), (64, 512, 16),
-                                       (33, 6400, 16), (17, 6400, 6400)])
+                                       (40, 256, 8), (9, 800, 32), (11, 960, 40), (33, 6400, 16), (17, 6400, 6400)])
 def test_geglu_forward_backward(sp, T, h, group):
     U, d = draw(T * 131 + h + group, T, h)
     out = sp.sp24_geglu_fwd(dev(U), group).cpu().numpy()
