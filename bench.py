@@ -406,6 +406,34 @@ def main():
     wg_flops = 2 * T * f * d
     wg_tflops = [wg_flops / (ms * 1e-3) / 1e12 for ms in wg_ms]
     wg_achieved = wg_flops / (float(np.mean(wg_ms)) * 1e-3) / 1e12
+    del dW1, dW2
+
+    # a whole training step of one gated FFN layer through the entry points
+    # (structured_sparse_transformer_amd/ffn.py): W1 (6400 x 1600) read as a
+    # gated layer with h = 3200 and W2 its 1600 x 3200 partner; refresh (both
+    # searches), forward (GEGLU fused into the first GEMM), backward (two
+    # input-gradient GEMMs, two weight gradients, the GEGLU backward)
+    from structured_sparse_transformer_amd.ffn import SparseGegluFFN
+    h = f // 2
+    layer = SparseGegluFFN(W1s[-1], W2s[-1][:, :h].contiguous(), DECAY)
+    layer.refresh()
+    fwd_out = {}
+
+    def layer_fwd():
+        fwd_out["y"], fwd_out["saved"] = layer.forward(X)
+
+    layer_fwd()
+    layer_parts = {
+        "refresh": layer.refresh,
+        "forward": layer_fwd,
+        "backward": lambda: layer.backward(dY2, fwd_out["saved"]),
+    }
+    layer_us = {name: round(timed_ms(fn, 5) * 1e3, 1) for name, fn in layer_parts.items()}
+    layer_ms = timed_ms(lambda: (layer.refresh(), layer_fwd(), layer.backward(dY2, fwd_out["saved"])), 5)
+    # dense-equivalent flops: forward and input-gradient GEMMs (2:4) plus the
+    # dense weight gradients, each 2*T*N*K
+    layer_flops = 3 * (2 * T * f * d + 2 * T * d * h)
+    del layer, fwd_out
     flops_step = cfg.dense_equiv_flops()
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
@@ -514,6 +542,15 @@ def main():
                                "frac": round(geglu_gbps[1] / HBM_PEAK_GBPS, 4),
                                "note": "backward kernel: 10 B per hidden unit and token (read value, gate, dOut; "
                                        "write both gradients); forward moves 6 B"}},
+        "ffn_layer_step": {"definition": "one training step of a gated 2:4 FFN layer (SparseGegluFFN): refresh both "
+                                         "weights' masks and forms, forward with GEGLU fused into the first GEMM, "
+                                         "backward with both input gradients, both weight gradients (masked decay) "
+                                         "and the GEGLU backward",
+                           "shape": {"tokens": T, "d": d, "h": h, "W1": [f, d], "W2": [d, h]},
+                           "ms": round(layer_ms, 4), "us_parts": layer_us,
+                           "TFLOPs_dense_equiv": round(layer_flops / (layer_ms * 1e-3) / 1e12, 1),
+                           "note": "dense-equivalent flops 2*T*N*K of the two forward GEMMs, the two input-gradient "
+                                   "GEMMs and the two weight gradients, over the whole step's time"},
         "mvue": {"definition": "MVUE 2:4 estimate of dY1 [T, 4d] with one caller-supplied uniform per group, "
                             "row-form output (sp24_mvue)",
                  "us": round(mvue_ms * 1e3, 1), "GBps": round(mvue_gbps, 1),
