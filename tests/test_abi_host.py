@@ -233,3 +233,15 @@ def test_spmm_fwd_geglu_validation(L):
     assert f(FAKE, FAKE, FAKE, 8, 64, 64, MIS, FAKE, NUL) == 3
     assert f(FAKE, FAKE, FAKE, 8, 64, 64, NUL, MIS, NUL) == 3
     assert f(NUL, NUL, NUL, 0, 64, 64, NUL, NUL, NUL) == 0
+
+
+def test_ffn_layer_rejects_bad_shapes():
+    """SparseGegluFFN checks its weights' shapes before any device work."""
+    torch = pytest.importorskip("torch")
+    from structured_sparse_transformer_amd.ffn import SparseGegluFFN
+    w1 = torch.zeros(64, 32, dtype=torch.float16)
+    SparseGegluFFN(w1, torch.zeros(32, 32, dtype=torch.float16))    # [2h, d] and [d, h], 2h = 64
+    with pytest.raises(ValueError):
+        SparseGegluFFN(w1, torch.zeros(32, 64, dtype=torch.float16))   # W2 must be [d, h]
+    with pytest.raises(ValueError):
+        SparseGegluFFN(torch.zeros(48, 32, dtype=torch.float16), torch.zeros(32, 24, dtype=torch.float16))
