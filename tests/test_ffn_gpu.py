@@ -73,3 +73,70 @@ def test_gated_ffn_step_matches_the_oracle(T, d, h):
     want_flips = [O.flip_count(O.mask_search(W1), O.mask_search(W1n)),
                   O.flip_count(O.mask_search(W2), O.mask_search(W2n))]
     assert layer.flips.cpu().tolist() == want_flips
+
+
+def test_gated_ffn_step_full_size_sampled():
+    """The layer step at the size the bench times it (16384 tokens, W1 6400 x 1600
+    read as h = 3200, W2 1600 x 3200), checked on samples the oracle computes
+    cheaply: 32 token rows of Y and dX, and 8 x 8 entries of each weight
+    gradient, from whole columns of U, Hg, dHg and dU over all tokens."""
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    from structured_sparse_transformer_amd.ffn import SparseGegluFFN
+    T, d, h, decay, seed = 16384, 1600, 3200, 2e-4, 4242
+    W1 = WL.normal_f16(seed, 1, (2 * h, d), 0.02)
+    W2 = WL.normal_f16(seed, 2, (d, h), 0.02)
+    X = WL.normal_f16(seed, 3, (T, d))
+    dY = WL.normal_f16(seed, 4, (T, d))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    layer = SparseGegluFFN(dev(W1), dev(W2), decay=decay)
+    layer.refresh()
+    Y, saved = layer.forward(dev(X))
+    dX, dW1, dW2 = layer.backward(dev(dY), saved)
+    torch.cuda.synchronize()
+
+    i1, i2 = O.mask_search(W1), O.mask_search(W2)
+    c1, c2 = O.compress(W1, i1), O.compress(W2, i2)
+    rng = np.random.default_rng(seed)
+    toks = np.sort(rng.choice(T, 32, replace=False))
+    units = np.sort(rng.choice(h, 8, replace=False))       # hidden units (columns of Hg, W2)
+    feats = np.sort(rng.choice(d, 8, replace=False))       # model features (columns of X, rows of W2)
+
+    def unit_cols(u):
+        # U columns of hidden unit u in blocks of 16 values then 16 gates: (value, gate)
+        v = 32 * (u // 16) + u % 16
+        return v, v + 16
+
+    # token rows: the oracle composition on 32 rows
+    U_s = f16(O.spmm_fwd(X[toks], c1["vals_row"], c1["meta_row"], 2 * h, d))
+    Hg_s = f16(O.geglu_fwd(U_s, 16))
+    Y_s = O.spmm_fwd(Hg_s, c2["vals_row"], c2["meta_row"], d, h)
+    dHg_s = f16(O.spmm_bwd_input(dY[toks], c2["vals_col"], c2["meta_col"], d, h))
+    dU_s = f16(O.geglu_bwd(U_s, dHg_s, 16))
+    dX_s = O.spmm_bwd_input(dU_s, c1["vals_col"], c1["meta_col"], 2 * h, d)
+
+    # whole columns for the sampled units: U's value and gate columns (rows of
+    # the row form of W1), Hg, dHg (rows of the column form of W2) and dU
+    Hg_u, dU_u, urows = [], [], []
+    for u in units:
+        vg = np.array(unit_cols(u))
+        U_vg = f16(O.spmm_fwd(X, c1["vals_row"][vg], c1["meta_row"][vg], 2, d))
+        Hg_u.append(f16(O.geglu_fwd(U_vg, 1))[:, 0])
+        dHg_u = f16(O.spmm_bwd_input(dY, c2["vals_col"][[u]], c2["meta_col"][[u]], d, 1))
+        dU_u.append(f16(O.geglu_bwd(U_vg, dHg_u, 1)))          # [T, 2]: d value, d gate
+        urows.extend(vg)
+    Hg_u = np.stack(Hg_u, axis=1)
+    dU_u = np.concatenate(dU_u, axis=1)
+    urows = np.array(urows)
+    # decay terms of both weights, from the oracle with no tokens
+    dec1 = O.weight_grad(np.zeros((0, 2 * h), np.float16), np.zeros((0, d), np.float16), W1, i1, decay)
+    dec2 = O.weight_grad(np.zeros((0, d), np.float16), np.zeros((0, h), np.float16), W2, i2, decay)
+    dW2_s = O.weight_grad(dY[:, feats], Hg_u, None, None, 0.0) + dec2[np.ix_(feats, units)]
+    dW1_s = O.weight_grad(dU_u, X[:, feats], None, None, 0.0) + dec1[np.ix_(urows, feats)]
+
+    got = {"Y": Y[toks].float().cpu().numpy(), "dX": dX[toks].float().cpu().numpy(),
+           "dW1": dW1.cpu().numpy()[np.ix_(urows, feats)], "dW2": dW2.cpu().numpy()[np.ix_(feats, units)]}
+    want = {"Y": Y_s, "dX": dX_s, "dW1": dW1_s, "dW2": dW2_s}
+    for k in want:
+        g = got[k].astype(np.float64)
+        err = np.abs(g - want[k]).max() / np.abs(want[k]).max()
+        assert err <= MAX_REL, (k, err)
