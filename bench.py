@@ -148,6 +148,18 @@ def profile_only(args, sp24, torch, dev, cfg, F1, F2, FL, W1s, W2s, X, dY1, H, d
         torch.cuda.synchronize()
         log(f"copy: {n} x 512 MiB")
         return
+    if args.profile_kernel == "ffn_layer":
+        # the gated FFN layer step of the ffn_layer_step object, alone
+        from structured_sparse_transformer_amd.ffn import SparseGegluFFN
+        layer = SparseGegluFFN(W1s[0], W2s[0][:, :f // 2].contiguous(), DECAY)
+        layer.refresh()
+        for _ in range(args.warmup + n):    # the clocks ramp over the first steps
+            layer.refresh()
+            _, saved = layer.forward(X)
+            layer.backward(dY2, saved)
+        torch.cuda.synchronize()
+        log(f"ffn_layer: {args.warmup} + {n} steps")
+        return
     if args.profile_kernel == "mvue":
         Um = mvue_uniforms(torch, dev, cfg)
         for _ in range(n):
@@ -207,7 +219,9 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the oracle's GEMMs in the CPU baseline, scaled to all tokens (0: all of them)")
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy context numbers")
-    ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "flip_count", "weight_grad", "geglu",
+    ap.add_argument("--no-layer-step", action="store_true",
+                    help="skip the gated FFN layer step (its GEMMs have other shapes than the step's)")
+    ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "flip_count", "weight_grad", "geglu", "ffn_layer",
                                                  "mvue", "copy"],
                     help="run only this kernel --steps times (for rocprofv3 counter passes); prints no JSON")
     args = ap.parse_args()
@@ -413,27 +427,38 @@ def main():
     # gated layer with h = 3200 and W2 its 1600 x 3200 partner; refresh (both
     # searches), forward (GEGLU fused into the first GEMM), backward (two
     # input-gradient GEMMs, two weight gradients, the GEGLU backward)
-    from structured_sparse_transformer_amd.ffn import SparseGegluFFN
     h = f // 2
-    layer = SparseGegluFFN(W1s[-1], W2s[-1][:, :h].contiguous(), DECAY)
-    layer.refresh()
-    fwd_out = {}
+    layer_obj = None
+    if not args.no_layer_step:
+        from structured_sparse_transformer_amd.ffn import SparseGegluFFN
+        layer = SparseGegluFFN(W1s[-1], W2s[-1][:, :h].contiguous(), DECAY)
+        layer.refresh()
+        fwd_out = {}
 
-    def layer_fwd():
-        fwd_out["y"], fwd_out["saved"] = layer.forward(X)
+        def layer_fwd():
+            fwd_out["y"], fwd_out["saved"] = layer.forward(X)
 
-    layer_fwd()
-    layer_parts = {
-        "refresh": layer.refresh,
-        "forward": layer_fwd,
-        "backward": lambda: layer.backward(dY2, fwd_out["saved"]),
-    }
-    layer_us = {name: round(timed_ms(fn, 5) * 1e3, 1) for name, fn in layer_parts.items()}
-    layer_ms = timed_ms(lambda: (layer.refresh(), layer_fwd(), layer.backward(dY2, fwd_out["saved"])), 5)
-    # dense-equivalent flops: forward and input-gradient GEMMs (2:4) plus the
-    # dense weight gradients, each 2*T*N*K
-    layer_flops = 3 * (2 * T * f * d + 2 * T * d * h)
-    del layer, fwd_out
+        layer_fwd()
+        layer_parts = {
+            "refresh": layer.refresh,
+            "forward": layer_fwd,
+            "backward": lambda: layer.backward(dY2, fwd_out["saved"]),
+        }
+        layer_us = {name: round(timed_ms(fn, 5) * 1e3, 1) for name, fn in layer_parts.items()}
+        layer_ms = timed_ms(lambda: (layer.refresh(), layer_fwd(), layer.backward(dY2, fwd_out["saved"])), 5)
+        # dense-equivalent flops: forward and input-gradient GEMMs (2:4) plus
+        # the dense weight gradients, each 2*T*N*K
+        layer_flops = 3 * (2 * T * f * d + 2 * T * d * h)
+        del layer, fwd_out
+        layer_obj = {"definition": "one training step of a gated 2:4 FFN layer (SparseGegluFFN): refresh both "
+                                   "weights' masks and forms, forward with GEGLU fused into the first GEMM, "
+                                   "backward with both input gradients, both weight gradients (masked decay) "
+                                   "and the GEGLU backward",
+                     "shape": {"tokens": T, "d": d, "h": h, "W1": [f, d], "W2": [d, h]},
+                     "ms": round(layer_ms, 4), "us_parts": layer_us,
+                     "TFLOPs_dense_equiv": round(layer_flops / (layer_ms * 1e-3) / 1e12, 1),
+                     "note": "dense-equivalent flops 2*T*N*K of the two forward GEMMs, the two input-gradient "
+                             "GEMMs and the two weight gradients, over the whole step's time"}
     flops_step = cfg.dense_equiv_flops()
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
@@ -542,15 +567,7 @@ def main():
                                "frac": round(geglu_gbps[1] / HBM_PEAK_GBPS, 4),
                                "note": "backward kernel: 10 B per hidden unit and token (read value, gate, dOut; "
                                        "write both gradients); forward moves 6 B"}},
-        "ffn_layer_step": {"definition": "one training step of a gated 2:4 FFN layer (SparseGegluFFN): refresh both "
-                                         "weights' masks and forms, forward with GEGLU fused into the first GEMM, "
-                                         "backward with both input gradients, both weight gradients (masked decay) "
-                                         "and the GEGLU backward",
-                           "shape": {"tokens": T, "d": d, "h": h, "W1": [f, d], "W2": [d, h]},
-                           "ms": round(layer_ms, 4), "us_parts": layer_us,
-                           "TFLOPs_dense_equiv": round(layer_flops / (layer_ms * 1e-3) / 1e12, 1),
-                           "note": "dense-equivalent flops 2*T*N*K of the two forward GEMMs, the two input-gradient "
-                                   "GEMMs and the two weight gradients, over the whole step's time"},
+        "ffn_layer_step": layer_obj,
         "mvue": {"definition": "MVUE 2:4 estimate of dY1 [T, 4d] with one caller-supplied uniform per group, "
                             "row-form output (sp24_mvue)",
                  "us": round(mvue_ms * 1e3, 1), "GBps": round(mvue_gbps, 1),
