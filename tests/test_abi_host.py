@@ -245,3 +245,13 @@ def test_ffn_layer_rejects_bad_shapes():
         SparseGegluFFN(w1, torch.zeros(32, 64, dtype=torch.float16))   # W2 must be [d, h]
     with pytest.raises(ValueError):
         SparseGegluFFN(torch.zeros(48, 32, dtype=torch.float16), torch.zeros(32, 24, dtype=torch.float16))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 ends with a message before any GPU work."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
