@@ -591,6 +591,10 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
           *reinterpret_cast<uint2*>(stage_base + t * 128 + ((chunk ^ (t & 7)) * 16) + 8 * g) =
               make_uint2(h2(o[0], o[1]), h2(o[2], o[3]));
         }
+        // one 32 x 32 block at a time: keeping the GELU temporaries of
+        // different blocks apart cut the epilogue's register spills (132 -> 96
+        // bytes per lane) and 2-4 us per 6400 x 1600 call, same outputs
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll 4
     for (int it = 0; it < WN * 8 / 64; ++it) {
