@@ -305,6 +305,29 @@ def check_full_gemm(out_dev, A, vals, meta, R, C, fwd: bool, seed: int):
     return mr, ma
 
 
+@pytest.mark.parametrize("N", [1152, 1280])
+def test_spmm_tail_split_ragged_tokens(sp, N):
+    """Feature counts whose last 256-wide strip leaves a partial round on 256
+    CUs run that strip as smaller tiles: 256 x 64 when 128 features remain
+    (N = 1152), 128 x 128 when 256 remain (N = 1280).  A ragged token count
+    (16347, not a multiple of 64) puts rows past T into the last tiles of both
+    launches; both products, all tokens' column sums and sampled rows checked."""
+    T, K = 16347, 128
+    W = WL.normal_f16(N + 7, 1, (N, K), 0.02)
+    X = WL.normal_f16(N + 7, 2, (T, K))
+    dY = WL.normal_f16(N + 7, 3, (T, N))
+    o = sp.sp24_search_compress(dev(W))
+    c = O.compress(W, O.mask_search(W))
+    Y = sp.sp24_spmm_fwd(dev(X), o["vals_row"], o["meta_row"], N, K)
+    dX = sp.sp24_spmm_bwd_input(dev(dY), o["vals_col"], o["meta_col"], N, K)
+    check_full_gemm(Y, X, c["vals_row"], c["meta_row"], N, K, True, N)
+    check_full_gemm(dX, dY, c["vals_col"], c["meta_col"], N, K, False, N + 1)
+    # the last rows of the last token tile, where the launches stop
+    tail = torch.arange(T - 40, T, device="cuda")
+    want = O.spmm_fwd(X[T - 40:], c["vals_row"], c["meta_row"], N, K)
+    check_gemm(host(Y[tail]), want)
+
+
 @pytest.mark.parametrize("cfg", [WL.GPT2_355M, WL.GPT2_774M, WL.GPT2_1P5B], ids=lambda c: c.name)
 def test_ffn_layer_configs(sp, cfg):
     inp = WL.ffn_inputs(cfg)
