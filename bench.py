@@ -459,6 +459,41 @@ def main():
                      "TFLOPs_dense_equiv": round(layer_flops / (layer_ms * 1e-3) / 1e12, 1),
                      "note": "dense-equivalent flops 2*T*N*K of the two forward GEMMs, the two input-gradient "
                              "GEMMs and the two weight gradients, over the whole step's time"}
+    # the other GPT-2 FFN shapes of the same path (355M, 774M), timed warm:
+    # one search+compress launch for both weights (no flip count) and each of
+    # the four sparse GEMMs, on device-generated N(0,1) activations and
+    # N(0, 0.02) weights
+    other = {}
+    for oc in (WL.GPT2_355M, WL.GPT2_774M):
+        og = torch.Generator(device=dev)
+        og.manual_seed(oc.seed)
+        od, of, oT = oc.d, oc.dff, oc.tokens
+        rnd = lambda *shape, sd=1.0: (torch.randn(*shape, generator=og, device=dev) * sd).half()  # noqa: E731
+        Wa, Wb = rnd(of, od, sd=0.02), rnd(od, of, sd=0.02)
+        Xa, Ha, dYa, dYb = rnd(oT, od), rnd(oT, of), rnd(oT, of), rnd(oT, od)
+        Fo = sp24.sp24_search_compress_batch([Wa, Wb])
+        sc_o = timed_ms(lambda: sp24.sp24_search_compress_batch([Wa, Wb], outs=Fo), 10)
+        Ya, dXa = torch.empty(oT, of, dtype=torch.float16, device=dev), torch.empty(oT, od, dtype=torch.float16, device=dev)
+        Yb, dXb = torch.empty(oT, od, dtype=torch.float16, device=dev), torch.empty(oT, of, dtype=torch.float16, device=dev)
+        fa, fb = Fo
+        calls = {
+            "fwd1": lambda: sp24.sp24_spmm_fwd(Xa, fa["vals_row"], fa["meta_row"], of, od, Y=Ya),
+            "bwd1": lambda: sp24.sp24_spmm_bwd_input(dYa, fa["vals_col"], fa["meta_col"], of, od, dX=dXa),
+            "fwd2": lambda: sp24.sp24_spmm_fwd(Ha, fb["vals_row"], fb["meta_row"], od, of, Y=Yb),
+            "bwd2": lambda: sp24.sp24_spmm_bwd_input(dYb, fb["vals_col"], fb["meta_col"], od, of, dX=dXb),
+        }
+        g_ms = {name: timed_ms(fn, 5) for name, fn in calls.items()}
+        g_flops = {name: 2 * t * n * k for name, t, n, k in oc.gemm_shapes()}
+        executed = sum(g_flops.values()) / 2 / (sum(g_ms.values()) * 1e-3) / 1e12
+        other[oc.name] = {
+            "d": od, "d_ff": of, "tokens": oT,
+            "search_compress_us_both_weights": round(sc_o * 1e3, 1),
+            "search_compress_GBps": round(4.3125 * 2 * of * od / (sc_o * 1e-3) / 1e9, 1),
+            "gemm_us": {k: round(v * 1e3, 1) for k, v in g_ms.items()},
+            "gemm_TFLOPs_dense_equiv": {k: round(g_flops[k] / (g_ms[k] * 1e-3) / 1e12, 1) for k in g_ms},
+            "gemm_frac_of_dense_mfma_peak": round(executed / FP16_MFMA_PEAK_TFLOPS, 4),
+        }
+        del Wa, Wb, Xa, Ha, dYa, dYb, Fo, fa, fb, Ya, dXa, Yb, dXb, calls
     flops_step = cfg.dense_equiv_flops()
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
@@ -568,6 +603,10 @@ def main():
                                "note": "backward kernel: 10 B per hidden unit and token (read value, gate, dOut; "
                                        "write both gradients); forward moves 6 B"}},
         "ffn_layer_step": layer_obj,
+        "other_configs": {"definition": "the same path at the other GPT-2 FFN shapes, timed warm outside the step: "
+                                        "one search+compress launch for both weights (4.3125 B per element, no flip "
+                                        "count) and each sparse GEMM; executed flops over the dense fp16 MFMA peak",
+                          **other},
         "mvue": {"definition": "MVUE 2:4 estimate of dY1 [T, 4d] with one caller-supplied uniform per group, "
                             "row-form output (sp24_mvue)",
                  "us": round(mvue_ms * 1e3, 1), "GBps": round(mvue_gbps, 1),
