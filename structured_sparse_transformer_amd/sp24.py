@@ -114,6 +114,24 @@ def _out(t, shape, dtype, device):
     return t
 
 
+def _need(t, shape, dtype, name):
+    """An input tensor the library reads through a plain pointer: its shape and
+    dtype must be exactly what the sizes passed alongside it imply, or the
+    kernels would read past its end."""
+    if t is None or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        got = "None" if t is None else f"{t.dtype} {tuple(t.shape)}"
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {got}")
+    return t
+
+
+def _row_form(vals, meta, R, C, name):
+    """The 2:4 form of an [R, C] matrix: vals fp16 [R, C/2], meta int16 [R, C/16]."""
+    if R % 16 or C % 16:
+        raise ValueError(f"{name}: both dimensions must be multiples of 16, got {R} x {C}")
+    _need(vals, (R, C // 2), torch.float16, f"{name} values")
+    _need(meta, (R, C // 16), torch.int16, f"{name} metadata")
+
+
 def _w(W):
     if W.dtype != torch.float16 or W.dim() != 2:
         raise ValueError("W must be a 2-D float16 tensor")
@@ -142,8 +160,7 @@ def _forms(R, C, device, row, col, out):
 def sp24_compress(W, idx, row=True, col=True, out=None, stream=None):
     """Row and/or column 2:4 forms of W pruned by the masks ``idx``."""
     R, C = _w(W)
-    if idx.dtype != torch.uint8:
-        raise ValueError("idx must be uint8")
+    _need(idx, (R // 4, C // 4), torch.uint8, "idx")
     o = _forms(R, C, W.device, row, col, out)
     _check("sp24_compress", lib().sp24_compress(
         _ptr(W), _ptr(idx), R, C, _ptr(o.get("vals_row")), _ptr(o.get("meta_row")),
@@ -196,7 +213,7 @@ def sp24_search_compress_batch(Ws, outs=None, want_idx=True, row=True, col=True,
             o["idx"] = _out(o.get("idx"), (R // 4, C // 4), torch.uint8, W.device)
         ptr = lambda t: _ptr(t).value if t is not None and t.numel() else None  # noqa: E731
         if prev[k] is not None:
-            _out(prev[k], (R // 4, C // 4), torch.uint8, W.device)
+            _need(prev[k], (R // 4, C // 4), torch.uint8, "prev")
         jobs[k] = ScJob(ptr(W), R, C, ptr(o.get("idx")), ptr(o.get("vals_row")), ptr(o.get("meta_row")),
                         ptr(o.get("vals_col")), ptr(o.get("meta_col")), ptr(prev[k]), _flip_counter(flips[k]))
         res.append(o)
@@ -221,12 +238,12 @@ def sp24_weight_grad(dY, X, W=None, idx=None, decay=0.0, dW=None, stream=None):
     """dW[R, C] (float32) = dY^T X + decay * (1 - M) * W, M the masks ``idx``."""
     T, R = dY.shape
     C = X.shape[1]
-    if dY.dtype != torch.float16 or X.dtype != torch.float16 or X.shape[0] != T:
+    if dY.dtype != torch.float16 or X.dtype != torch.float16 or X.dim() != 2 or X.shape[0] != T:
         raise ValueError("dY and X must be float16 [T, R] and [T, C]")
-    if W is not None and (W.dtype != torch.float16 or tuple(W.shape) != (R, C)):
-        raise ValueError("W must be float16 [R, C]")
-    if idx is not None and (idx.dtype != torch.uint8 or tuple(idx.shape) != (R // 4, C // 4)):
-        raise ValueError("idx must be uint8 [R/4, C/4]")
+    if W is not None:
+        _need(W, (R, C), torch.float16, "W")
+    if idx is not None:
+        _need(idx, (R // 4, C // 4), torch.uint8, "idx")
     dW = _out(dW, (R, C), torch.float32, dY.device)
     _check("sp24_weight_grad", lib().sp24_weight_grad(_ptr(dY), _ptr(X), _ptr(W), _ptr(idx), float(decay), T, R, C,
                                                       _ptr(dW), _stream(stream)))
@@ -282,6 +299,7 @@ def sp24_spmm_fwd(X, vals_row, meta_row, R, C, Y=None, stream=None):
     T = X.shape[0]
     if X.dtype != torch.float16 or tuple(X.shape) != (T, C):
         raise ValueError("X must be float16 [T, C]")
+    _row_form(vals_row, meta_row, R, C, "the row form")
     Y = _out(Y, (T, R), torch.float16, X.device)
     _check("sp24_spmm_fwd", lib().sp24_spmm_fwd(_ptr(X), _ptr(vals_row), _ptr(meta_row), T, R, C,
                                                 _ptr(Y), _stream(stream)))
@@ -295,6 +313,7 @@ def sp24_spmm_fwd_geglu(X, vals_row, meta_row, R, C, out=None, U=False, stream=N
     T = X.shape[0]
     if X.dtype != torch.float16 or tuple(X.shape) != (T, C):
         raise ValueError("X must be float16 [T, C]")
+    _row_form(vals_row, meta_row, R, C, "the row form")
     out = _out(out, (T, R // 2), torch.float16, X.device)
     if U is True:
         U = torch.empty(T, R, dtype=torch.float16, device=X.device)
@@ -312,6 +331,7 @@ def sp24_spmm_bwd_input(dY, vals_col, meta_col, R, C, dX=None, stream=None):
     T = dY.shape[0]
     if dY.dtype != torch.float16 or tuple(dY.shape) != (T, R):
         raise ValueError("dY must be float16 [T, R]")
+    _row_form(vals_col, meta_col, C, R, "the column form")
     dX = _out(dX, (T, C), torch.float16, dY.device)
     _check("sp24_spmm_bwd_input", lib().sp24_spmm_bwd_input(_ptr(dY), _ptr(vals_col), _ptr(meta_col), T, R, C,
                                                             _ptr(dX), _stream(stream)))

@@ -255,3 +255,38 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_binding_checks_operand_shapes_before_any_pointer():
+    """The C ABI takes plain pointers, so the binding must refuse an operand
+    whose shape or dtype disagrees with the sizes passed beside it: the
+    kernels would otherwise read past its end.  The checks run before any
+    pointer is taken, so CPU tensors are enough to exercise them."""
+    torch = pytest.importorskip("torch")
+    from structured_sparse_transformer_amd import sp24 as sp
+    h = lambda *s: torch.zeros(*s, dtype=torch.float16)   # noqa: E731
+    i16 = lambda *s: torch.zeros(*s, dtype=torch.int16)   # noqa: E731
+    u8 = lambda *s: torch.zeros(*s, dtype=torch.uint8)    # noqa: E731
+    R, C, T = 64, 32, 8
+    good = (h(R, C // 2), i16(R, C // 16))
+    bad_forms = [(h(R, C // 2 - 8), good[1]), (good[0], i16(R - 16, C // 16)),
+                 (good[0].float(), good[1]), (good[0], good[1].to(torch.int32)), (None, good[1])]
+    for vals, meta in bad_forms:
+        with pytest.raises(ValueError):
+            sp.sp24_spmm_fwd(h(T, C), vals, meta, R, C)
+        with pytest.raises(ValueError):
+            sp.sp24_spmm_fwd_geglu(h(T, C), vals, meta, R, C)
+    with pytest.raises(ValueError):       # column form of the same weight is [C, R/2]
+        sp.sp24_spmm_bwd_input(h(T, R), h(R, C // 2), i16(R, C // 16), R, C)
+    with pytest.raises(ValueError):       # a dimension that is not a multiple of 16
+        sp.sp24_spmm_fwd(h(T, 40), h(R, 20), i16(R, 2), R, 40)
+    with pytest.raises(ValueError):
+        sp.sp24_compress(h(R, C), u8(R // 4, C // 4 - 1))
+    with pytest.raises(ValueError):
+        sp.sp24_weight_grad(h(T, R), h(T, C), h(R, C), u8(R // 4 + 1, C // 4))
+    with pytest.raises(ValueError):
+        sp.sp24_search_compress_batch([h(R, C)], prev=[u8(R // 4, C // 4 + 4)],
+                                      flips=[torch.zeros(1, dtype=torch.int64)])
+    # well-formed operands get past the checks and stop at the device test
+    with pytest.raises(ValueError, match="on the GPU"):
+        sp.sp24_spmm_fwd(h(T, C), *good, R, C)

@@ -272,6 +272,19 @@ def test_spmm_empty_tokens(sp):
     assert tuple(Y.shape) == (0, 32)
 
 
+def test_spmm_empty_reduction(sp):
+    """A weight with no columns (fwd) or no rows (bwd): every output is an
+    empty sum, +0, and the kernels read no operand."""
+    T, N = 300, 48
+    e = lambda *s, dt=torch.float16: torch.empty(*s, dtype=dt, device="cuda")  # noqa: E731
+    Y = torch.full((T, N), float("nan"), dtype=torch.float16, device="cuda")
+    sp.sp24_spmm_fwd(e(T, 0), e(N, 0), e(N, 0, dt=torch.int16), N, 0, Y=Y)
+    dX = torch.full((T, N), float("nan"), dtype=torch.float16, device="cuda")
+    sp.sp24_spmm_bwd_input(e(T, 0), e(N, 0), e(N, 0, dt=torch.int16), 0, N, dX=dX)
+    for out in (Y, dX):
+        assert (out.view(torch.int16) == 0).all()
+
+
 def test_spmm_exact_small_integers(sp):
     # small integers: every product and sum is exact in fp32 and the results
     # fit fp16 exactly, so the GEMM must match the oracle exactly
