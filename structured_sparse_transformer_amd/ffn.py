@@ -60,15 +60,20 @@ class SparseGegluFFN:
                 [self.W1, self.W2], outs=self.forms, prev=[f["idx"] for f in self.forms],
                 flips=[self.flips[0:1], self.flips[1:2]])
 
+    def _current_forms(self):
+        if self.forms is None:
+            raise RuntimeError("call refresh() first: the layer has no compressed weights yet")
+        return self.forms
+
     def forward(self, X: torch.Tensor):
-        f1, f2 = self.forms
+        f1, f2 = self._current_forms()
         two_h, d = self.W1.shape
         Hg, U = sp24.sp24_spmm_fwd_geglu(X, f1["vals_row"], f1["meta_row"], two_h, d, U=True)
         Y = sp24.sp24_spmm_fwd(Hg, f2["vals_row"], f2["meta_row"], d, two_h // 2)
         return Y, Saved(X, U, Hg)
 
     def backward(self, dY: torch.Tensor, saved: Saved):
-        f1, f2 = self.forms
+        f1, f2 = self._current_forms()
         two_h, d = self.W1.shape
         dHg = sp24.sp24_spmm_bwd_input(dY, f2["vals_col"], f2["meta_col"], d, two_h // 2)
         dW2 = sp24.sp24_weight_grad(dY, saved.Hg, self.W2, f2["idx"], self.decay)

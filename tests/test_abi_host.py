@@ -245,6 +245,9 @@ def test_ffn_layer_rejects_bad_shapes():
         SparseGegluFFN(w1, torch.zeros(32, 64, dtype=torch.float16))   # W2 must be [d, h]
     with pytest.raises(ValueError):
         SparseGegluFFN(torch.zeros(48, 32, dtype=torch.float16), torch.zeros(32, 24, dtype=torch.float16))
+    layer = SparseGegluFFN(w1, torch.zeros(32, 32, dtype=torch.float16))
+    with pytest.raises(RuntimeError, match="refresh"):
+        layer.forward(torch.zeros(8, 32, dtype=torch.float16))
 
 
 def test_bench_refuses_more_than_one_gpu():
