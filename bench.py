@@ -221,6 +221,8 @@ def main():
     ap.add_argument("--no-context", action="store_true", help="skip the dense-matmul and copy context numbers")
     ap.add_argument("--no-layer-step", action="store_true",
                     help="skip the gated FFN layer step (its GEMMs have other shapes than the step's)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the 355M and 774M shapes (their launches would mix into a kernel trace's averages)")
     ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "flip_count", "weight_grad", "geglu", "ffn_layer",
                                                  "mvue", "copy"],
                     help="run only this kernel --steps times (for rocprofv3 counter passes); prints no JSON")
@@ -464,7 +466,7 @@ def main():
     # the four sparse GEMMs, on device-generated N(0,1) activations and
     # N(0, 0.02) weights
     other = {}
-    for oc in (WL.GPT2_355M, WL.GPT2_774M):
+    for oc in () if args.no_other_configs else (WL.GPT2_355M, WL.GPT2_774M):
         og = torch.Generator(device=dev)
         og.manual_seed(oc.seed)
         od, of, oT = oc.d, oc.dff, oc.tokens
@@ -603,10 +605,11 @@ def main():
                                "note": "backward kernel: 10 B per hidden unit and token (read value, gate, dOut; "
                                        "write both gradients); forward moves 6 B"}},
         "ffn_layer_step": layer_obj,
-        "other_configs": {"definition": "the same path at the other GPT-2 FFN shapes, timed warm outside the step: "
-                                        "one search+compress launch for both weights (4.3125 B per element, no flip "
-                                        "count) and each sparse GEMM; executed flops over the dense fp16 MFMA peak",
-                          **other},
+        "other_configs": None if args.no_other_configs else {
+            "definition": "the same path at the other GPT-2 FFN shapes, timed warm outside the step: one "
+                          "search+compress launch for both weights (4.3125 B per element, no flip count) and each "
+                          "sparse GEMM; executed flops over the dense fp16 MFMA peak",
+            **other},
         "mvue": {"definition": "MVUE 2:4 estimate of dY1 [T, 4d] with one caller-supplied uniform per group, "
                             "row-form output (sp24_mvue)",
                  "us": round(mvue_ms * 1e3, 1), "GBps": round(mvue_gbps, 1),

@@ -119,7 +119,10 @@ __device__ __forceinline__ int search_fast(const BlockMag& b, int emin) {
   return 127 - (int)(best & 127u);
 }
 
-__device__ __noinline__ int search_exact_order(const BlockMag& b) {
+// Out of line: only blocks outside the exact regime take it.  The block is
+// passed by value, in registers: a reference would make every caller store
+// the block to scratch memory, taken or not.
+__device__ __noinline__ int search_exact_order(BlockMag b) {
   constexpr const PatternTables& T = kTables;
   float a[16];
 #pragma unroll
