@@ -213,7 +213,10 @@ constexpr int kTilesPerWg = 1;
 // i0 | i1 << 2.  Computed in a few VALU operations rather than looked up:
 // per-lane lookups of a per-pattern table land on a quarter of the LDS banks.
 __device__ __forceinline__ uint32_t pair_selector(uint32_t nib) {
-  return 0x01000100u + (nib & 3u) * 0x0202u + ((nib >> 2) * 0x0202u << 16);
+  // i0 into byte 0 and i1 into byte 2; one 24-bit multiply-add by 0x202 then
+  // doubles each and copies it into the byte above (no carries: i < 4)
+  const uint32_t spread = (nib & 3u) | (nib >> 2) << 16;
+  return spread * 0x0202u + 0x01000100u;
 }
 
 // One 8-byte entry per pattern: x = row nibbles (bits 0..15) | column
@@ -248,6 +251,7 @@ struct CompressSmem {
   uint32_t flips[kTilesPerWg][kCompressWaves];  // per-wave flip counts of each tile
 };
 static_assert(sizeof(PatTable) % 4 == 0, "the pattern table is copied in dwords");
+static_assert(kCompressThreads == 256 && kTile == 128, "write_full_tile: 8 lanes per 128-byte row, 32 rows per pass");
 
 // Tile geometry of one workgroup-tile of one job.  The job is copied by
 // value (selected with static indices), so the kernel-argument table never
@@ -356,8 +360,64 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
   return v;
 }
 
+// Stores of a whole 128 x 128 tile (every tile but those on a weight's ragged
+// edge).  Lane tid writes 16-byte segment tid % 8 of rows (and columns)
+// tid / 8 + 32 k, so its addresses are computed once and then advance by a
+// uniform stride: no per-segment division or 64-bit multiply.
+__device__ __forceinline__ void write_full_tile(const TileRef& tr, int tid, const CompressSmem& sm) {
+  const ScJob& jb = tr.jb;
+  const int64_t R = jb.R, C = jb.C, r0 = tr.r0, c0 = tr.c0;
+  constexpr int kStep = kCompressThreads / 8;   // rows (columns) per pass: 32
+  const int g4 = tid % 8, r = tid / 8;
+  if (jb.idx_out) {
+    // block row r, blocks 4*g4 .. 4*g4+3
+    const uint32_t v = (uint32_t)sm.idx[r][4 * g4] | (uint32_t)sm.idx[r][4 * g4 + 1] << 8 |
+                       (uint32_t)sm.idx[r][4 * g4 + 2] << 16 | (uint32_t)sm.idx[r][4 * g4 + 3] << 24;
+    *reinterpret_cast<uint32_t*>(jb.idx_out + (r0 / 4 + r) * (C / 4) + c0 / 4 + 4 * g4) = v;
+  }
+  if (jb.vals_row) {
+    uint16_t* vp = jb.vals_row + (r0 + r) * (C / 2) + c0 / 2 + 8 * g4;
+    uint16_t* mp = jb.meta_row + (r0 + r) * (C / 16) + c0 / 16 + g4;
+    const int64_t vstep = kStep * (C / 2), mstep = kStep * (C / 16);
+    const int sh = 4 * (r & 3);   // the row within its block (kStep is a multiple of 4)
+#pragma unroll
+    for (int k = 0; k < kTile / kStep; ++k) {
+      const int rr = r + kStep * k;
+      *reinterpret_cast<uint4*>(vp + k * vstep) =
+          make_uint4(sm.vals_row[rr][4 * g4 + 0], sm.vals_row[rr][4 * g4 + 1], sm.vals_row[rr][4 * g4 + 2],
+                     sm.vals_row[rr][4 * g4 + 3]);
+      uint32_t word = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) word |= ((sm.bnibs[rr >> 2][4 * g4 + q] >> sh) & 0xFu) << (4 * q);
+      mp[k * mstep] = (uint16_t)word;
+    }
+  }
+  if (jb.vals_col) {
+    uint16_t* vp = jb.vals_col + (c0 + r) * (R / 2) + r0 / 2 + 8 * g4;
+    uint16_t* mp = jb.meta_col + (c0 + r) * (R / 16) + r0 / 16 + g4;
+    const int64_t vstep = kStep * (R / 2), mstep = kStep * (R / 16);
+    const int sh = 16 + 4 * (r & 3);
+#pragma unroll
+    for (int k = 0; k < kTile / kStep; ++k) {
+      const int c = r + kStep * k;
+      const int cs = col_swz(kStep * k);   // equals col_swz(c), since r < kStep
+      *reinterpret_cast<uint4*>(vp + k * vstep) =
+          make_uint4(sm.vals_col[c][(4 * g4 + 0) ^ cs], sm.vals_col[c][(4 * g4 + 1) ^ cs],
+                     sm.vals_col[c][(4 * g4 + 2) ^ cs], sm.vals_col[c][(4 * g4 + 3) ^ cs]);
+      uint32_t word = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) word |= ((sm.bnibs[4 * g4 + q][c >> 2] >> sh) & 0xFu) << (4 * q);
+      mp[k * mstep] = (uint16_t)word;
+    }
+  }
+}
+
 // Coalesced stores of a staged tile: 16-byte row and column segments.
 __device__ __forceinline__ void write_tile(const TileRef& tr, int tid, const CompressSmem& sm) {
+  if (tr.rows == kTile && tr.cols == kTile) {
+    write_full_tile(tr, tid, sm);
+    return;
+  }
   const ScJob& jb = tr.jb;
   const int64_t R = jb.R, C = jb.C, r0 = tr.r0, c0 = tr.c0;
   const int rows = tr.rows, cols = tr.cols, nbc_t = cols / 4, nbr_t = rows / 4;
