@@ -357,6 +357,24 @@ def main():
     pw_us = [per_weight_us(W1s, F1), per_weight_us(W2s, F2)]
     pw_gbps = [SC_BYTES_PER_ELEM * d * f / (us * 1e-6) / 1e9 for us in pw_us]
 
+    # the step's batched launch (both weights, flips counted) back to back over
+    # every weight version: one pair of events around all of them, so no
+    # event's cost falls on a launch
+    bb_ctr = torch.zeros(2, dtype=torch.int64, device=dev)
+    def both_weights_us():
+        run = lambda a, b: sp24.sp24_search_compress_batch(  # noqa: E731
+            [a, b], outs=[F1, F2], prev=[F1["idx"], F2["idx"]], flips=[bb_ctr[0:1], bb_ctr[1:2]])
+        run(W1s[0], W2s[0])
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for a, b in zip(W1s, W2s):
+            run(a, b)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / len(W1s)
+    bb_us = both_weights_us()
+    bb_gbps = sc_bytes / (bb_us * 1e-6) / 1e9
+
     # the standalone flip count (two index arrays of W1, 640000 blocks each),
     # back-to-back calls: launch-bound at this size
     fl_prev, fl_ctr, fl_calls = torch.roll(F1["idx"], 1, 0).contiguous(), FLb[0, 0:1], 50
@@ -569,6 +587,12 @@ def main():
                                        "W1_GBps": round(pw_gbps[0], 1), "W2_GBps": round(pw_gbps[1], 1),
                                        "note": "one launch per weight over all weight versions of the run "
                                                "(distinct buffers, 4.375 B per element with the flip count)"},
+        "search_compress_back_to_back": {"us_both_weights": round(bb_us, 2), "GBps": round(bb_gbps, 1),
+                                         "frac_hbm": round(bb_gbps / HBM_PEAK_GBPS, 4),
+                                         "note": "the step's batched launch for both weights over all weight "
+                                                 "versions of the run, back to back between one pair of events; "
+                                                 "search_compress_GBps above times each launch inside the step, "
+                                                 "between the step's own events"},
         "flip_rate": {"definition": "mask entries changed since the previous step's search / entries",
                       "w1_mean": float(f"{flips[:, 0].mean():.4g}"), "w2_mean": float(f"{flips[:, 1].mean():.4g}"),
                       "w1_first_last": [float(f"{flips[0, 0]:.4g}"), float(f"{flips[-1, 0]:.4g}")],
