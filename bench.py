@@ -514,6 +514,15 @@ def main():
             "gemm_frac_of_dense_mfma_peak": round(executed / FP16_MFMA_PEAK_TFLOPS, 4),
         }
         del Wa, Wb, Xa, Ha, dYa, dYb, Fo, fa, fb, Ya, dXa, Yb, dXb, calls
+    if not args.no_other_configs:
+        # the 4096 x 4096 stress weight (integer rows, a constant band across
+        # the seam, N(0, 0.02) rows): search and compression only
+        Wst = torch.from_numpy(WL.stress_weight(WL.STRESS_SEED)).to(dev)
+        Fst = sp24.sp24_search_compress_batch([Wst])
+        st_ms = timed_ms(lambda: sp24.sp24_search_compress_batch([Wst], outs=Fst), 10)
+        other["stress-4096"] = {"shape": list(Wst.shape), "search_compress_us": round(st_ms * 1e3, 1),
+                                "search_compress_GBps": round(4.3125 * Wst.numel() / (st_ms * 1e-3) / 1e9, 1)}
+        del Wst, Fst
     flops_step = cfg.dense_equiv_flops()
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
@@ -632,7 +641,8 @@ def main():
         "other_configs": None if args.no_other_configs else {
             "definition": "the same path at the other GPT-2 FFN shapes, timed warm outside the step: one "
                           "search+compress launch for both weights (4.3125 B per element, no flip count) and each "
-                          "sparse GEMM; executed flops over the dense fp16 MFMA peak",
+                          "sparse GEMM; executed flops over the dense fp16 MFMA peak; and search+compress alone "
+                          "on the 4096 x 4096 stress weight",
             **other},
         "mvue": {"definition": "MVUE 2:4 estimate of dY1 [T, 4d] with one caller-supplied uniform per group, "
                             "row-form output (sp24_mvue)",
