@@ -84,35 +84,39 @@ def traffic_from_counters():
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, inp, sample_tokens: int):
-    """The CPU oracle on a bounded sample of one step, scaled to TFLOP/s."""
+def cpu_baseline(cfg, inp, sample_tokens: int, steps: int = 3):
+    """The CPU oracle on a bounded sample of the loop (its first `steps`
+    steps), scaled to TFLOP/s."""
     from oracle import sp24_oracle as O
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         blas_threads = os.cpu_count() or 1
-    # stand-in previous masks (seeded indices): the count's cost does not
-    # depend on their values
-    prev = [WL.random_idx(cfg.seed, 200 + k, (w.shape[0] // 4, w.shape[1] // 4))
-            for k, w in enumerate((inp.w1, inp.w2))]
-    t0 = time.perf_counter()
-    forms = []
-    for W, p in zip((inp.w1, inp.w2), prev):
-        idx = O.mask_search(W)
-        O.flip_count(p, idx)
-        forms.append(O.compress(W, idx))
-    t_sc = time.perf_counter() - t0
+    # the loop's first weight versions and the masks before step 0 (untimed)
+    w1s = [w for _, w in WL.noisy_weights(cfg, inp.w1, 1, steps)]
+    w2s = [w for _, w in WL.noisy_weights(cfg, inp.w2, 2, steps)]
+    prev = [O.mask_search(inp.w1), O.mask_search(inp.w2)]
     Ts = sample_tokens if 0 < sample_tokens < cfg.tokens else cfg.tokens
-    t0 = time.perf_counter()
-    (f1, f2) = forms
     d, f = cfg.d, cfg.dff
-    O.spmm_fwd(inp.x[:Ts], f1["vals_row"], f1["meta_row"], f, d)
-    O.spmm_bwd_input(inp.dy1[:Ts], f1["vals_col"], f1["meta_col"], f, d)
-    O.spmm_fwd(inp.h[:Ts], f2["vals_row"], f2["meta_row"], d, f)
-    O.spmm_bwd_input(inp.dy2[:Ts], f2["vals_col"], f2["meta_col"], d, f)
-    t_gemm = time.perf_counter() - t0
-    step_s = t_sc + t_gemm * cfg.tokens / Ts
+    t_sc = t_gemm = 0.0
+    for s in range(steps):
+        t0 = time.perf_counter()
+        forms = []
+        for k, W in enumerate((w1s[s], w2s[s])):
+            idx = O.mask_search(W)
+            O.flip_count(prev[k], idx)
+            forms.append(O.compress(W, idx))
+            prev[k] = idx
+        t_sc += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        (f1, f2) = forms
+        O.spmm_fwd(inp.x[:Ts], f1["vals_row"], f1["meta_row"], f, d)
+        O.spmm_bwd_input(inp.dy1[:Ts], f1["vals_col"], f1["meta_col"], f, d)
+        O.spmm_fwd(inp.h[:Ts], f2["vals_row"], f2["meta_row"], d, f)
+        O.spmm_bwd_input(inp.dy2[:Ts], f2["vals_col"], f2["meta_col"], d, f)
+        t_gemm += time.perf_counter() - t0
+    step_s = (t_sc + t_gemm * cfg.tokens / Ts) / steps
     cpu_model = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -126,12 +130,12 @@ def cpu_baseline(cfg, inp, sample_tokens: int):
         "cpu_model": cpu_model,
         "affinity_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
-        "sample": (f"one step of the 1.5B loop: mask search + flip count + compress of W1 and W2 in full "
-                   f"(NumPy, single thread, {t_sc:.1f} s) and the four float64 GEMMs "
+        "sample": (f"the first {steps} steps of the 1.5B loop: mask search + flip count + compress of W1 and W2 "
+                   f"in full (NumPy, single thread, {t_sc:.1f} s) and the four float64 GEMMs "
                    + (f"on all {cfg.tokens} tokens" if Ts == cfg.tokens else
                       f"on the first {Ts} of {cfg.tokens} tokens, time scaled linearly to all tokens")
                    + f" (BLAS, {blas_threads} threads, {t_gemm:.1f} s)"),
-        "search_compress_GBps": round(SC_BYTES_PER_ELEM * (inp.w1.size + inp.w2.size) / t_sc / 1e9, 4),
+        "search_compress_GBps": round(SC_BYTES_PER_ELEM * (inp.w1.size + inp.w2.size) * steps / t_sc / 1e9, 4),
     }
 
 
