@@ -26,6 +26,8 @@
 // register prefetch of the next stage.  Rows beyond N or T are clamped on load
 // and not stored; K beyond the end (K is a multiple of 16) is zero-filled.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <cstdint>
 
 #include "sp24_device.hpp"
@@ -228,10 +230,17 @@ hipError_t launch_cfg(const uint16_t* A, const uint16_t* vals, const uint16_t* m
   const int tiles_m = (int)((N + BM - 1) / BM), tiles_n = (int)((T + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
   const int grid = ((ntiles + 7) / 8) * 8;
-  // thread-safe one-time opt-in to more than 64 KiB of dynamic LDS
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&spmm_nt_kernel<BM, BN, WM, WN>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::SMEM);
-  if (attr != hipSuccess) return attr;
+  // opt-in to more than 64 KiB of dynamic LDS, once per device (the
+  // attribute belongs to the current device's copy of the kernel)
+  static std::atomic<bool> attr_set[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev < 0 || dev >= 64 || !attr_set[dev].load(std::memory_order_acquire)) {
+    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&spmm_nt_kernel<BM, BN, WM, WN>),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::SMEM);
+    if (attr != hipSuccess) return attr;
+    if (dev >= 0 && dev < 64) attr_set[dev].store(true, std::memory_order_release);
+  }
   hipLaunchKernelGGL((spmm_nt_kernel<BM, BN, WM, WN>), dim3(grid), dim3(Cfg::THREADS), Cfg::SMEM, s, A, vals, meta, T,
                      N, K, out, tiles_m, tiles_n);
   return hipGetLastError();
