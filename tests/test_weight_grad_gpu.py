@@ -116,7 +116,7 @@ def _sampled_check(got, dY, X, W, idx, decay, seed, n=48):
     assert err <= 1e-4, err
 
 
-@pytest.mark.parametrize("cfg", [WL.GPT2_355M, WL.GPT2_1P5B], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [WL.GPT2_355M, WL.GPT2_774M, WL.GPT2_1P5B], ids=lambda c: c.name)
 def test_weight_grad_ffn_configs(sp, cfg):
     """Both weight gradients of one FFN layer at 16384 tokens: dW1 = dY1^T X
     (shape of W1) and dW2 = dY2^T H (shape of W2), with the decay term."""
