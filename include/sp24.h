@@ -211,8 +211,8 @@ int sp24_spmm_fwd(const void* X, const void* vals_row, const uint16_t* meta_row,
  * 32b .. 32b+15 are the value units 16b .. 16b+15 and rows 32b+16 .. 32b+31
  * their gate units, so U has sp24_geglu_fwd's layout with group 16.  `out`
  * is GEGLU of the fp16 products with the same fp32 GELU code as
- * sp24_geglu_fwd; the two agree to within one fp16 ulp (near rounding ties
- * the device library's erfc may round differently in the two kernels).
+ * sp24_geglu_fwd (the same inlined functions, no fp contraction), so it
+ * equals sp24_geglu_fwd of U bit for bit.
  * Each value meets its gate in the same lane's accumulators, so U need not
  * be stored or read back.
  *
@@ -224,7 +224,8 @@ int sp24_spmm_fwd(const void* X, const void* vals_row, const uint16_t* meta_row,
  * When C is not a multiple of 64, C is 4M or more, or an operand exceeds
  * 2 GiB, the library stores U and runs the GEGLU kernel on it; U must then be
  * given, else SP24_ERR_UNSUPPORTED.
- * Errors: NULL, SHAPE, ALIGN, TOO_LARGE, UNSUPPORTED, LAUNCH.
+ * Errors: NULL, SHAPE, ALIGN, UNSUPPORTED, LAUNCH; TOO_LARGE as for
+ * sp24_spmm_fwd, and when T*R/16 > 2^32 - 256 (the GEGLU kernel's launch).
  */
 int sp24_spmm_fwd_geglu(const void* X, const void* vals_row, const uint16_t* meta_row,
                         int64_t T, int64_t R, int64_t C, void* U, void* out, void* stream);
@@ -281,7 +282,8 @@ int sp24_weight_grad(const void* dY, const void* X, const void* W, const uint8_t
  *               later.  group = h is the two-halves layout [value | gate].
  *   T, h, group  T >= 0; h >= 0 and group > 0, multiples of 8; h % group == 0
  *   out    out  fp16 [T, h]
- * Errors: NULL, SHAPE, ALIGN, TOO_LARGE (T*2h >= 2^40), LAUNCH.
+ * Errors: NULL, SHAPE, ALIGN, LAUNCH; TOO_LARGE when T*2h >= 2^40 or when
+ * T*h/8 > 2^32 - 256 (one work-item per 8 units, the most one launch takes).
  */
 int sp24_geglu_fwd(const void* U, int64_t T, int64_t h, int64_t group, void* out, void* stream);
 
@@ -305,8 +307,11 @@ int sp24_geglu_bwd(const void* U, const void* dout, int64_t T, int64_t h, int64_
  *     right.  If some p_k > 1, p_k = 1 and the others are |a_j| / (S - |a_k|).
  *   - Sampling: the cumulative sums C_0 = p_0, C_1 = C_0 + p_1,
  *     C_2 = C_1 + p_2 split [0, 2).  The picks are i = #{C_j <= u} and
- *     k = #{C_j <= u + 1}.  If rounding makes k == i, k = i + 1, or
- *     (i, k) = (2, 3) when i == 3.
+ *     k = #{C_j <= u + 1}.  Rounding can put u in the last interval
+ *     (i == 3, which exact arithmetic never does, as u < 1 <= C_2); u + 1 is
+ *     then there too, and the picks are (i, k) = (2, 3).  Before the last
+ *     interval, u + 1 always lies past u's: every p_j <= 1, and the fp32
+ *     evaluation below keeps that order.
  *   - Kept values are a_i / p_i (0 where p_i == 0).  A group with fewer than
  *     two non-zero entries keeps its non-zero entry (if any) and the lowest
  *     other index, unchanged.
@@ -327,7 +332,9 @@ int sp24_geglu_bwd(const void* U, const void* dout, int64_t T, int64_t h, int64_
  *               The library's 2:4 row form: the kept pair of group g in
  *               order, and its nibble i | k << 2.  The sparse GEMMs accept it
  *               as their sparse operand.
- * Errors: NULL, SHAPE, ALIGN, TOO_LARGE, LAUNCH.
+ * Errors: NULL, SHAPE, ALIGN, LAUNCH; TOO_LARGE when a dimension reaches
+ * 2^31, rows*cols reaches 2^40, or rows*cols/16 > 2^32 - 256 (one work-item
+ * per meta word, the most one launch takes).
  */
 int sp24_mvue(const void* M, const float* U, int64_t rows, int64_t cols, void* vals, uint16_t* meta,
               void* stream);

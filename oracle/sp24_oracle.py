@@ -25,7 +25,8 @@ What the method computes, and the readings taken where the pages are silent:
      pairs, coded 0:{0,1} 1:{0,2} 2:{0,3} 3:{1,2} 4:{1,3} 5:{2,3}.  A pattern
      is a tuple (a, b, c, d) of codes for rows 0..3.  The list is every valid
      tuple in lexicographic order, a slowest.
-   * "argmax(out, dim=2)" is read as the argmax over the pattern axis.
+   * The argmax is taken over the pattern axis (in the convolution's own
+     output layout the axis the listing names would be a spatial one).
    * Score precision and order (silent): fp32, the kept magnitudes added one
      at a time in row-major order, starting from +0.
    * Tie-break (silent): the first maximum in pattern order (strict >).
@@ -80,7 +81,11 @@ What the method computes, and the readings taken where the pages are silent:
    an implementation with the same fp32 operations reproduces it bit for bit;
    that order compares cumulative masses with u times a scale instead of
    dividing (the same decisions in exact arithmetic), and a kept value is
-   sign(a_i) times that scale, so no step divides.
+   sign(a_i) times that scale, so no step divides.  The uniform enters only
+   through two fp32 roundings, fl(u D) and fl(fl(u D) + D): within an fp32
+   rounding of an interval boundary the picks are those of the definition at
+   u' = fl(u D) / D (and u'' = fl(fl(u D) + D) / D for u + 1), not at u.
+   That is the reading taken for such draws; elsewhere the two agree.
 """
 from __future__ import annotations
 
@@ -137,7 +142,7 @@ def _blocks(W: np.ndarray) -> np.ndarray:
 
 
 def block_scores(W: np.ndarray) -> np.ndarray:
-    """float32 [R/4, C/4, 90]: the correlation ``out`` of [HZ24 Alg.1].
+    """float32 [R/4, C/4, 90]: the per-block pattern scores of [HZ24 Alg.1].
 
     Step 1 takes |W| (fp16 -> fp32 is exact; the sign bit is cleared, so -0
     becomes +0).  Step 2 scores block (bi, bj) against pattern p by adding the
@@ -388,10 +393,15 @@ def mvue_group(a: np.ndarray, u: np.float32) -> tuple:
     i = int(W0 <= uD) + int(W1 <= uD) + int(W2 <= uD)
     k = int(W0 <= uD1) + int(W1 <= uD1) + int(W2 <= uD1)
     if k == i:
-        if i < 3:
-            k = i + 1
-        else:
-            i, k = 2, 3
+        # Only possible in the last interval.  Every mass is at most D, and
+        # fp32 rounding is monotone, so W_i = fl(W_(i-1) + w_i) <= fl(uD + D)
+        # whenever W_(i-1) <= uD: u + 1 always lies past u's interval when
+        # that is not the last.  u's interval is the last only by rounding (in
+        # exact arithmetic u < 1 <= C_2): W_2 <= fl(u D) needs a sum that rounds
+        # up, outside the 11-binade range where the sums are exact.  The picks
+        # are then the last two entries.
+        assert i == 3, "u and u + 1 share an interval before the last"
+        i, k = 2, 3
 
     def val(j):
         if j == kc:

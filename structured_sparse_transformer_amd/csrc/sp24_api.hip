@@ -14,6 +14,10 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;        // each dimension below 2^31
 constexpr int64_t kMaxElems = (int64_t)1 << 40;      // each matrix below 2^40 entries
+// the streaming kernels (GEGLU, MVUE) launch one work-item per 8 or 16
+// entries in one grid dimension, whose work-items HIP counts in 32 bits:
+// 256-wide workgroups allow at most 2^32 - 256 of them
+constexpr int64_t kMaxLaunchItems = ((int64_t)1 << 32) - 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
@@ -78,6 +82,7 @@ int check_geglu(int64_t T, int64_t h, int64_t group) {
   if (T < 0 || h < 0 || group <= 0 || h % 8 != 0 || group % 8 != 0 || (h != 0 && h % group != 0))
     return SP24_ERR_SHAPE;
   if (T >= kMaxDim || h >= kMaxDim || (T != 0 && 2 * h >= kMaxElems / T)) return SP24_ERR_TOO_LARGE;
+  if (T != 0 && h / 8 > kMaxLaunchItems / T) return SP24_ERR_TOO_LARGE;   // T * h/8 work-items
   return SP24_OK;
 }
 
@@ -150,6 +155,8 @@ int sp24_spmm_fwd_geglu(const void* X, const void* vals_row, const uint16_t* met
   if (R % 32 != 0) return SP24_ERR_SHAPE;
   if (T >= kMaxDim) return SP24_ERR_TOO_LARGE;
   if (T != 0 && (C >= kMaxElems / T || R >= kMaxElems / T)) return SP24_ERR_TOO_LARGE;
+  // the GEGLU kernel that finishes the shapes the fused kernel does not take
+  if (T != 0 && R / 16 > kMaxLaunchItems / T) return SP24_ERR_TOO_LARGE;
   if (T == 0 || R == 0) return SP24_OK;
   if (out == nullptr || (C != 0 && (X == nullptr || vals_row == nullptr || meta_row == nullptr))) return SP24_ERR_NULL;
   if (!aligned16(out) || (U && !aligned16(U)) ||
@@ -208,6 +215,7 @@ int sp24_mvue(const void* M, const float* U, int64_t rows, int64_t cols, void* v
   int st = check_dims(rows, cols, 1);
   if (st != SP24_OK) return st;
   if (cols % 16 != 0) return SP24_ERR_SHAPE;
+  if (rows != 0 && cols / 16 > kMaxLaunchItems / rows) return SP24_ERR_TOO_LARGE;   // one work-item per 16 entries
   if (rows == 0 || cols == 0) return SP24_OK;
   if (M == nullptr || U == nullptr || vals == nullptr || meta == nullptr) return SP24_ERR_NULL;
   if (!aligned16(M) || !aligned16(U) || !aligned16(vals) || !aligned16(meta)) return SP24_ERR_ALIGN;

@@ -204,6 +204,11 @@ def test_geglu_validation(L):
     assert fw(NUL, 4, 16, 8, FAKE, NUL) == 1
     assert fw(FAKE, 4, 16, 8, MIS, NUL) == 3
     assert fw(FAKE, 1 << 30, 1 << 10, 8, FAKE, NUL) == 6
+    # one launch takes at most 2^32 - 256 work-items of 8 units each
+    assert fw(FAKE, 1 << 20, (1 << 15) - 16, 8, MIS, NUL) == 3       # 2^32 - 2^21 items: allowed
+    assert fw(FAKE, 1 << 20, 1 << 15, 8, FAKE, NUL) == 6             # 2^32 items
+    assert bw(FAKE, FAKE, (1 << 32) // 2048 - 1, 2048 * 8, 8, MIS, NUL) == 3   # 2^32 - 2048 items: allowed
+    assert bw(FAKE, FAKE, 1 << 21, 2048 * 8, 8, FAKE, NUL) == 6
     assert fw(NUL, 0, 16, 8, NUL, NUL) == 0
     assert bw(FAKE, NUL, 4, 16, 8, FAKE, NUL) == 1
     assert bw(FAKE, FAKE, 4, 16, 8, MIS, NUL) == 3
@@ -220,6 +225,10 @@ def test_mvue_validation(L):
     assert f(FAKE, FAKE, 4, 16, FAKE, NUL, NUL) == 1
     assert f(FAKE, MIS, 4, 16, FAKE, FAKE, NUL) == 3
     assert f(FAKE, FAKE, 1 << 31, 16, FAKE, FAKE, NUL) == 6
+    # one work-item per 16 entries, at most 2^32 - 256 per launch
+    assert f(FAKE, FAKE, (1 << 28) - 16, 256, MIS, FAKE, NUL) == 3   # exactly 2^32 - 256 items: allowed
+    assert f(FAKE, FAKE, (1 << 28) - 15, 256, FAKE, FAKE, NUL) == 6
+    assert f(FAKE, FAKE, 1 << 22, 1 << 14, FAKE, FAKE, NUL) == 6     # 2^32 items
     assert f(NUL, NUL, 0, 16, NUL, NUL, NUL) == 0
 
 
@@ -233,6 +242,9 @@ def test_spmm_fwd_geglu_validation(L):
     assert f(FAKE, FAKE, FAKE, 8, 64, 64, MIS, FAKE, NUL) == 3
     assert f(FAKE, FAKE, FAKE, 8, 64, 64, NUL, MIS, NUL) == 3
     assert f(NUL, NUL, NUL, 0, 64, 64, NUL, NUL, NUL) == 0
+    # T * R/16 work-items of the GEGLU kernel that finishes unfused shapes
+    assert f(FAKE, FAKE, FAKE, 1 << 20, 1 << 16, 16, NUL, FAKE, NUL) == 6
+    assert f(FAKE, FAKE, FAKE, 1 << 20, (1 << 16) - 32, 16, NUL, MIS, NUL) == 3
 
 
 def test_ffn_layer_rejects_bad_shapes():

@@ -12,6 +12,8 @@ import pytest
 from oracle import sp24_oracle as O
 from structured_sparse_transformer_amd import workloads as WL
 
+from gpu_checks import Guarded
+
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
@@ -27,6 +29,13 @@ def sp():
 
 def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# 1 - 2^-11, 1791 * 2^-22, 1027 * 2^-24 and 1: their fp32 running sums are
+# exact, 1 - 2^-24 and then 2 (a tie, to even), so u = 1 - 2^-24 reaches the
+# last interval both for u and for u + 1
+FALLBACK_GROUP = np.array([1 - 2.0 ** -11, 1791 * 2.0 ** -22, 1027 * 2.0 ** -24, 1.0], np.float16)
+FALLBACK_U = np.float32(1 - 2.0 ** -24)
 
 
 def special_matrix(seed, rows, cols):
@@ -68,7 +77,15 @@ def test_mvue_bit_exact(sp, rows, cols):
     M = special_matrix(rows * 7 + cols, rows, cols)
     U = WL.uniform_f32(rows + cols, 9, (rows, cols // 4))
     U[0, : min(4, cols // 4)] = np.float32([0.0, 0.5, 0.999999940395, 0.25])[: min(4, cols // 4)]
-    assert_same(sp.sp24_mvue(dev(M), dev(U)), O.mvue(M, U))
+    # the group whose fp32 cumulative masses put u and u + 1 in the last
+    # interval (the oracle's (2, 3) fallback), with the largest u below 1
+    M[-1, :4] = FALLBACK_GROUP
+    U[-1, 0] = FALLBACK_U
+    gv, gm = Guarded((rows, cols // 2), torch.float16), Guarded((rows, cols // 16), torch.int16)
+    got = sp.sp24_mvue(dev(M), dev(U), out={"vals": gv.t, "meta": gm.t})
+    gv.check("vals")
+    gm.check("meta")
+    assert_same(got, O.mvue(M, U))
 
 
 def test_mvue_empty(sp):

@@ -8,9 +8,9 @@ Every test here runs on the CPU.  The oracle is pinned by:
 * hand-worked blocks in ``tests/golden/handworked_blocks.txt``;
 * metamorphic properties (sign flips, power-of-two scaling, transposition,
   separable blocks, planted patterns);
-* the literal form of Algorithm 1 ("Accelerating Transformer Pre-training
-  with 2:4 Sparsity"): a float64 ``conv2d`` with stride 4 and an ``argmax``
-  over the pattern axis, run with PyTorch's CPU library ops;
+* Algorithm 1 ("Accelerating Transformer Pre-training with 2:4 Sparsity")
+  restated as one float64 matrix product of the flattened 4x4 blocks with
+  the flattened patterns, and numpy's first-maximum argmax;
 * for the GEMMs, an explicit float64 loop over the compressed storage and
   identity-matrix special cases.
 """
@@ -233,18 +233,23 @@ def test_shape_rules():
 
 
 # ----------------------------------------------------------------------------
-# the literal Algorithm 1: conv2d with stride 4 and argmax over patterns
-def test_literal_conv2d_argmax_formulation():
-    torch = pytest.importorskip("torch")
+# Algorithm 1 of "Accelerating Transformer Pre-training with 2:4 Sparsity"
+# (reproducibility table, Pseudocode row) scores every 4x4 block of
+# |W| against every pattern (a correlation with stride 4 and no padding) and
+# keeps the best pattern per block.  The same scores as one float64 matrix
+# product: each block's 16 magnitudes, flattened row-major, against the 90
+# patterns flattened the same way.
+def test_blockwise_matmul_formulation():
     W = np.concatenate([_w(16, 32, 64, "normal"), _w(17, 32, 64, "ints")], axis=0)
-    Wabs = torch.from_numpy(np.abs(W).astype(np.float64))[None, None]     # step 1
-    m = torch.from_numpy(O.pattern_masks().astype(np.float64))[:, None]    # [90, 1, 4, 4]
-    out = torch.nn.functional.conv2d(Wabs, m, stride=4, padding=0)         # step 2: [1, 90, R/4, C/4]
-    out = out[0].permute(1, 2, 0)                                          # [R/4, C/4, 90]
-    index = torch.argmax(out, dim=2).numpy()                               # step 3: first maximum
-    assert (index == O.mask_search(W)).all()
-    # in this (exact) regime the fp32 row-major scores equal the float64 conv
-    assert (O.block_scores(W).astype(np.float64) == out.numpy()).all()
+    R, C = W.shape
+    mags = np.abs(W.astype(np.float64))
+    blocks = mags.reshape(R // 4, 4, C // 4, 4).transpose(0, 2, 1, 3).reshape(-1, 16)
+    patterns = O.pattern_masks().reshape(90, 16).astype(np.float64)
+    scores = blocks @ patterns.T                                     # [blocks, 90]
+    best = np.argmax(scores, axis=1).reshape(R // 4, C // 4)         # numpy returns the first maximum
+    assert (best == O.mask_search(W)).all()
+    # in this (exact) regime the fp32 row-major scores equal the float64 products
+    assert (O.block_scores(W).astype(np.float64).reshape(-1, 90) == scores).all()
 
 
 # ----------------------------------------------------------------------------
@@ -546,40 +551,95 @@ def test_mvue_matches_exact_rational_definition():
     exact rational arithmetic: p_i = 2|a_i|/S, the cap at 1 with the others
     rescaled by S - |a_k|, the cumulative sums, the intervals holding u and
     u + 1, and a_i / p_i.  Magnitudes span under 11 binades, so the fp32 sums
-    are exact; draws with u within 1e-6 of a cumulative sum are skipped."""
+    are exact and so is the scale D (p_j = w_j / D).  No draw is skipped: the
+    picks must be the definition's at u' = fl(u D) / D and u'' = fl(fl(u D) +
+    D) / D, the fp32 reading for the uniform, and they must equal the
+    definition's at u itself except within an fp32 rounding of a boundary.  A
+    quarter of the draws put u on or next to a cumulative sum on purpose."""
     from fractions import Fraction as Fr
+    f32 = np.float32
     rng = np.random.default_rng(62)
-    checked = capped = 0
-    for _ in range(4000):
+    checked = capped = moved = near = 0
+    for _ in range(6000):
         mag = rng.uniform(0.25, 8.0, 4)
         mag[rng.random(4) < 0.1] *= 16.0            # some groups get a capped entry
         a = (rng.choice([-1.0, 1.0], 4) * mag).astype(np.float16)
         a[rng.random(4) < 0.15] = 0
-        u = np.float32(rng.random())
         m = [abs(Fr(float(x))) for x in a]
         if sum(1 for x in m if x) < 2:
             continue
         S = sum(m)
         p = [2 * x / S for x in m]
+        D = S / 2
         over = [j for j in range(4) if p[j] > 1]
         if over:
             kc = over[0]
-            p = [Fr(1) if j == kc else m[j] / (S - m[kc]) for j in range(4)]
+            D = S - m[kc]
+            p = [Fr(1) if j == kc else m[j] / D for j in range(4)]
         assert sum(p) == 2
         C = [p[0], p[0] + p[1], p[0] + p[1] + p[2]]
+        u = f32(rng.random())
+        if rng.random() < 0.25:
+            # on a boundary: a cumulative sum (or one minus 1) rounded to fp32,
+            # or its fp32 neighbour
+            c = C[rng.integers(3)]
+            t = float(c - 1) if c >= 1 else float(c)
+            u = f32(t)
+            if rng.random() < 0.5:
+                u = np.nextafter(u, f32(rng.choice([-1.0, 2.0])), dtype=np.float32)
+            if not 0 <= u < 1:
+                continue
         uf = Fr(float(u))
-        if any(abs(c - uf) < Fr(1, 10**6) or abs(c - uf - 1) < Fr(1, 10**6) for c in C):
-            continue
-        i = sum(c <= uf for c in C)
-        k = sum(c <= uf + 1 for c in C)
+        assert Fr(float(f32(float(D)))) == D                # D is exact in fp32
+        uD = f32(u) * f32(float(D))
+        u1 = Fr(float(uD)) / D
+        u2 = Fr(float(f32(uD + f32(float(D))))) / D
+        i = sum(c <= u1 for c in C)
+        k = sum(c <= u2 for c in C)
         got = O.mvue_group(a, u)
         assert got[:2] == (i, k), (a, u)
         for j, v in ((i, got[2]), (k, got[3])):
             want = Fr(float(a[j])) / p[j] if p[j] else Fr(0)
             assert Fr(float(v)) == want, (a, u, j)
+        # the definition at u itself: the same picks unless u is within an
+        # fp32 rounding of a boundary
+        i0, k0 = sum(c <= uf for c in C), sum(c <= uf + 1 for c in C)
+        close = any(abs(c - uf) <= Fr(1, 2 ** 23) or abs(c - uf - 1) <= Fr(1, 2 ** 22) for c in C)
+        near += close
+        if (i0, k0) != (i, k):
+            assert close, (a, u)
+            moved += 1
         checked += 1
         capped += bool(over)
-    assert checked > 3000 and capped > 300
+    assert checked > 4000 and capped > 300 and near > 500, (checked, capped, near)
+    # the reading matters for some boundary draws, and only for those
+    assert 0 < moved < near, (moved, near)
+    print(f"{checked} draws, {capped} capped, {near} near a boundary, {moved} decided by the fp32 reading")
+
+
+def test_mvue_last_interval_fallback():
+    """fp32 rounding can put u in the last interval, which in exact arithmetic
+    it never is (u < 1 <= C_2).  With magnitudes 1 - 2^-11, 1791 * 2^-22,
+    1027 * 2^-24 and 1, the fp32 running sums are exact up to 1 - 2^-24, and
+    adding the last 1 gives 2 - 2^-24, a tie that rounds to 2 (even).  So S = 2,
+    D = 1, and u = 1 - 2^-24 satisfies W_2 <= u D: both u and u + 1 land in
+    the last interval.  The picks are then the last two entries, which is also
+    the exact answer: C_2 = (2 - 2^-23) / (2 - 2^-24) > u, and u + 1 > C_2."""
+    from fractions import Fraction as Fr
+    a = np.array([1 - 2.0 ** -11, 1791 * 2.0 ** -22, 1027 * 2.0 ** -24, 1.0], np.float16)
+    u = np.float32(1 - 2.0 ** -24)
+    assert [float(x) for x in a] == [1 - 2.0 ** -11, 1791 * 2.0 ** -22, 1027 * 2.0 ** -24, 1.0]
+    w2 = np.float32(np.float32(np.float32(a[0]) + np.float32(a[1])) + np.float32(a[2]))
+    assert w2 == np.float32(1 - 2.0 ** -24) and np.float32(w2 + np.float32(1)) == 2 and w2 <= u
+    i, k, vi, vk = O.mvue_group(a, u)
+    assert (i, k) == (2, 3)
+    m = [Fr(float(x)) for x in a]
+    S = sum(m)
+    C = [2 * m[0] / S, 2 * (m[0] + m[1]) / S, 2 * (m[0] + m[1] + m[2]) / S]
+    uf = Fr(float(u))
+    assert sum(c <= uf for c in C) == 2 and sum(c <= uf + 1 for c in C) == 3
+    # exact kept values are S / 2 = 1 - 2^-25; fp16 rounds both to 1
+    assert np.float16(vi) == np.float16(float(S / 2)) == 1 and np.float16(vk) == np.float16(float(S / 2))
 
 
 def test_mvue_matrix_form():

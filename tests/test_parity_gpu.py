@@ -3,9 +3,10 @@
 Masks, indices, compressed values and metadata must match the oracle bit for
 bit.  GEMM outputs (fp16 in, fp32 accumulation, fp16 out) must be within a
 normwise max relative error of 1e-2 and a mean absolute error of 1e-3 of the
-oracle's float64 product.  Full-size GEMMs are checked on sampled token rows
-(computed one by one by the oracle) plus a column-sum identity over every
-output.  All inputs are seeded synthetic draws (structured_sparse_transformer_amd.workloads).
+oracle's float64 product.  Full-size GEMMs are checked element by element
+(the oracle runs over chunks of token rows), with the column-sum identity as
+an extra check; the 1.5B noisy loop's middle steps compare 512 random token
+rows per GEMM.  Guard bands around outputs catch writes outside them.  All inputs are seeded synthetic draws (structured_sparse_transformer_amd.workloads).
 """
 import os
 
@@ -14,6 +15,8 @@ import pytest
 
 from oracle import sp24_oracle as O
 from structured_sparse_transformer_amd import workloads as WL
+
+from gpu_checks import Guarded, check_all, gemm_full, guarded_forms
 
 pytestmark = pytest.mark.gpu
 
@@ -304,11 +307,9 @@ def _sampled_rows(T, n, seed):
 
 
 def check_full_gemm(out_dev, A, vals, meta, R, C, fwd: bool, seed: int):
-    """Sampled rows against the oracle, plus the column-sum identity over all rows."""
-    rows = _sampled_rows(A.shape[0], 256, seed)
-    out_rows = host(out_dev[torch.from_numpy(rows).cuda()])
-    ref_rows = (O.spmm_fwd if fwd else O.spmm_bwd_input)(A[rows], vals, meta, R, C)
-    mr, ma = check_gemm(out_rows, ref_rows)
+    """Every element against the oracle (chunked over tokens), plus the
+    column-sum identity over all rows as an extra check."""
+    mr, ma = gemm_full(out_dev, A, vals, meta, R, C, fwd)
     # sum over tokens: sum_t out[t] = (sum_t A[t]) * Ws^T (fwd) or * Ws (bwd)
     colsum = out_dev.float().sum(dim=0).double().cpu().numpy()
     a_sum = A.astype(np.float64).sum(axis=0, keepdims=True)
@@ -318,43 +319,63 @@ def check_full_gemm(out_dev, A, vals, meta, R, C, fwd: bool, seed: int):
     return mr, ma
 
 
-@pytest.mark.parametrize("N", [1152, 1280])
+@pytest.mark.parametrize("N", [1152, 1280, 6400])
 def test_spmm_tail_split_ragged_tokens(sp, N):
     """Feature counts whose last 256-wide strip leaves a partial round on 256
     CUs run that strip as smaller tiles: 256 x 64 when 128 features remain
-    (N = 1152), 128 x 128 when 256 remain (N = 1280).  A ragged token count
-    (16347, not a multiple of 64) puts rows past T into the last tiles of both
-    launches; both products, all tokens' column sums and sampled rows checked."""
+    (N = 1152), 128 x 128 when 256 remain (N = 1280, and the 6400 features of
+    the GPT-2-1.5B FFN).  A ragged token count (16347, not a multiple of 64)
+    puts rows past T into the last tiles of both launches.  Every element of
+    both products is checked, with guard bands around each output: the strip
+    launch writes at a column offset with the full row stride."""
     T, K = 16347, 128
     W = WL.normal_f16(N + 7, 1, (N, K), 0.02)
     X = WL.normal_f16(N + 7, 2, (T, K))
-    dY = WL.normal_f16(N + 7, 3, (T, N))
-    o = sp.sp24_search_compress(dev(W))
+    Wt = WL.normal_f16(N + 7, 4, (K, N), 0.02)          # input gradient with N output features
+    dY = WL.normal_f16(N + 7, 3, (T, K))
     c = O.compress(W, O.mask_search(W))
-    Y = sp.sp24_spmm_fwd(dev(X), o["vals_row"], o["meta_row"], N, K)
-    dX = sp.sp24_spmm_bwd_input(dev(dY), o["vals_col"], o["meta_col"], N, K)
-    check_full_gemm(Y, X, c["vals_row"], c["meta_row"], N, K, True, N)
-    check_full_gemm(dX, dY, c["vals_col"], c["meta_col"], N, K, False, N + 1)
-    # the last rows of the last token tile, where the launches stop
-    tail = torch.arange(T - 40, T, device="cuda")
-    want = O.spmm_fwd(X[T - 40:], c["vals_row"], c["meta_row"], N, K)
-    check_gemm(host(Y[tail]), want)
+    ct = O.compress(Wt, O.mask_search(Wt))
+    fw = guarded_forms(N, K)
+    o = sp.sp24_search_compress(dev(W), out={k: g.t for k, g in fw.items()})
+    bw = guarded_forms(K, N)
+    ot = sp.sp24_search_compress(dev(Wt), out={k: g.t for k, g in bw.items()})
+    assert_forms_equal(o, c)
+    assert_forms_equal(ot, ct)
+    gY, gdX = Guarded((T, N), torch.float16), Guarded((T, N), torch.float16)
+    sp.sp24_spmm_fwd(dev(X), o["vals_row"], o["meta_row"], N, K, Y=gY.t)
+    sp.sp24_spmm_bwd_input(dev(dY), ot["vals_col"], ot["meta_col"], K, N, dX=gdX.t)
+    check_all(fw)
+    check_all(bw)
+    gY.check("Y")
+    gdX.check("dX")
+    check_full_gemm(gY.t, X, c["vals_row"], c["meta_row"], N, K, True, N)
+    check_full_gemm(gdX.t, dY, ct["vals_col"], ct["meta_col"], K, N, False, N + 1)
 
 
 @pytest.mark.parametrize("cfg", [WL.GPT2_355M, WL.GPT2_774M, WL.GPT2_1P5B], ids=lambda c: c.name)
 def test_ffn_layer_configs(sp, cfg):
+    """Search, compression and the four sparse GEMMs of a GPT-2 FFN layer at
+    full size: masks and forms bit for bit, every GEMM output element against
+    the oracle, guard bands around every output."""
     inp = WL.ffn_inputs(cfg)
     for which, W, A_fwd, A_bwd in ((1, inp.w1, inp.x, inp.dy1), (2, inp.w2, inp.h, inp.dy2)):
         R, C = W.shape
+        T = A_fwd.shape[0]
+        print(f"{cfg.name} W{which} {R}x{C}", flush=True)
         idx = O.mask_search(W)
         want = O.compress(W, idx)
-        o = sp.sp24_search_compress(dev(W))
+        g = guarded_forms(R, C)
+        o = sp.sp24_search_compress(dev(W), out={k: v.t for k, v in g.items()})
+        gY, gdX = Guarded((T, R), torch.float16), Guarded((T, C), torch.float16)
+        sp.sp24_spmm_fwd(dev(A_fwd), o["vals_row"], o["meta_row"], R, C, Y=gY.t)
+        sp.sp24_spmm_bwd_input(dev(A_bwd), o["vals_col"], o["meta_col"], R, C, dX=gdX.t)
+        check_all(g)
+        gY.check("Y")
+        gdX.check("dX")
         assert_idx_equal(o["idx"], idx)
         assert_forms_equal(o, want)
-        Y = sp.sp24_spmm_fwd(dev(A_fwd), o["vals_row"], o["meta_row"], R, C)
-        dX = sp.sp24_spmm_bwd_input(dev(A_bwd), o["vals_col"], o["meta_col"], R, C)
-        check_full_gemm(Y, A_fwd, want["vals_row"], want["meta_row"], R, C, True, which)
-        check_full_gemm(dX, A_bwd, want["vals_col"], want["meta_col"], R, C, False, 10 + which)
+        check_full_gemm(gY.t, A_fwd, want["vals_row"], want["meta_row"], R, C, True, which)
+        check_full_gemm(gdX.t, A_bwd, want["vals_col"], want["meta_col"], R, C, False, 10 + which)
 
 
 @pytest.mark.parametrize("chunk", range(4))
