@@ -42,6 +42,8 @@ SC_BYTES_PER_ELEM = 4.375           # read W 2 and previous idx 1/16; write idx 
 COUNTERS = os.path.join(ROOT, "profiles", "spmm_nt_gpt2-1.5b_counters.json")
 DECAY = 2e-4                         # masked decay factor of the weight-gradient leg
 GEGLU_GROUP = 16                     # GEGLU column layout: blocks of 16 values, then their 16 gates
+TRIALS = 5                           # repeated timings behind each reported median
+ROTATE_BYTES = 512 * 1024 * 1024     # rotating input sets exceed L2 and the 256 MB last-level cache
 
 
 def mvue_uniforms(torch, dev, cfg):
@@ -62,6 +64,8 @@ def geglu_inputs(torch, dev, cfg):
     gd = torch.randn(cfg.tokens, cfg.dff, generator=g, device=dev).half()
     return U, gd
 GEMM_SRC = os.path.join(ROOT, "structured_sparse_transformer_amd", "csrc", "sp24_spmm.hip")
+SC_SRC = os.path.join(ROOT, "structured_sparse_transformer_amd", "csrc", "sp24_search.hip")
+SC_COUNTERS = os.path.join(ROOT, "profiles", "search_compress_gpt2-1.5b_counters.json")
 
 
 def log(*a):
@@ -80,6 +84,18 @@ def traffic_from_counters():
     except (OSError, ValueError):
         return None
     if c.get("source_sha256_16") != src_hash(GEMM_SRC):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def sc_traffic_from_counters():
+    """HBM bytes per batched search+compress launch (both 1.5B weights) from the
+    committed counter summary, or None when missing or stale."""
+    try:
+        c = json.load(open(SC_COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha256_16") != src_hash(SC_SRC):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -313,6 +329,19 @@ def main():
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
     log(f"timed {args.steps} steps: {ms_total:.3f} ms on events, {wall_ms:.3f} ms wall")
+    # the same --steps steps timed again in TRIALS more blocks, each between its
+    # own synchronised pair of events (flips into scratch counters), for the
+    # median beside the contract's single timing above
+    trial_ms = []
+    for _ in range(TRIALS):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for s in range(args.warmup, nsteps):
+            step(s, fl=FLb)
+        t1.record()
+        torch.cuda.synchronize()
+        trial_ms.append(t0.elapsed_time(t1) / args.steps)
     # search: from the previous step's last GEMM (or the start) to the end of
     # the search; GEMMs: the four calls of each step
     sc_ms = float(np.mean([(start if k == 0 else tev[k - 1][5]).elapsed_time(tev[k][1]) for k in range(args.steps)]))
@@ -321,17 +350,21 @@ def main():
     # per-GEMM breakdown: the same steps again with events between every
     # call, all enqueued before a single synchronisation so that host-side
     # call overhead never sits between two events of an idle GPU
-    evs = []
-    for s in range(args.warmup, nsteps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        step(s, ev, FLb)
-        evs.append(ev)
-    torch.cuda.synchronize()
-    seg = np.zeros(5)
-    for ev in evs:
-        seg += [ev[i].elapsed_time(ev[i + 1]) for i in range(5)]
-    seg /= args.steps
-    gemm_ms = seg[1:]
+    seg_trials = []
+    for _ in range(TRIALS):
+        evs = []
+        for s in range(args.warmup, nsteps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+            step(s, ev, FLb)
+            evs.append(ev)
+        torch.cuda.synchronize()
+        seg = np.zeros(5)
+        for ev in evs:
+            seg += [ev[i].elapsed_time(ev[i + 1]) for i in range(5)]
+        seg_trials.append(seg / args.steps)
+    seg_trials = np.array(seg_trials)
+    gemm_ms = np.median(seg_trials[:, 1:], axis=0)
+    gemm_ms_mean = seg_trials[:, 1:].mean(axis=0)
     gemm_shapes = cfg.gemm_shapes()
     sc_bytes = SC_BYTES_PER_ELEM * 2 * d * f
     sc_gbps = sc_bytes / (sc_ms * 1e-3) / 1e9
@@ -358,7 +391,8 @@ def main():
         t1.record()
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) * 1e3 / len(Ws)
-    pw_us = [per_weight_us(W1s, F1), per_weight_us(W2s, F2)]
+    pw_trials = [[per_weight_us(W1s, F1) for _ in range(TRIALS)], [per_weight_us(W2s, F2) for _ in range(TRIALS)]]
+    pw_us = [float(np.median(t)) for t in pw_trials]
     pw_gbps = [SC_BYTES_PER_ELEM * d * f / (us * 1e-6) / 1e9 for us in pw_us]
 
     # the step's batched launch (both weights, flips counted) back to back over
@@ -376,8 +410,10 @@ def main():
         t1.record()
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) * 1e3 / len(W1s)
-    bb_us = both_weights_us()
+    bb_trials = [both_weights_us() for _ in range(TRIALS)]
+    bb_us = float(np.median(bb_trials))
     bb_gbps = sc_bytes / (bb_us * 1e-6) / 1e9
+    sc_traffic = sc_traffic_from_counters()
 
     # the standalone flip count (two index arrays of W1, 640000 blocks each),
     # back-to-back calls: launch-bound at this size
@@ -483,93 +519,128 @@ def main():
                      "TFLOPs_dense_equiv": round(layer_flops / (layer_ms * 1e-3) / 1e12, 1),
                      "note": "dense-equivalent flops 2*T*N*K of the two forward GEMMs, the two input-gradient "
                              "GEMMs and the two weight gradients, over the whole step's time"}
-    # the other GPT-2 FFN shapes of the same path (355M, 774M), timed warm:
-    # one search+compress launch for both weights (no flip count) and each of
-    # the four sparse GEMMs, on device-generated N(0,1) activations and
-    # N(0, 0.02) weights
+    # the other GPT-2 FFN shapes of the same path (355M, 774M): one
+    # search+compress launch for both weights (no flip count), back to back
+    # over distinct weight pairs and output sets totalling more than
+    # ROTATE_BYTES of inputs, so the caches cannot serve them; and each of the
+    # four sparse GEMMs, warm.  Device-generated N(0, 0.02) weights and N(0, 1)
+    # activations.
+    def rotating_us(run, sets):
+        """Median over TRIALS of the average µs per call of run(set) over all
+        sets back to back between one pair of events."""
+        run(sets[0])
+        out = []
+        for _ in range(TRIALS):
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for st in sets:
+                run(st)
+            t1.record()
+            torch.cuda.synchronize()
+            out.append(t0.elapsed_time(t1) * 1e3 / len(sets))
+        return float(np.median(out)), out
+
     other = {}
     for oc in () if args.no_other_configs else (WL.GPT2_355M, WL.GPT2_774M):
         og = torch.Generator(device=dev)
         og.manual_seed(oc.seed)
         od, of, oT = oc.d, oc.dff, oc.tokens
         rnd = lambda *shape, sd=1.0: (torch.randn(*shape, generator=og, device=dev) * sd).half()  # noqa: E731
-        Wa, Wb = rnd(of, od, sd=0.02), rnd(od, of, sd=0.02)
+        n_rot = -(-ROTATE_BYTES // (2 * 2 * of * od)) + 8
+        pairs = [(rnd(of, od, sd=0.02), rnd(od, of, sd=0.02)) for _ in range(n_rot)]
+        pair_forms = [sp24.sp24_search_compress_batch(list(wp)) for wp in pairs]
+        sc_us, sc_trials = rotating_us(lambda k: sp24.sp24_search_compress_batch(list(pairs[k]), outs=pair_forms[k]),
+                                       list(range(n_rot)))
+        Wa, Wb = pairs[0]
+        fa, fb = pair_forms[0]
+        del pairs, pair_forms
         Xa, Ha, dYa, dYb = rnd(oT, od), rnd(oT, of), rnd(oT, of), rnd(oT, od)
-        Fo = sp24.sp24_search_compress_batch([Wa, Wb])
-        sc_o = timed_ms(lambda: sp24.sp24_search_compress_batch([Wa, Wb], outs=Fo), 10)
         Ya, dXa = torch.empty(oT, of, dtype=torch.float16, device=dev), torch.empty(oT, od, dtype=torch.float16, device=dev)
         Yb, dXb = torch.empty(oT, od, dtype=torch.float16, device=dev), torch.empty(oT, of, dtype=torch.float16, device=dev)
-        fa, fb = Fo
         calls = {
             "fwd1": lambda: sp24.sp24_spmm_fwd(Xa, fa["vals_row"], fa["meta_row"], of, od, Y=Ya),
             "bwd1": lambda: sp24.sp24_spmm_bwd_input(dYa, fa["vals_col"], fa["meta_col"], of, od, dX=dXa),
             "fwd2": lambda: sp24.sp24_spmm_fwd(Ha, fb["vals_row"], fb["meta_row"], od, of, Y=Yb),
             "bwd2": lambda: sp24.sp24_spmm_bwd_input(dYb, fb["vals_col"], fb["meta_col"], od, of, dX=dXb),
         }
-        g_ms = {name: timed_ms(fn, 5) for name, fn in calls.items()}
+        g_ms = {name: float(np.median([timed_ms(fn, 5) for _ in range(TRIALS)])) for name, fn in calls.items()}
         g_flops = {name: 2 * t * n * k for name, t, n, k in oc.gemm_shapes()}
         executed = sum(g_flops.values()) / 2 / (sum(g_ms.values()) * 1e-3) / 1e12
+        sc_gbps_o = 4.3125 * 2 * of * od / (sc_us * 1e-6) / 1e9
         other[oc.name] = {
             "d": od, "d_ff": of, "tokens": oT,
-            "search_compress_us_both_weights": round(sc_o * 1e3, 1),
-            "search_compress_GBps": round(4.3125 * 2 * of * od / (sc_o * 1e-3) / 1e9, 1),
+            "search_compress_us_both_weights": round(sc_us, 1),
+            "search_compress_GBps": round(sc_gbps_o, 1),
+            "search_compress_frac_hbm": round(sc_gbps_o / HBM_PEAK_GBPS, 4),
+            "search_compress_trials_us": [round(x, 1) for x in sc_trials],
+            "search_compress_rotation": f"{n_rot} distinct weight pairs and output sets, "
+                                        f"{n_rot * 4 * of * od / 1e6:.0f} MB of weights",
             "gemm_us": {k: round(v * 1e3, 1) for k, v in g_ms.items()},
             "gemm_TFLOPs_dense_equiv": {k: round(g_flops[k] / (g_ms[k] * 1e-3) / 1e12, 1) for k in g_ms},
             "gemm_frac_of_dense_mfma_peak": round(executed / FP16_MFMA_PEAK_TFLOPS, 4),
         }
-        del Wa, Wb, Xa, Ha, dYa, dYb, Fo, fa, fb, Ya, dXa, Yb, dXb, calls
+        del Wa, Wb, Xa, Ha, dYa, dYb, fa, fb, Ya, dXa, Yb, dXb, calls
     if not args.no_other_configs:
         # the 4096 x 4096 stress weight (integer rows, a constant band across
-        # the seam, N(0, 0.02) rows): search and compression only
-        Wst = torch.from_numpy(WL.stress_weight(WL.STRESS_SEED)).to(dev)
-        Fst = sp24.sp24_search_compress_batch([Wst])
-        st_ms = timed_ms(lambda: sp24.sp24_search_compress_batch([Wst], outs=Fst), 10)
-        other["stress-4096"] = {"shape": list(Wst.shape), "search_compress_us": round(st_ms * 1e3, 1),
-                                "search_compress_GBps": round(4.3125 * Wst.numel() / (st_ms * 1e-3) / 1e9, 1)}
-        del Wst, Fst
+        # the seam, N(0, 0.02) rows): search and compression only, over
+        # distinct copies and output sets
+        Wst0 = torch.from_numpy(WL.stress_weight(WL.STRESS_SEED)).to(dev)
+        n_rot = -(-ROTATE_BYTES // (2 * Wst0.numel())) + 8
+        Wst = [Wst0.clone() for _ in range(n_rot)]
+        Fst = [sp24.sp24_search_compress_batch([w]) for w in Wst]
+        st_us, st_trials = rotating_us(lambda k: sp24.sp24_search_compress_batch([Wst[k]], outs=Fst[k]),
+                                       list(range(n_rot)))
+        st_gbps = 4.3125 * Wst0.numel() / (st_us * 1e-6) / 1e9
+        other["stress-4096"] = {"shape": list(Wst0.shape), "search_compress_us": round(st_us, 1),
+                                "search_compress_GBps": round(st_gbps, 1),
+                                "search_compress_frac_hbm": round(st_gbps / HBM_PEAK_GBPS, 4),
+                                "search_compress_trials_us": [round(x, 1) for x in st_trials],
+                                "search_compress_rotation": f"{n_rot} distinct copies and output sets, "
+                                                            f"{n_rot * 2 * Wst0.numel() / 1e6:.0f} MB of weights"}
+        del Wst0, Wst, Fst
     flops_step = cfg.dense_equiv_flops()
     value = flops_step / (ms_per_step * 1e-3) / 1e12
 
     context = None
     if not args.no_context:
         context = {}
-        # dense fp16 library GEMM of the same shapes (hipBLASLt through torch) and a copy
-        Wd1 = W1s[0]
-        for _ in range(2):
-            torch.matmul(X, Wd1.t())
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
-            torch.matmul(X, Wd1.t())
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 10
-        context["dense_torch_matmul_fp16_TFLOPs"] = round(2 * T * f * d / (ms * 1e-3) / 1e12, 1)
-        context["dense_torch_matmul_ms"] = round(ms, 4)
+        # dense fp16 library GEMMs (hipBLASLt through torch) of the four shapes
+        # of the step, on the dense weights: the MI355X sparse/dense ratio
+        Wd1, Wd2 = W1s[0], W2s[0]
+        dense = {"fwd1": lambda: torch.matmul(X, Wd1.t()), "bwd1": lambda: torch.matmul(dY1, Wd1),
+                 "fwd2": lambda: torch.matmul(H, Wd2.t()), "bwd2": lambda: torch.matmul(dY2, Wd2)}
+        dense_ms = {k: float(np.median([timed_ms(fn, 10) for _ in range(TRIALS)])) for k, fn in dense.items()}
+        context["dense_torch_matmul_fp16_TFLOPs"] = {
+            n: round(2 * Tt * N * K / (dense_ms[n] * 1e-3) / 1e12, 1) for n, Tt, N, K in gemm_shapes}
+        context["dense_torch_matmul_us"] = {k: round(v * 1e3, 1) for k, v in dense_ms.items()}
+        context["sparse_over_dense_speedup"] = {n: round(dense_ms[n] / gemm_ms[i], 3)
+                                                for i, (n, *_) in enumerate(gemm_shapes)}
         # the library's dense weight-gradient product, dY1^T X, fp16 out
         dYt = dY1.t()
-        torch.matmul(dYt, X)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(10):
-            torch.matmul(dYt, X)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 10
+        ms = float(np.median([timed_ms(lambda: torch.matmul(dYt, X), 10) for _ in range(TRIALS)]))
         context["dense_torch_matmul_dYT_X_fp16_TFLOPs"] = round(2 * T * f * d / (ms * 1e-3) / 1e12, 1)
+        # a 512 MiB device copy: the achievable HBM rate at a large size
         src = torch.empty(512 * 1024 * 1024 // 2, dtype=torch.float16, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(5):
-            dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 5
+        ms = float(np.median([timed_ms(lambda: dst.copy_(src), 5) for _ in range(TRIALS)]))
         context["copy_512MiB_GBps"] = round(2 * src.numel() * 2 / (ms * 1e-3) / 1e9, 1)
         del src, dst
+        # the streaming floor at search+compress's own size: device copies that
+        # move the same bytes as one launch (one weight: 20.5 MB read + 23.7 MB
+        # written; both weights: twice that), each copy half reads and half
+        # writes, rotating over distinct buffer sets beyond the caches
+        floor = {}
+        for name, nbytes in (("one_weight", SC_BYTES_PER_ELEM * d * f), ("both_weights", sc_bytes)):
+            half = int(nbytes / 2) // 256 * 256
+            n_rot = -(-ROTATE_BYTES // half) + 8
+            bufs = [(torch.empty(half // 2, dtype=torch.float16, device=dev),
+                     torch.empty(half // 2, dtype=torch.float16, device=dev)) for _ in range(n_rot)]
+            us, tr = rotating_us(lambda k: bufs[k][1].copy_(bufs[k][0]), list(range(n_rot)))
+            gbps = 2 * half / (us * 1e-6) / 1e9
+            floor[name] = {"bytes": 2 * half, "us": round(us, 2), "GBps": round(gbps, 1),
+                           "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4), "rotation": n_rot}
+            del bufs
+        context["streaming_floor_same_traffic"] = floor
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -584,6 +655,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_trials": {"median": round(float(np.median(trial_ms)), 4),
+                               "mean": round(float(np.mean(trial_ms)), 4),
+                               "all": [round(x, 4) for x in trial_ms],
+                               "note": f"{TRIALS} more timings of the same --steps steps after the one above"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -606,6 +681,13 @@ def main():
                                                  "versions of the run, back to back between one pair of events; "
                                                  "search_compress_GBps above times each launch inside the step, "
                                                  "between the step's own events"},
+        "search_compress_roofline": {
+            "kernel": "search_compress_kernel (one sp24_search_compress_batch launch for W1 and W2, flips counted)",
+            "bound": "hbm", "achieved": round(bb_gbps, 1), "launch_us": round(bb_us, 2), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(bb_gbps / HBM_PEAK_GBPS, 4), "traffic": sc_traffic,
+            "trials_us": [round(x, 2) for x in bb_trials],
+            "note": "4.375 algorithmic bytes per weight element over the median back-to-back launch time; traffic is "
+                    "FETCH_SIZE + WRITE_SIZE per launch from the committed counter summary (null when stale)"},
         "flip_rate": {"definition": "mask entries changed since the previous step's search / entries",
                       "w1_mean": float(f"{flips[:, 0].mean():.4g}"), "w2_mean": float(f"{flips[:, 1].mean():.4g}"),
                       "w1_first_last": [float(f"{flips[0, 0]:.4g}"), float(f"{flips[-1, 0]:.4g}")],
@@ -614,9 +696,11 @@ def main():
                       "standalone_GBps": round(fl_bytes / (fl_us * 1e-6) / 1e9, 1)},
         "gemm_TFLOPs_dense_equiv": {n: round(v, 1) for (n, *_), v in zip(gemm_shapes, gemm_dense_tflops)},
         "gemm_us": {n: round(ms * 1e3, 1) for (n, *_), ms in zip(gemm_shapes, gemm_ms)},
-        "gemm_breakdown_note": "gemm_us and gemm_TFLOPs_dense_equiv come from a second pass of the same steps with "
-                               "events between every call; roofline and search_compress from events in the timed "
-                               "region (after each search and after each step's four GEMMs)",
+        "gemm_us_mean": {n: round(ms * 1e3, 1) for (n, *_), ms in zip(gemm_shapes, gemm_ms_mean)},
+        "gemm_breakdown_note": f"gemm_us (median) and gemm_us_mean over {TRIALS} more passes of the same steps with "
+                               "events between every call; gemm_TFLOPs_dense_equiv from the medians; roofline and "
+                               "search_compress from events in the timed region (after each search and after each "
+                               "step's four GEMMs)",
         "roofline": {"kernel": "spmm_nt (one sp24_spmm_* call)", "bound": "mfma", "achieved": round(achieved, 1),
                      "launch_us": round(avg_launch_ms * 1e3, 1),
                      "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),

@@ -113,9 +113,16 @@ __device__ __forceinline__ void gelu_cdf_pdf(float x, float& cdf, float& pdf) {
   pdf = (r.ex * __builtin_amdgcn_exp2f(-r.p * kLog2E)) * kInvSqrt2Pi;
 }
 __device__ __forceinline__ float gelu_f32(float x) { return x * gelu_cdf(x); }
-// value * GELU(gate) from fp16 inputs, rounded to nearest even in fp16
+// value * GELU(gate) from fp16 inputs: the fp32 product, rounded to nearest
+// even in fp16.  The empty asm pins the product as an fp32 value.  Without
+// it the backend may fold the multiply and the conversion into one mixed
+// fp16 FMA (v_fma_mixlo_f16), which rounds once instead of twice; it did so
+// in the fused GEMM epilogue but not in the GEGLU kernel, and near fp16
+// rounding ties the two then differed by one ulp.
 __device__ __forceinline__ _Float16 geglu_f16(_Float16 value, _Float16 gate) {
-  return (_Float16)((float)value * gelu_f32((float)gate));
+  float prod = (float)value * gelu_f32((float)gate);
+  asm volatile("" : "+v"(prod));
+  return (_Float16)prod;
 }
 
 // Number of compute units of the current device (cached per device; host
