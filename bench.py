@@ -8,8 +8,8 @@ timing), and each step runs
     search+compress(W1_s and W2_s, one launch)         (sp24_search_compress_batch)
         with the flip count of each weight fused in: each weight's index
         buffer is updated in place and the entries that changed are counted
-    Y1  = X   W1s^T,  dX1 = dY1 W1s                     (sp24_spmm_fwd / _bwd_input)
-    Y2  = H   W2s^T,  dX2 = dY2 W2s
+    Y1  = X   W1s^T,  dX1 = dY1 W1s                     (one sp24_spmm_group launch
+    Y2  = H   W2s^T,  dX2 = dY2 W2s                      for all four products)
 
 Prints one JSON line.  ``value`` is dense-equivalent GEMM TFLOP/s over the
 whole step (2*T*N*K summed over the four GEMMs, divided by the wall time of
@@ -221,6 +221,12 @@ def profile_only(args, sp24, torch, dev, cfg, F1, F2, FL, W1s, W2s, X, dY1, H, d
             break
     torch.cuda.synchronize()
     if args.profile_kernel == "gemm":
+        prods = [(X, F1["vals_row"], F1["meta_row"], Y1), (dY1, F1["vals_col"], F1["meta_col"], dX1),
+                 (H, F2["vals_row"], F2["meta_row"], Y2), (dY2, F2["vals_col"], F2["meta_col"], dX2)]
+        for _ in range(n):
+            sp24.sp24_spmm_group(prods)
+        torch.cuda.synchronize()
+    if args.profile_kernel == "gemm_single":
         for _ in range(n):
             sp24.sp24_spmm_fwd(X, F1["vals_row"], F1["meta_row"], f, d, Y=Y1)
             sp24.sp24_spmm_bwd_input(dY1, F1["vals_col"], F1["meta_col"], f, d, dX=dX1)
@@ -243,8 +249,8 @@ def main():
                     help="skip the gated FFN layer step (its GEMMs have other shapes than the step's)")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the 355M and 774M shapes (their launches would mix into a kernel trace's averages)")
-    ap.add_argument("--profile-kernel", choices=["gemm", "search_compress", "flip_count", "weight_grad", "geglu", "ffn_layer",
-                                                 "mvue", "copy"],
+    ap.add_argument("--profile-kernel", choices=["gemm", "gemm_single", "search_compress", "flip_count", "weight_grad",
+                                                 "geglu", "ffn_layer", "mvue", "copy"],
                     help="run only this kernel --steps times (for rocprofv3 counter passes); prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -286,9 +292,12 @@ def main():
     Y2 = torch.empty(T, d, dtype=torch.float16, device=dev)
     dX2 = torch.empty(T, f, dtype=torch.float16, device=dev)
 
-    def step(s, ev=None, fl=FL, marks=(0, 1, 2, 3, 4, 5)):
+    step_products = [(X, F1["vals_row"], F1["meta_row"], Y1), (dY1, F1["vals_col"], F1["meta_col"], dX1),
+                     (H, F2["vals_row"], F2["meta_row"], Y2), (dY2, F2["vals_col"], F2["meta_col"], dX2)]
+
+    def step(s, ev=None, fl=FL, marks=(0, 1, 5)):
         # ev[i] is recorded at mark i when i is in `marks`: 0 before the search,
-        # 1 after it, 2..4 between the GEMMs, 5 after the last one
+        # 1 after it, 5 after the grouped launch of the four GEMMs
         def mark(i):
             if ev is not None and i in marks:
                 ev[i].record()
@@ -296,14 +305,25 @@ def main():
         sp24.sp24_search_compress_batch([W1s[s], W2s[s]], outs=[F1, F2], prev=[F1["idx"], F2["idx"]],
                                         flips=[fl[s, 0:1], fl[s, 1:2]])
         mark(1)
-        sp24.sp24_spmm_fwd(X, F1["vals_row"], F1["meta_row"], f, d, Y=Y1)
-        mark(2)
-        sp24.sp24_spmm_bwd_input(dY1, F1["vals_col"], F1["meta_col"], f, d, dX=dX1)
-        mark(3)
-        sp24.sp24_spmm_fwd(H, F2["vals_row"], F2["meta_row"], d, f, Y=Y2)
-        mark(4)
-        sp24.sp24_spmm_bwd_input(dY2, F2["vals_col"], F2["meta_col"], d, f, dX=dX2)
+        sp24.sp24_spmm_group(step_products)
         mark(5)
+
+    def step_single(s, ev, fl):
+        # the same step with the four GEMMs as single launches and events
+        # between them (the per-GEMM breakdown): ev[0] before the search, ev[1]
+        # after it, ev[2..4] between the GEMMs, ev[5] after the last one
+        ev[0].record()
+        sp24.sp24_search_compress_batch([W1s[s], W2s[s]], outs=[F1, F2], prev=[F1["idx"], F2["idx"]],
+                                        flips=[fl[s, 0:1], fl[s, 1:2]])
+        ev[1].record()
+        sp24.sp24_spmm_fwd(X, F1["vals_row"], F1["meta_row"], f, d, Y=Y1)
+        ev[2].record()
+        sp24.sp24_spmm_bwd_input(dY1, F1["vals_col"], F1["meta_col"], f, d, dX=dX1)
+        ev[3].record()
+        sp24.sp24_spmm_fwd(H, F2["vals_row"], F2["meta_row"], d, f, Y=Y2)
+        ev[4].record()
+        sp24.sp24_spmm_bwd_input(dY2, F2["vals_col"], F2["meta_col"], d, f, dX=dX2)
+        ev[5].record()
 
     if args.profile_kernel:
         profile_only(args, sp24, torch, dev, cfg, F1, F2, FL, W1s, W2s, X, dY1, H, dY2, Y1, dX1, Y2, dX2)
@@ -345,7 +365,7 @@ def main():
     # search: from the previous step's last GEMM (or the start) to the end of
     # the search; GEMMs: the four calls of each step
     sc_ms = float(np.mean([(start if k == 0 else tev[k - 1][5]).elapsed_time(tev[k][1]) for k in range(args.steps)]))
-    gemm_call_ms = float(np.mean([tev[k][1].elapsed_time(tev[k][5]) for k in range(args.steps)])) / 4
+    group_ms = float(np.mean([tev[k][1].elapsed_time(tev[k][5]) for k in range(args.steps)]))
 
     # per-GEMM breakdown: the same steps again with events between every
     # call, all enqueued before a single synchronisation so that host-side
@@ -355,7 +375,7 @@ def main():
         evs = []
         for s in range(args.warmup, nsteps):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-            step(s, ev, FLb)
+            step_single(s, ev, FLb)
             evs.append(ev)
         torch.cuda.synchronize()
         seg = np.zeros(5)
@@ -370,9 +390,9 @@ def main():
     sc_gbps = sc_bytes / (sc_ms * 1e-3) / 1e9
     gemm_dense_tflops = [2 * Tt * N * K / (ms * 1e-3) / 1e12 for (_, Tt, N, K), ms in zip(gemm_shapes, gemm_ms)]
     # roofline of the GEMM kernel: executed (non-zero) flops T*N*K per launch
-    launch_flops = [Tt * N * K for (_, Tt, N, K) in gemm_shapes]
-    avg_launch_ms = gemm_call_ms
-    achieved = float(np.mean(launch_flops)) / (avg_launch_ms * 1e-3) / 1e12
+    launch_flops = sum(Tt * N * K for (_, Tt, N, K) in gemm_shapes)     # one grouped launch: all four
+    achieved = launch_flops / (group_ms * 1e-3) / 1e12
+    single_achieved = launch_flops / (float(np.sum(gemm_ms)) * 1e-3) / 1e12
     traffic = traffic_from_counters()
 
     flips = FL[args.warmup:].cpu().numpy().astype(np.float64) / np.array([f * d, d * f], dtype=np.float64)
@@ -698,15 +718,20 @@ def main():
         "gemm_us": {n: round(ms * 1e3, 1) for (n, *_), ms in zip(gemm_shapes, gemm_ms)},
         "gemm_us_mean": {n: round(ms * 1e3, 1) for (n, *_), ms in zip(gemm_shapes, gemm_ms_mean)},
         "gemm_breakdown_note": f"gemm_us (median) and gemm_us_mean over {TRIALS} more passes of the same steps with "
-                               "events between every call; gemm_TFLOPs_dense_equiv from the medians; roofline and "
-                               "search_compress from events in the timed region (after each search and after each "
-                               "step's four GEMMs)",
-        "roofline": {"kernel": "spmm_nt (one sp24_spmm_* call)", "bound": "mfma", "achieved": round(achieved, 1),
-                     "launch_us": round(avg_launch_ms * 1e3, 1),
+                               "the four GEMMs as single launches and events between every call; "
+                               "gemm_TFLOPs_dense_equiv from the medians; roofline and search_compress from events in "
+                               "the timed region (after each search and after each step's grouped GEMM launch)",
+        "roofline": {"kernel": "spmm_group_kernel (one sp24_spmm_group launch: the step's four sparse GEMMs)",
+                     "bound": "mfma", "achieved": round(achieved, 1), "launch_us": round(group_ms * 1e3, 1),
+                     "single_launches": {"achieved": round(single_achieved, 1),
+                                         "frac": round(single_achieved / FP16_MFMA_PEAK_TFLOPS, 4),
+                                         "note": "the same four GEMMs as sp24_spmm_fwd / sp24_spmm_bwd_input calls "
+                                                 "(gemm_us)"},
                      "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic,
-                     "note": "executed non-zero flops T*N*K per launch (half the dense-equivalent 2*T*N*K) over the "
-                             "dense fp16 MFMA peak; equal to dense-equivalent flops over the 2:4 sparse peak"},
+                     "note": "executed non-zero flops T*N*K of the four GEMMs per launch (half the dense-equivalent "
+                             "2*T*N*K) over the dense fp16 MFMA peak; equal to dense-equivalent flops over the 2:4 "
+                             "sparse peak"},
         "weight_grad": {"definition": "dW = dY^T X + decay * (1 - M) * W, fp16 in, fp32 out (sp24_weight_grad)",
                         "decay": DECAY, "us": {"dW1": round(wg_ms[0] * 1e3, 1), "dW2": round(wg_ms[1] * 1e3, 1)},
                         "TFLOPs": {"dW1": round(wg_tflops[0], 1), "dW2": round(wg_tflops[1], 1)},

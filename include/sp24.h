@@ -244,6 +244,47 @@ int sp24_spmm_bwd_input(const void* dY, const void* vals_col, const uint16_t* me
                         int64_t T, int64_t R, int64_t C, void* dX, void* stream);
 
 /*
+ * Several independent 2:4 sparse GEMMs in one launch [Abstract, SW]: for
+ * each entry g of gemms[0..count),
+ *     out[T][N] = A[T][K] * S^T,
+ * S the [N, K] matrix whose 2:4 row form (groups of 4 along K) is
+ * (vals, meta).  The forward product of a layer is {A = X, (vals, meta) =
+ * its row form, N = R, K = C}; its input gradient is {A = dY, (vals, meta) =
+ * its column form, N = C, K = R}.  Each output equals the corresponding
+ * sp24_spmm_fwd / sp24_spmm_bwd_input result bit for bit.
+ * One persistent launch serves every product whose K is a multiple of 64
+ * and at least 192 (and whose operands each stay below 2 GiB): its
+ * workgroups take 256 x 256 output tiles from per-XCD queues, the
+ * products with the longest K first, so the tiles of all products share
+ * the GPU without a partly filled last round per product.  Other products
+ * run as single launches before it.
+ *
+ *   gemms     in   host array of `count` descriptors (1..SP24_MAX_GROUP)
+ *   workspace in   device memory of SP24_GROUP_WORKSPACE_BYTES bytes that
+ *                  must be all zero before the first call (e.g. from
+ *                  hipMemset); every call that completes leaves it all zero
+ *                  again.  Calls that overlap in time must use different
+ *                  workspaces.
+ * The products must be independent: no output may overlap any input or
+ * another output.  Per product: N, K multiples of 16, T >= 0, the buffers as
+ * for sp24_spmm_fwd; an empty product (T or N zero) is skipped.
+ * Errors: NULL, SHAPE (also count outside 1..SP24_MAX_GROUP), ALIGN,
+ * TOO_LARGE, LAUNCH.
+ */
+typedef struct sp24_gemm {
+  const void* A;           /* fp16 [T, K] */
+  const void* vals;        /* fp16 [N, K/2] */
+  const uint16_t* meta;    /* uint16 [N, K/16] */
+  void* out;               /* fp16 [T, N] */
+  int64_t T, N, K;
+} sp24_gemm;
+
+#define SP24_MAX_GROUP 8
+#define SP24_GROUP_WORKSPACE_BYTES 64
+
+int sp24_spmm_group(const sp24_gemm* gemms, int count, void* workspace, void* stream);
+
+/*
  * Weight gradient of a 2:4 FFN linear layer with the masked decay term
  * [Decay]:
  *     dW[r][c] = sum_t dY[t][r] * X[t][c]  +  decay * (1 - M[r][c]) * W[r][c]
@@ -349,7 +390,7 @@ const char* sp24_status_str(int status);
  */
 int sp24_pattern_table(uint16_t* out);
 
-/* Host only: the library's ABI version (6 for this header). */
+/* Host only: the library's ABI version (7 for this header). */
 int sp24_abi_version(void);
 
 #ifdef __cplusplus

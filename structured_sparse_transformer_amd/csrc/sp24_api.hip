@@ -64,8 +64,8 @@ int compress_common(const void* W, const uint8_t* idx_in, uint8_t* idx_out, int6
       static_cast<uint16_t*>(vals_col), meta_col, as_stream(stream)));
 }
 
-int spmm_common(const void* A, const void* vals, const uint16_t* meta, int64_t T, int64_t N, int64_t K, void* out,
-                void* stream) {
+int check_spmm(const void* A, const void* vals, const uint16_t* meta, int64_t T, int64_t N, int64_t K,
+               const void* out) {
   if (T < 0) return SP24_ERR_SHAPE;
   int st = check_dims(N, K, 16);
   if (st != SP24_OK) return st;
@@ -74,6 +74,13 @@ int spmm_common(const void* A, const void* vals, const uint16_t* meta, int64_t T
   if (T == 0 || N == 0) return SP24_OK;
   if (out == nullptr || (K != 0 && (A == nullptr || vals == nullptr || meta == nullptr))) return SP24_ERR_NULL;
   if (!aligned16(out) || (K != 0 && (!aligned16(A) || !aligned16(vals) || !aligned16(meta)))) return SP24_ERR_ALIGN;
+  return SP24_OK;
+}
+
+int spmm_common(const void* A, const void* vals, const uint16_t* meta, int64_t T, int64_t N, int64_t K, void* out,
+                void* stream) {
+  const int st = check_spmm(A, vals, meta, T, N, K, out);
+  if (st != SP24_OK || T == 0 || N == 0) return st;
   return launch_status(sp24::launch_spmm_nt(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(vals), meta,
                                             T, N, K, static_cast<uint16_t*>(out), as_stream(stream)));
 }
@@ -169,6 +176,23 @@ int sp24_spmm_fwd_geglu(const void* X, const void* vals_row, const uint16_t* met
   return launch_status(e);
 }
 
+int sp24_spmm_group(const sp24_gemm* gemms, int count, void* workspace, void* stream) {
+  if (gemms == nullptr) return SP24_ERR_NULL;
+  if (count < 1 || count > SP24_MAX_GROUP) return SP24_ERR_SHAPE;
+  static_assert(SP24_MAX_GROUP <= 8, "the launcher's job table holds 8 products");
+  sp24::GemmDesc d[SP24_MAX_GROUP];
+  for (int j = 0; j < count; ++j) {
+    const sp24_gemm& g = gemms[j];
+    const int st = check_spmm(g.A, g.vals, g.meta, g.T, g.N, g.K, g.out);
+    if (st != SP24_OK) return st;
+    d[j] = {static_cast<const uint16_t*>(g.A), static_cast<const uint16_t*>(g.vals), g.meta,
+            static_cast<uint16_t*>(g.out), g.T, g.N, g.K};
+  }
+  if (workspace == nullptr) return SP24_ERR_NULL;
+  if (!aligned16(workspace)) return SP24_ERR_ALIGN;
+  return launch_status(sp24::launch_spmm_group(d, count, static_cast<unsigned int*>(workspace), as_stream(stream)));
+}
+
 int sp24_spmm_bwd_input(const void* dY, const void* vals_col, const uint16_t* meta_col, int64_t T, int64_t R,
                         int64_t C, void* dX, void* stream) {
   // dX[T][C] = dY[T][R] * Ws: output features C, reduction over R
@@ -242,6 +266,6 @@ int sp24_pattern_table(uint16_t* out) {
   return SP24_OK;
 }
 
-int sp24_abi_version(void) { return 6; }
+int sp24_abi_version(void) { return 7; }
 
 }  // extern "C"

@@ -75,4 +75,17 @@ hipError_t launch_spmm_nt(const uint16_t* A, const uint16_t* vals, const uint16_
 hipError_t launch_spmm_nt_geglu(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T,
                                 int64_t N, int64_t K, uint16_t* out, uint16_t* gout, hipStream_t s);
 
+// One product of a grouped launch: out[T][N] = A[T][K] * S[N][K]^T.
+struct GemmDesc {
+  const uint16_t* A;
+  const uint16_t* vals;
+  const uint16_t* meta;
+  uint16_t* out;
+  int64_t T, N, K;
+};
+// Independent products in one persistent launch (fast-path shapes with
+// K >= 192; the others run as single launches first).  work: 16 uint32 of
+// device memory, zero on entry; a completed launch leaves them zero.
+hipError_t launch_spmm_group(const GemmDesc* jobs, int count, unsigned int* work, hipStream_t s);
+
 }  // namespace sp24

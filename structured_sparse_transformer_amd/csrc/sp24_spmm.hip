@@ -27,6 +27,7 @@
 // and not stored; K beyond the end (K is a multiple of 16) is zero-filled.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 
@@ -282,41 +283,20 @@ struct FastCfg {
   static_assert(LOADS <= 63, "vmcnt range");
 };
 
-// kGeglu: the feature rows of S come in blocks of 32, 16 value rows then the
-// 16 matching gate rows, and the epilogue also writes gout[T][ldg] columns
-// [0, N/2) = value * GELU(gate) from the fp16-rounded products, with the
-// GEGLU kernel's GELU code.  `out` may then be null (the products are not
-// stored).
+// One BM x BN output tile at tile coordinates (tm, tn), computed by the
+// whole workgroup with the ring in `smem`.  When `post` is set, thread 0
+// stores `post_val` to *post_dst once the K loop is done, before the
+// epilogue's stores (the grouped kernel hands its next tile index over
+// there, while no load of this tile is still in flight).
 template <int BM, int BN, int WM, int WN, bool kGeglu>
-__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ vals, const uint16_t* __restrict__ meta,
-    int64_t T, int64_t N, int64_t K, uint16_t* __restrict__ out, int64_t ldo, uint16_t* __restrict__ gout,
-    int64_t ldg, int tiles_m, int tiles_n) {
+__device__ __forceinline__ void spmm_fast_tile(unsigned char* __restrict__ smem, const uint16_t* __restrict__ A,
+                                               const uint16_t* __restrict__ vals, const uint16_t* __restrict__ meta,
+                                               int64_t T, int64_t N, int64_t K, uint16_t* __restrict__ out,
+                                               int64_t ldo, uint16_t* __restrict__ gout, int64_t ldg, int tm, int tn,
+                                               int tid, bool post, int* post_dst, int post_val) {
   using Cfg = FastCfg<BM, BN, WM, WN>;
-  // one LDS block: 3 S slots, 3 B slots, 3 meta slots (the epilogue reuses
-  // the start of it to stage the output tile)
-  __shared__ __align__(1024) unsigned char smem[3 * (Cfg::S_BYTES + Cfg::B_BYTES + Cfg::M_BYTES)];
-
-  // tile order: groups of kGroupM feature tiles, token tiles within a group,
-  // features fastest; each XCD (workgroups are dealt round-robin to 8 XCDs)
-  // takes a contiguous run of that order so concurrent tiles share operands in
-  // its L2
-  constexpr int kGroupM = 8;
-  const int ntiles = tiles_m * tiles_n;
-  const int per_xcd = (ntiles + 7) / 8;
-  const int lin = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (lin >= ntiles) return;
-  const int group = lin / (kGroupM * tiles_n);
-  const int gm0 = group * kGroupM;
-  const int gsize = min(kGroupM, tiles_m - gm0);
-  const int in_group = lin - group * kGroupM * tiles_n;
-  // the tile indices are uniform; readfirstlane keeps them (and the buffer
-  // descriptors built from them) in scalar registers
-  const int tn = __builtin_amdgcn_readfirstlane(in_group / gsize);
-  const int tm = __builtin_amdgcn_readfirstlane(gm0 + in_group % gsize);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  const int tid = threadIdx.x;
   // the wave index is uniform across the wave; say so, since the direct
   // loads take their LDS destination from a scalar register
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -514,6 +494,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
   // and the barrier makes sure no wave still reads its last fragments.
   static_assert(Cfg::WAVES * WN * WM * 2 <= 3 * (Cfg::S_BYTES + Cfg::B_BYTES), "staging does not fit");
   static_assert(WM == 128, "epilogue assumes 16 chunks of 8 features per token row");
+  if (post && tid == 0) *post_dst = post_val;
   __builtin_amdgcn_s_barrier();
   unsigned char* stage_base = smem + (size_t)wave * WN * WM * 2;
   auto h2 = [](float x, float y) {
@@ -616,6 +597,151 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_ke
   }
 }
 
+// kGeglu: the feature rows of S come in blocks of 32, 16 value rows then the
+// 16 matching gate rows, and the epilogue also writes gout[T][ldg] columns
+// [0, N/2) = value * GELU(gate) from the fp16-rounded products, with the
+// GEGLU kernel's GELU code.  `out` may then be null (the products are not
+// stored).
+template <int BM, int BN, int WM, int WN, bool kGeglu>
+__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_nt_fast_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ vals, const uint16_t* __restrict__ meta,
+    int64_t T, int64_t N, int64_t K, uint16_t* __restrict__ out, int64_t ldo, uint16_t* __restrict__ gout,
+    int64_t ldg, int tiles_m, int tiles_n) {
+  using Cfg = FastCfg<BM, BN, WM, WN>;
+  // one LDS block: 3 S slots, 3 B slots, 3 meta slots (the epilogue reuses
+  // the start of it to stage the output tile)
+  __shared__ __align__(1024) unsigned char smem[3 * (Cfg::S_BYTES + Cfg::B_BYTES + Cfg::M_BYTES)];
+
+  // tile order: groups of kGroupM feature tiles, token tiles within a group,
+  // features fastest; each XCD (workgroups are dealt round-robin to 8 XCDs)
+  // takes a contiguous run of that order so concurrent tiles share operands in
+  // its L2
+  constexpr int kGroupM = 8;
+  const int ntiles = tiles_m * tiles_n;
+  const int per_xcd = (ntiles + 7) / 8;
+  const int lin = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (lin >= ntiles) return;
+  const int group = lin / (kGroupM * tiles_n);
+  const int gm0 = group * kGroupM;
+  const int gsize = min(kGroupM, tiles_m - gm0);
+  const int in_group = lin - group * kGroupM * tiles_n;
+  // the tile indices are uniform; readfirstlane keeps them (and the buffer
+  // descriptors built from them) in scalar registers
+  const int tn = __builtin_amdgcn_readfirstlane(in_group / gsize);
+  const int tm = __builtin_amdgcn_readfirstlane(gm0 + in_group % gsize);
+  spmm_fast_tile<BM, BN, WM, WN, kGeglu>(smem, A, vals, meta, T, N, K, out, ldo, gout, ldg, tm, tn,
+                                         (int)threadIdx.x, false, nullptr, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped launch: several independent fast-path GEMMs (the forward and
+// input-gradient products of both FFN linears, say) in one persistent launch.
+//
+// One workgroup per CU loops over tiles.  The tiles of every job are split
+// into 8 contiguous runs of the single launch's tile order (groups of 8
+// feature tiles, token tiles within a group, features fastest), one per XCD,
+// and queue x lists run x of each job, jobs in the order given (the host puts
+// the longest reductions first).  Workgroup b serves queue b % 8 (the XCD it
+// is dispatched to), taking the next tile with one atomic increment, so the
+// concurrent tiles of an XCD share operand strips in its L2, and tiles of
+// different lengths pack the CUs with no partial round per GEMM.  Each
+// workgroup takes its next tile index while the current tile runs and hands
+// it over in LDS once the tile's K loop is done.
+//
+// work[0..7] are the queue heads and work[8..15] count the workgroups that
+// found their queue empty; the last one of a queue sets both back to zero,
+// so a launch that runs to completion leaves the workspace as it found it
+// (all zero).
+constexpr int kMaxGroupJobs = 8;
+struct GroupJob {
+  const uint16_t* A;
+  const uint16_t* vals;
+  const uint16_t* meta;
+  uint16_t* out;
+  int64_t T, N, K;
+  int tiles_m, tiles_n;
+};
+struct GroupArgs {
+  GroupJob job[kMaxGroupJobs];
+  int njobs;
+  int lo[8][kMaxGroupJobs];    // first position of queue x's run in job j's tile order
+  int cnt[8][kMaxGroupJobs];   // tiles of job j in queue x
+  int total[8];                // tiles in queue x
+  int wgs[8];                  // workgroups serving queue x
+};
+
+// LDS-only workgroup barrier: this wave's LDS accesses are complete, and the
+// compiler moves no memory access across it (no wait for global stores).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_group_kernel(GroupArgs args,
+                                                                                   unsigned int* __restrict__ work) {
+  using Cfg = FastCfg<BM, BN, WM, WN>;
+  __shared__ __align__(1024) unsigned char smem[3 * (Cfg::S_BYTES + Cfg::B_BYTES + Cfg::M_BYTES)];
+  __shared__ int sh_next;
+  constexpr int kGroupM = 8;
+  const int x = (int)(blockIdx.x % 8);
+  unsigned int* const queue = work + x;
+  unsigned int* const done = work + 8 + x;
+  const int total = args.total[x];
+  if (threadIdx.x == 0) sh_next = (int)atomicAdd(queue, 1u);
+  lds_barrier();
+  int cur = __builtin_amdgcn_readfirstlane(sh_next);
+  while (cur < total) {
+    // the tile after this one, taken now and handed over after the K loop
+    int nxt = 0;
+    if (threadIdx.x == 0) {
+      // the address goes through a vector register, so the compiler cannot
+      // turn this into a wave-aggregated atomic whose result it waits for at
+      // once: the value is first needed after the K loop
+      typedef __attribute__((address_space(1))) unsigned int global_u32;
+      global_u32* q = (global_u32*)queue;
+      asm volatile("" : "+v"(q));
+      nxt = (int)__hip_atomic_fetch_add(q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    int j = 0, i = cur;
+    while (j + 1 < args.njobs && i >= args.cnt[x][j]) {
+      i -= args.cnt[x][j];
+      ++j;
+    }
+    const GroupJob& jb = args.job[j];
+    const int tiles_m = jb.tiles_m, tiles_n = jb.tiles_n;
+    const int lin = args.lo[x][j] + i;
+    const int group = lin / (kGroupM * tiles_n);
+    const int gm0 = group * kGroupM;
+    const int gsize = min(kGroupM, tiles_m - gm0);
+    const int in_group = lin - group * kGroupM * tiles_n;
+    const int tn = __builtin_amdgcn_readfirstlane(in_group / gsize);
+    const int tm = __builtin_amdgcn_readfirstlane(gm0 + in_group % gsize);
+    // the thread index through an opaque copy, so that the tile's per-lane
+    // offsets are recomputed for every tile rather than hoisted out of this
+    // loop (held across it they would not fit in the registers)
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    spmm_fast_tile<BM, BN, WM, WN, false>(smem, jb.A, jb.vals, jb.meta, jb.T, jb.N, jb.K, jb.out, jb.N, nullptr, 0,
+                                          tm, tn, tid, true, &sh_next, nxt);
+    // every wave has read back its staged outputs (the ring is free for the
+    // next tile's loads) and the next index is visible
+    lds_barrier();
+    cur = __builtin_amdgcn_readfirstlane(sh_next);
+  }
+  if (threadIdx.x == 0) {
+    // this workgroup's last increment of the queue has returned (its value
+    // ended the loop); the last workgroup of the queue resets it
+    const unsigned int d = atomicAdd(done, 1u);
+    if (d == (unsigned int)args.wgs[x] - 1u) {
+      atomicExch(queue, 0u);
+      atomicExch(done, 0u);
+    }
+  }
+}
+
 // out[T][ldo] columns [0, N) = A * S^T for the N feature rows of S given;
 // with kGeglu also gout[T][ldg] columns [0, N/2).
 template <int BM, int BN, int WM, int WN, bool kGeglu = false>
@@ -708,6 +834,66 @@ hipError_t launch_spmm_nt_geglu(const uint16_t* A, const uint16_t* vals, const u
     return launch_fast<256, 64, 128, 32, true>(A, v2, m2, T, N - n1, K, o2, N, s, gout + n1 / 2, N / 2);
   }
   return launch_fast<256, 256, 128, 64, true>(A, vals, meta, T, N, K, out, N, s, gout, N / 2);
+}
+
+hipError_t launch_spmm_group(const GemmDesc* jobs, int count, unsigned int* work, hipStream_t s) {
+  // jobs the fast kernel cannot take run as single launches first
+  GroupArgs args{};
+  int order[kMaxGroupJobs];
+  int n = 0;
+  for (int j = 0; j < count; ++j) {
+    const GemmDesc& g = jobs[j];
+    if (g.T == 0 || g.N == 0) continue;
+    if (!fast_path(g.T, g.N, g.K) || g.K < 3 * 64 || n == kMaxGroupJobs) {
+      const hipError_t e = launch_spmm_nt(g.A, g.vals, g.meta, g.T, g.N, g.K, g.out, s);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    order[n++] = j;
+  }
+  if (n == 0) return hipSuccess;
+  // longest reductions first: their tiles take the most time, and the short
+  // ones then fill in behind them
+  for (int a = 1; a < n; ++a)
+    for (int b = a; b > 0 && jobs[order[b]].K > jobs[order[b - 1]].K; --b) {
+      const int t = order[b];
+      order[b] = order[b - 1];
+      order[b - 1] = t;
+    }
+  int64_t all_tiles = 0;
+  args.njobs = n;
+  for (int q = 0; q < n; ++q) {
+    const GemmDesc& g = jobs[order[q]];
+    GroupJob& jb = args.job[q];
+    jb.A = g.A;
+    jb.vals = g.vals;
+    jb.meta = g.meta;
+    jb.out = g.out;
+    jb.T = g.T;
+    jb.N = g.N;
+    jb.K = g.K;
+    jb.tiles_m = (int)((g.N + 255) / 256);
+    jb.tiles_n = (int)((g.T + 255) / 256);
+    const int64_t ntiles = (int64_t)jb.tiles_m * jb.tiles_n;
+    all_tiles += ntiles;
+    for (int x = 0; x < 8; ++x) {
+      const int64_t lo = x * ntiles / 8, hi = (x + 1) * ntiles / 8;
+      args.lo[x][q] = (int)lo;
+      args.cnt[x][q] = (int)(hi - lo);
+      args.total[x] += (int)(hi - lo);
+    }
+  }
+  // one workgroup per CU (the ring takes 150 KB of LDS), a multiple of 8 so
+  // every queue has the same number of workgroups, and no more than there
+  // are tiles
+  int64_t grid = device_cu_count();
+  grid = std::min<int64_t>(grid, (all_tiles + 7) / 8 * 8);
+  grid = std::max<int64_t>(8, grid / 8 * 8);
+  for (int x = 0; x < 8; ++x) args.wgs[x] = (int)(grid / 8);
+  using Cfg = FastCfg<256, 256, 128, 64>;
+  hipLaunchKernelGGL((spmm_group_kernel<256, 256, 128, 64>), dim3((unsigned)grid), dim3(Cfg::THREADS), 0, s, args,
+                     work);
+  return hipGetLastError();
 }
 
 }  // namespace sp24

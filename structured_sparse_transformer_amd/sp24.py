@@ -26,9 +26,11 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_
                 5: "ERR_UNSUPPORTED", 6: "ERR_TOO_LARGE"}
 EXPORTS = ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
            "sp24_flip_count", "sp24_weight_grad", "sp24_geglu_fwd", "sp24_geglu_bwd", "sp24_mvue",
-           "sp24_spmm_fwd", "sp24_spmm_fwd_geglu", "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table",
-           "sp24_abi_version")
+           "sp24_spmm_fwd", "sp24_spmm_fwd_geglu", "sp24_spmm_bwd_input", "sp24_spmm_group", "sp24_status_str",
+           "sp24_pattern_table", "sp24_abi_version")
 MAX_BATCH = 8
+MAX_GROUP = 8
+GROUP_WORKSPACE_BYTES = 64
 
 
 class ScJob(ctypes.Structure):
@@ -37,6 +39,12 @@ class ScJob(ctypes.Structure):
                 ("vals_row", ctypes.c_void_p), ("meta_row", ctypes.c_void_p),
                 ("vals_col", ctypes.c_void_p), ("meta_col", ctypes.c_void_p),
                 ("idx_prev", ctypes.c_void_p), ("flips", ctypes.c_void_p)]
+
+
+class Gemm(ctypes.Structure):
+    """Mirror of sp24_gemm (include/sp24.h)."""
+    _fields_ = [("A", ctypes.c_void_p), ("vals", ctypes.c_void_p), ("meta", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("T", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
 class Sp24Error(RuntimeError):
@@ -69,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "sp24_spmm_fwd": [p, p, p, i64, i64, i64, p, p],
             "sp24_spmm_fwd_geglu": [p, p, p, i64, i64, i64, p, p, p],
             "sp24_spmm_bwd_input": [p, p, p, i64, i64, i64, p, p],
+            "sp24_spmm_group": [p, i32, p, p],
             "sp24_status_str": [i32],
             "sp24_pattern_table": [p],
             "sp24_abi_version": [],
@@ -343,3 +352,49 @@ def sp24_pattern_table():
     buf = (ctypes.c_uint16 * 90)()
     _check("sp24_pattern_table", lib().sp24_pattern_table(ctypes.cast(buf, ctypes.c_void_p)))
     return list(buf)
+
+
+_group_ws = {}
+
+
+def group_workspace(device=None):
+    """The binding's workspace for sp24_spmm_group on a device: zeroed once,
+    and left zero by every call that completes.  Calls that overlap in time
+    (on different streams) must pass workspaces of their own."""
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else torch.device(device).index)
+    ws = _group_ws.get(dev.index)
+    if ws is None:
+        ws = torch.zeros(GROUP_WORKSPACE_BYTES // 4, dtype=torch.int32, device=dev)
+        _group_ws[dev.index] = ws
+    return ws
+
+
+def sp24_spmm_group(gemms, workspace=None, stream=None):
+    """Several independent products out = A * S^T in one launch.
+
+    ``gemms`` is a list of (A, vals, meta, out) with A fp16 [T, K], (vals,
+    meta) the 2:4 row form of S [N, K] (fp16 [N, K/2], int16 [N, K/16]) and
+    out fp16 [T, N] or None (allocated).  The forward product of a layer is
+    (X, vals_row, meta_row, Y); its input gradient (dY, vals_col, meta_col,
+    dX).  Returns the outputs."""
+    if not 1 <= len(gemms) <= MAX_GROUP:
+        raise ValueError(f"between 1 and {MAX_GROUP} products per group")
+    descs, outs = (Gemm * len(gemms))(), []
+    for k, (A, vals, meta, out) in enumerate(gemms):
+        if A.dtype != torch.float16 or A.dim() != 2:
+            raise ValueError("A must be a 2-D float16 tensor")
+        T, K = A.shape
+        if vals.dim() != 2:
+            raise ValueError("vals must be 2-D")
+        N = vals.shape[0]
+        _row_form(vals, meta, N, K, f"product {k}")
+        out = _out(out, (T, N), torch.float16, A.device)
+        outs.append(out)
+        ptr = lambda t: _ptr(t).value if t is not None and t.numel() else None  # noqa: E731
+        descs[k] = Gemm(ptr(A), ptr(vals), ptr(meta), ptr(out), T, N, K)
+    ws = group_workspace() if workspace is None else workspace
+    if ws.numel() * ws.element_size() < GROUP_WORKSPACE_BYTES:
+        raise ValueError(f"the workspace needs {GROUP_WORKSPACE_BYTES} bytes")
+    _check("sp24_spmm_group", lib().sp24_spmm_group(ctypes.cast(descs, ctypes.c_void_p), len(gemms), _ptr(ws),
+                                                    _stream(stream)))
+    return outs

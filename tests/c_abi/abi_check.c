@@ -27,7 +27,7 @@ int main(void) {
   unsigned key[90];
   int p, ones, r, c;
 
-  CHECK(sp24_abi_version() == 6);
+  CHECK(sp24_abi_version() == 7);
   CHECK(sp24_pattern_table(NULL) == SP24_ERR_NULL);
   CHECK(sp24_pattern_table(table) == SP24_OK);
   /* every pattern keeps two entries in each row and each column */
@@ -77,6 +77,23 @@ int main(void) {
     job.idx_prev = (const uint8_t*)fake;   /* without a counter */
     CHECK(sp24_search_compress_batch(&job, 1, NULL) == SP24_ERR_NULL);
     CHECK(sp24_search_compress_batch(&job, 0, NULL) == SP24_ERR_SHAPE);
+  }
+  {
+    sp24_gemm g[2];
+    memset(g, 0, sizeof(g));
+    g[0].A = fake;
+    g[0].vals = fake;
+    g[0].meta = (const uint16_t*)fake;
+    g[0].out = fake;
+    g[0].T = 300;
+    g[0].N = 256;
+    g[0].K = 1600;
+    g[1] = g[0];
+    g[1].K = 20;   /* not a multiple of 16 */
+    CHECK(sp24_spmm_group(g, 2, fake, NULL) == SP24_ERR_SHAPE);
+    CHECK(sp24_spmm_group(g, 1, NULL, NULL) == SP24_ERR_NULL);
+    CHECK(sp24_spmm_group(g, SP24_MAX_GROUP + 1, fake, NULL) == SP24_ERR_SHAPE);
+    CHECK(SP24_GROUP_WORKSPACE_BYTES >= 64);
   }
   if (failures == 0) printf("ok\n");
   return failures == 0 ? 0 : 1;

@@ -40,7 +40,8 @@ def test_header_declares_the_entry_points():
     for n in ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
               "sp24_flip_count", "sp24_weight_grad", "sp24_geglu_fwd", "sp24_geglu_bwd", "sp24_mvue",
               "sp24_spmm_fwd", "sp24_spmm_fwd_geglu",
-              "sp24_spmm_bwd_input", "sp24_status_str", "sp24_pattern_table", "sp24_abi_version"):
+              "sp24_spmm_bwd_input", "sp24_spmm_group", "sp24_status_str", "sp24_pattern_table",
+              "sp24_abi_version"):
         assert n in names
 
 
@@ -59,7 +60,7 @@ def test_pattern_table_matches_oracle(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sp24_abi_version() == 6
+    assert L.sp24_abi_version() == 7
     for s in range(7):
         assert L.sp24_status_str(s)
     assert L.sp24_status_str(99) == b"unknown status"
@@ -245,6 +246,31 @@ def test_spmm_fwd_geglu_validation(L):
     # T * R/16 work-items of the GEGLU kernel that finishes unfused shapes
     assert f(FAKE, FAKE, FAKE, 1 << 20, 1 << 16, 16, NUL, FAKE, NUL) == 6
     assert f(FAKE, FAKE, FAKE, 1 << 20, (1 << 16) - 32, 16, NUL, MIS, NUL) == 3
+
+
+def test_spmm_group_validation(L):
+    from structured_sparse_transformer_amd.sp24 import Gemm
+    f = L.sp24_spmm_group
+
+    def arr(*gs):
+        a = (Gemm * len(gs))()
+        for k, g in enumerate(gs):
+            a[k] = g
+        return ctypes.cast(a, ctypes.c_void_p)
+
+    ok = Gemm(0x1000, 0x1000, 0x1000, 0x1000, 300, 256, 1600)
+    assert f(None, 1, FAKE, NUL) == 1
+    assert f(arr(ok), 0, FAKE, NUL) == 2                                    # count outside 1..8
+    assert f(arr(*([ok] * 9)), 9, FAKE, NUL) == 2
+    assert f(arr(ok), 1, NUL, NUL) == 1                                     # no workspace
+    assert f(arr(ok), 1, MIS, NUL) == 3
+    assert f(arr(ok, Gemm(0x1000, 0x1000, 0x1000, 0x1000, 300, 250, 1600)), 2, FAKE, NUL) == 2   # N % 16
+    assert f(arr(ok, Gemm(0x1000, 0x1000, 0x1000, 0x1000, -1, 256, 64)), 2, FAKE, NUL) == 2
+    assert f(arr(ok, Gemm(0x1000, 0, 0x1000, 0x1000, 300, 256, 64)), 2, FAKE, NUL) == 1
+    assert f(arr(ok, Gemm(0x1000, 0x1000, 0x1000, 0x1008, 300, 256, 64)), 2, FAKE, NUL) == 3
+    assert f(arr(ok, Gemm(0x1000, 0x1000, 0x1000, 0x1000, 1 << 31, 16, 16)), 2, FAKE, NUL) == 6
+    # every product is checked before anything is launched; empty products need no buffers
+    assert f(arr(Gemm(0, 0, 0, 0, 0, 256, 64), Gemm(0, 0, 0, 0, 16, 0, 64)), 2, FAKE, NUL) == 0
 
 
 def test_ffn_layer_rejects_bad_shapes():
