@@ -494,7 +494,13 @@ __device__ __forceinline__ void spmm_fast_tile(unsigned char* __restrict__ smem,
   // and the barrier makes sure no wave still reads its last fragments.
   static_assert(Cfg::WAVES * WN * WM * 2 <= 3 * (Cfg::S_BYTES + Cfg::B_BYTES), "staging does not fit");
   static_assert(WM == 128, "epilogue assumes 16 chunks of 8 features per token row");
-  if (post && tid == 0) *post_dst = post_val;
+  if (post) {
+    // every wave takes the value through readfirstlane (wave 0 gets thread
+    // 0's), so the wait for it is not on a divergent path and nothing is
+    // left pending for the next tile's first instructions
+    const int v = __builtin_amdgcn_readfirstlane(post_val);
+    if (tid == 0) *post_dst = v;
+  }
   __builtin_amdgcn_s_barrier();
   unsigned char* stage_base = smem + (size_t)wave * WN * WM * 2;
   auto h2 = [](float x, float y) {
@@ -695,7 +701,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void spmm_group_kern
   int cur = __builtin_amdgcn_readfirstlane(sh_next);
   while (cur < total) {
     // the tile after this one, taken now and handed over after the K loop
-    int nxt = 0;
+    int nxt;   // only thread 0's value is used; no initialisation to wait behind
     if (threadIdx.x == 0) {
       // the address goes through a vector register, so the compiler cannot
       // turn this into a wave-aggregated atomic whose result it waits for at
