@@ -1,0 +1,375 @@
+"""Host model of the kernels' address arithmetic (CPU only, no kernel runs).
+
+For every shape the GPU tests and the benchmark use, the index formulas of
+the HIP kernels are replayed here in numpy, and the test checks that:
+
+* every tile of a launch is visited exactly once (the workgroup -> tile maps,
+  the tail split and the grouped launch's per-XCD queues);
+* every output element is written exactly once, and only inside its buffer
+  (the epilogues' lane -> element maps with their bounds checks);
+* every direct-load offset fits the 32-bit signed arithmetic the kernels form
+  it in, and each buffer descriptor's base and byte range lie inside the
+  operand it reads (rows past the end then read as zero, by design).
+
+The formulas are transcribed from the sources named in each function
+(structured_sparse_transformer_amd/csrc); a change to a kernel's indexing has
+to be mirrored here.  The device is modelled with 256 CUs.
+"""
+import numpy as np
+import pytest
+
+from structured_sparse_transformer_amd import workloads as WL
+
+CUS = 256
+I32 = 2 ** 31
+U32 = 2 ** 32
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+# ----------------------------------------------------------------------------
+# workgroup -> tile maps
+
+def xcd_run_map(ntiles, grid):
+    """blockIdx -> linear tile of the single launches (sp24_spmm.hip,
+    sp24_dw.hip): XCD b % 8 walks a contiguous run of the tile order."""
+    per_xcd = cdiv(ntiles, 8)
+    b = np.arange(grid)
+    lin = (b % 8) * per_xcd + b // 8
+    return lin[lin < ntiles]
+
+
+def group_order(lin, tiles_m, tiles_n, group_m=8):
+    """Linear position -> (tm, tn): groups of 8 row tiles, column tiles within
+    a group, rows fastest."""
+    group = lin // (group_m * tiles_n)
+    gm0 = group * group_m
+    gsize = np.minimum(group_m, tiles_m - gm0)
+    in_group = lin - group * group_m * tiles_n
+    return gm0 + in_group % gsize, in_group // gsize
+
+
+def check_tile_map(tiles_m, tiles_n):
+    grid = cdiv(tiles_m * tiles_n, 8) * 8
+    tm, tn = group_order(xcd_run_map(tiles_m * tiles_n, grid), tiles_m, tiles_n)
+    seen = np.zeros((tiles_m, tiles_n), np.int64)
+    np.add.at(seen, (tm, tn), 1)
+    assert (seen == 1).all(), "a tile is missed or visited twice"
+    return tm, tn
+
+
+# ----------------------------------------------------------------------------
+# sparse GEMM (sp24_spmm.hip)
+
+def fast_path(T, N, K):
+    return K % 64 == 0 and K > 0 and K * 512 < I32 and T * K * 2 < I32 and N * K < I32 and T * N * 2 < 2 ** 40
+
+
+def tail_tiles(T, w):
+    return 2 * cdiv(T, 128) if w > 128 else cdiv(T, 64)
+
+
+def split_features(T, N):
+    tiles_n, tiles_m = cdiv(T, 256), cdiv(N, 256)
+    if tiles_m < 2 or (tiles_m * tiles_n) % CUS == 0 or ((tiles_m - 1) * tiles_n) % CUS != 0:
+        return 0
+    n1 = (tiles_m - 1) * 256
+    return n1 if tail_tiles(T, N - n1) <= CUS else 0
+
+
+def fast_launches(T, N, K):
+    """launch_spmm_nt's fast-path launches: (BM, BN, WM, WN, first feature, features)."""
+    n1 = split_features(T, N)
+    if n1 == 0:
+        return [(256, 256, 128, 64, 0, N)]
+    tail = (128, 128, 128, 32) if N - n1 > 128 else (256, 64, 128, 32)
+    return [(256, 256, 128, 64, 0, n1), tail + (n1, N - n1)]
+
+
+def swz_s(r):
+    return ((r >> 1) ^ (r >> 2)) & 3
+
+
+def swz_b(r):
+    return (r & 7) ^ ((r >> 3) & 1)
+
+
+def fast_tile_writes(BM, BN, WM, WN):
+    """(token, feature) of every 16-byte store of spmm_fast_tile's epilogue,
+    relative to the tile: lane t of wave (wm, wn) writes row t/16 + 4 it,
+    chunk t % 16 (8 features), it < WN*16/64."""
+    waves = (BM // WM) * (BN // WN)
+    rows, cols = [], []
+    for wave in range(waves):
+        wm, wn = wave % (BM // WM), wave // (BM // WM)
+        for it in range(WN * 16 // 64):
+            lane = np.arange(64)
+            t, c = it * 4 + lane // 16, lane % 16
+            rows.append(wn * WN + t)
+            cols.append(wm * WM + c * 8)
+    return np.concatenate(rows), np.concatenate(cols)
+
+
+def check_fast_tile_pattern(BM, BN, WM, WN):
+    n, m = fast_tile_writes(BM, BN, WM, WN)
+    assert WM == 128 and (m % 8 == 0).all()
+    cover = np.zeros((BN, BM // 8), np.int64)
+    np.add.at(cover, (n, m // 8), 1)
+    assert (cover == 1).all(), f"the {BM}x{BN} epilogue does not write its tile exactly once"
+    return n, m
+
+
+def check_fast_loads(BM, BN, WM, WN, T, N, K, m0, n0):
+    """Direct-load offsets of one tile (int32 arithmetic) and its descriptors."""
+    waves = (BM // WM) * (BN // WN)
+    Kh, Km, nk = K // 2, K // 16, K // 64
+    s_loads, b_loads, m_loads = BM * 64 // 1024 // waves, BN * 128 // 1024 // waves, BM * 8 // 256 // waves
+    lane = np.arange(64)
+    worst = 0
+    for wave in range(waves):
+        for i in range(s_loads):
+            r = 16 * (wave * s_loads + i) + lane // 4
+            off = r * Kh * 2 + ((lane % 4) ^ swz_s(r)) * 16
+            assert (off >= 0).all()
+            worst = max(worst, int(off.max()) + (nk - 1) * 64)
+        for i in range(b_loads):
+            r = 8 * (wave * b_loads + i) + lane // 8
+            off = r * K * 2 + ((lane % 8) ^ swz_b(r)) * 16
+            worst = max(worst, int(off.max()) + (nk - 1) * 128)
+        for i in range(m_loads):
+            r = 32 * (wave * m_loads + i) + lane // 2
+            worst = max(worst, int((r * Km * 2 + (lane % 2) * 4).max()) + (nk - 1) * 8)
+    assert worst + 16 <= I32, "a direct-load offset overflows 32-bit arithmetic"
+    # descriptors: from this tile's first row to the operand's end
+    for base, rng, total in ((m0 * Kh * 2, (N - m0) * Kh * 2, N * Kh * 2), (n0 * K * 2, (T - n0) * K * 2, T * K * 2),
+                             (m0 * Km * 2, (N - m0) * Km * 2, N * Km * 2)):
+        assert 0 <= base and base + rng == total and 0 < rng < U32
+
+
+def check_spmm(T, N, K):
+    """Every output element of out[T][N] = A S^T written once, in bounds."""
+    if T == 0 or N == 0:
+        return
+    cover = np.zeros((T, N // 8), np.int8)
+    if fast_path(T, N, K):
+        for BM, BN, WM, WN, f0, nf in fast_launches(T, N, K):
+            tiles_m, tiles_n = cdiv(nf, BM), cdiv(T, BN)
+            tm, tn = check_tile_map(tiles_m, tiles_n)
+            n_rel, m_rel = check_fast_tile_pattern(BM, BN, WM, WN)
+            for a, b in zip(tm, tn):
+                m0, n0 = a * BM, b * BN
+                check_fast_loads(BM, BN, WM, WN, T, nf, K, m0, n0)
+                n, m = n0 + n_rel, m0 + m_rel
+                ok = (n < T) & (m < nf)             # the epilogue's bounds check
+                assert (m[ok] + 8 <= nf).all()
+                np.add.at(cover, (n[ok], (f0 + m[ok]) // 8), 1)
+    else:
+        # spmm_nt_kernel (256 x 128 tiles, waves of 128 x 64): lane (l32, g)
+        # of wave (wm, wn) writes 4 features 8 i4 + 4 g of each 32-feature
+        # block mt, token l32 of block nt; rows are clamped on load
+        BM, BN, WM, WN = 256, 128, 128, 64
+        tiles_m, tiles_n = cdiv(N, BM), cdiv(T, BN)
+        tm, tn = check_tile_map(tiles_m, tiles_n)
+        lane = np.arange(64)
+        l32, g = lane & 31, lane >> 5
+        rel_n, rel_m = [], []
+        for wave in range(4):
+            wm, wn = wave % 2, wave // 2
+            for mt in range(WM // 32):
+                for nt in range(WN // 32):
+                    for i4 in range(4):
+                        rel_n.append(wn * WN + nt * 32 + l32)
+                        rel_m.append(wm * WM + mt * 32 + 8 * i4 + 4 * g)
+        rel_n, rel_m = np.concatenate(rel_n), np.concatenate(rel_m)
+        quad = np.zeros((BN, BM // 4), np.int64)
+        np.add.at(quad, (rel_n, rel_m // 4), 1)
+        assert (quad == 1).all()
+        cover4 = np.zeros((T, N // 4), np.int8)
+        for a, b in zip(tm, tn):
+            n, m = b * BN + rel_n, a * BM + rel_m
+            ok = (n < T) & (m < N)
+            assert (m[ok] + 4 <= N).all()
+            np.add.at(cover4, (n[ok], m[ok] // 4), 1)
+        assert (cover4 == 1).all()
+        return
+    assert (cover == 1).all(), "an output element is written twice or not at all"
+
+
+def group_queues(jobs):
+    """The grouped launch's queues (launch_spmm_group, spmm_group_kernel):
+    jobs sorted by K, longest first; run x of each job's tile order per XCD."""
+    order = sorted(range(len(jobs)), key=lambda j: -jobs[j][2])
+    tiles = []
+    for x in range(8):
+        for q in order:
+            T, N, K = jobs[q]
+            tiles_m, tiles_n = cdiv(N, 256), cdiv(T, 256)
+            nt = tiles_m * tiles_n
+            lo, hi = x * nt // 8, (x + 1) * nt // 8
+            tm, tn = group_order(np.arange(lo, hi), tiles_m, tiles_n)
+            tiles += [(q, int(a), int(b)) for a, b in zip(tm, tn)]
+    return tiles
+
+
+# ----------------------------------------------------------------------------
+# weight gradient (sp24_dw.hip)
+
+DW_SHAPES = [(256, 256, 128, 128, 1.0), (256, 160, 64, 160, 0.9), (160, 256, 160, 64, 0.9), (128, 128, 64, 64, 0.75)]
+
+
+def dw_shape(R, C):
+    best, best_t = None, 0.0
+    for k, (bm, bn, wm, wn, speed) in enumerate(DW_SHAPES):
+        t = cdiv(cdiv(R, bm) * cdiv(C, bn), CUS) * bm * bn / speed
+        if best is None or t < best_t:
+            best, best_t = k, t
+    return DW_SHAPES[best][:4]
+
+
+def check_weight_grad(T, R, C):
+    BM, BN, WM, WN = dw_shape(R, C)
+    tiles_m, tiles_n = cdiv(R, BM), cdiv(C, BN)
+    tm, tn = check_tile_map(tiles_m, tiles_n)
+    waves = (BM // WM) * (BN // WN)
+    lane = np.arange(64)
+    l32, g = lane & 31, lane >> 5
+    rel_r, rel_c = [], []
+    for wave in range(waves):
+        wm, wn = wave % (BM // WM), wave // (BM // WM)
+        for mt in range(WM // 32):
+            for nt in range(WN // 32):
+                for i4 in range(4):
+                    rel_c.append(wn * WN + nt * 32 + l32)
+                    rel_r.append(wm * WM + mt * 32 + 8 * i4 + 4 * g)
+    rel_r, rel_c = np.concatenate(rel_r), np.concatenate(rel_c)
+    quad = np.zeros((BM // 4, BN), np.int64)
+    np.add.at(quad, (rel_r // 4, rel_c), 1)
+    assert (quad == 1).all(), "the weight-gradient epilogue does not cover its tile once"
+    cover = np.zeros((R // 4, C), np.int8)
+    nk = cdiv(T, 32)
+    for a, b in zip(tm, tn):
+        m0, n0 = a * BM, b * BN
+        r4, c = m0 + rel_r, n0 + rel_c
+        ok = (r4 < R) & (c < C)
+        assert (r4[ok] + 4 <= R).all()
+        np.add.at(cover, (r4[ok] // 4, c[ok]), 1)
+        # direct loads: 32 token rows per stage, rows of the tile's columns;
+        # offsets row*R*2 + slot*16 + kt*32*R*2 in 32-bit arithmetic
+        if T:
+            worst_a = 31 * R * 2 + (BM // 8 - 1) * 16 + (nk - 1) * 32 * R * 2
+            worst_b = 31 * C * 2 + (BN // 8 - 1) * 16 + (nk - 1) * 32 * C * 2
+            assert max(worst_a, worst_b) + 16 <= I32
+            for base, rng, total in ((m0 * 2, (T * R - m0) * 2, T * R * 2), (n0 * 2, (T * C - n0) * 2, T * C * 2)):
+                assert base + rng == total and 0 < rng < U32
+    assert (cover == 1).all()
+
+
+# ----------------------------------------------------------------------------
+# search + compression (sp24_search.hip), 128 x 128 tiles, 256 threads
+
+TILE, THREADS, TILES_PER_WG = 128, 256, 1
+
+
+def check_search_compress(shapes):
+    """One batched launch over `shapes`: tiles map onto jobs once, and the
+    index, both values and both meta outputs of every job are written once."""
+    begin, total = [], 0
+    for R, C in shapes:
+        begin.append(total)
+        total += cdiv(R, TILE) * cdiv(C, TILE)
+    groups = cdiv(total, TILES_PER_WG)
+    grid = cdiv(groups, 8) * 8
+    per_xcd = cdiv(groups, 8)
+    b = np.arange(grid)
+    grp = (b % 8) * per_xcd + b // 8
+    ts = [int(gp) * TILES_PER_WG + k for gp in grp[grp < groups] for k in range(TILES_PER_WG)
+          if int(gp) * TILES_PER_WG + k < total]
+    assert sorted(ts) == list(range(total))
+    cov = [dict(idx=np.zeros((R // 4, C // 16), np.int8), vr=np.zeros((R, C // 16), np.int8),
+                mr=np.zeros((R, C // 16), np.int8), vc=np.zeros((C, R // 16), np.int8),
+                mc=np.zeros((C, R // 16), np.int8)) for R, C in shapes]
+    for t in ts:
+        k = max(i for i in range(len(shapes)) if t >= begin[i])
+        R, C = shapes[k]
+        tiles_c = cdiv(C, TILE)
+        u = t - begin[k]
+        ti, tj = u // tiles_c, u % tiles_c
+        r0, c0 = ti * TILE, tj * TILE
+        rows, cols = min(TILE, R - r0), min(TILE, C - c0)
+        cv = cov[k]
+        tid = np.arange(THREADS)
+        if rows == TILE and cols == TILE:
+            # write_full_tile: segment tid % 8 of rows (columns) tid / 8 + 32 k
+            g4, r = tid % 8, tid // 8
+            np.add.at(cv["idx"], (r0 // 4 + r, c0 // 16 + g4), 1)
+            for kk in range(TILE // 32):
+                rr = r + 32 * kk
+                np.add.at(cv["vr"], (r0 + rr, c0 // 16 + g4), 1)
+                np.add.at(cv["mr"], (r0 + rr, c0 // 16 + g4), 1)
+                np.add.at(cv["vc"], (c0 + rr, r0 // 16 + g4), 1)
+                np.add.at(cv["mc"], (c0 + rr, r0 // 16 + g4), 1)
+        else:
+            # write_tile's loops over the ragged tile
+            nbc, nbr = cols // 4, rows // 4
+            i = np.arange(nbr * (nbc // 4))
+            np.add.at(cv["idx"], (r0 // 4 + i // (nbc // 4), c0 // 16 + i % (nbc // 4)), 1)
+            i = np.arange(rows * (nbc // 4))
+            for key in ("vr", "mr"):
+                np.add.at(cv[key], (r0 + i // (nbc // 4), c0 // 16 + i % (nbc // 4)), 1)
+            i = np.arange(cols * (nbr // 4))
+            for key in ("vc", "mc"):
+                np.add.at(cv[key], (c0 + i // (nbr // 4), r0 // 16 + i % (nbr // 4)), 1)
+    for (R, C), cv in zip(shapes, cov):
+        for key, a in cv.items():
+            assert (a == 1).all(), f"{key} of a {R}x{C} weight is not written exactly once"
+
+
+# ----------------------------------------------------------------------------
+# the shapes of the GPU tests and the benchmark
+
+FFN = [WL.GPT2_355M, WL.GPT2_774M, WL.GPT2_1P5B]
+GEMMS = sorted({(T, N, K) for cfg in [WL.TINY] + FFN for _, T, N, K in cfg.gemm_shapes()} | {
+    (1, 16, 16), (7, 48, 80), (100, 272, 144), (129, 256, 512), (300, 528, 336), (256, 64, 4112), (300, 320, 192),
+    (16347, 1152, 128), (16347, 1280, 128), (16347, 6400, 128), (16347, 128, 1152), (16347, 128, 1280),
+    (16347, 128, 6400), (16384, 256, 65472), (16401, 256, 65472), (300, 272, 192), (37, 48, 80), (513, 528, 256),
+    (1000, 1040, 448), (96, 160, 192), (96, 192, 160)})
+
+
+@pytest.mark.parametrize("T,N,K", GEMMS)
+def test_spmm_writes_and_loads(T, N, K):
+    check_spmm(T, N, K)
+
+
+def test_max_size_shapes_take_the_paths_their_tests_name():
+    assert fast_path(16384, 256, 65472) and not fast_path(16401, 256, 65472)
+
+
+@pytest.mark.parametrize("cfg", [WL.TINY] + FFN, ids=lambda c: c.name)
+def test_grouped_queues_cover_every_tile_once(cfg):
+    jobs = [(T, N, K) for _, T, N, K in cfg.gemm_shapes()]
+    tiles = group_queues(jobs)
+    want = {(q, a, b) for q, (T, N, K) in enumerate(jobs) for a in range(cdiv(N, 256)) for b in range(cdiv(T, 256))}
+    assert len(tiles) == len(want) and set(tiles) == want
+    # each tile of a grouped launch is a fast-path tile of its product
+    for T, N, K in jobs:
+        if fast_path(T, N, K) and K >= 192:
+            for a in range(cdiv(N, 256)):
+                check_fast_loads(256, 256, 128, 64, T, N, K, a * 256, 0)
+
+
+@pytest.mark.parametrize("T,R,C", sorted({(T, R, C) for cfg in FFN for (T, R, C) in
+                                          ((cfg.tokens, cfg.dff, cfg.d), (cfg.tokens, cfg.d, cfg.dff))} | {
+    (1, 16, 16), (33, 272, 144), (100, 528, 336), (700, 256, 160), (64, 1040, 656), (2048, 4096, 4096),
+    (16384, 65520, 16), (0, 272, 400), (16384, 1600, 3200)}))
+def test_weight_grad_writes_and_loads(T, R, C):
+    check_weight_grad(T, R, C)
+
+
+@pytest.mark.parametrize("shapes", [[(64, 64)], [(4096, 4096)], [(6400, 1600), (1600, 6400)],
+                                    [(4096, 1024), (1024, 4096)], [(5120, 1280), (1280, 5120)],
+                                    [(144, 272), (272, 144), (16, 16), (512, 128), (64, 1040)], [(16, 1040)]],
+                         ids=lambda s: "+".join(f"{r}x{c}" for r, c in s))
+def test_search_compress_writes(shapes):
+    check_search_compress(shapes)
