@@ -285,6 +285,23 @@ typedef struct sp24_gemm {
 int sp24_spmm_group(const sp24_gemm* gemms, int count, void* workspace, void* stream);
 
 /*
+ * sp24_spmm_group without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The queue counters live in the
+ * library's own device array of SP24_GROUP_WORKSPACE_BYTES bytes, one copy
+ * per GPU, held until the process ends: zero when the library is loaded,
+ * and left zero by every call that completes.  Its device address is looked
+ * up (hipGetSymbolAddress) on a device's first call.  The call allocates and
+ * frees nothing.  Every call on a GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (on different streams) race and must not be
+ * made.  Same products, results (bit for bit) and limits as
+ * sp24_spmm_group: up to SP24_MAX_GROUP products, SP24_ERR_SHAPE beyond.
+ * Errors: as sp24_spmm_group; LAUNCH also when the array's address cannot be
+ * had.
+ */
+int sp24_spmm_group_noalloc(const sp24_gemm* gemms, int count, void* stream);
+
+/*
  * Weight gradient of a 2:4 FFN linear layer with the masked decay term
  * [Decay]:
  *     dW[r][c] = sum_t dY[t][r] * X[t][c]  +  decay * (1 - M[r][c]) * W[r][c]

@@ -176,11 +176,10 @@ int sp24_spmm_fwd_geglu(const void* X, const void* vals_row, const uint16_t* met
   return launch_status(e);
 }
 
-int sp24_spmm_group(const sp24_gemm* gemms, int count, void* workspace, void* stream) {
+// Checks a group's products and fills the launcher's descriptors.
+int check_group(const sp24_gemm* gemms, int count, sp24::GemmDesc* d) {
   if (gemms == nullptr) return SP24_ERR_NULL;
   if (count < 1 || count > SP24_MAX_GROUP) return SP24_ERR_SHAPE;
-  static_assert(SP24_MAX_GROUP <= 8, "the launcher's job table holds 8 products");
-  sp24::GemmDesc d[SP24_MAX_GROUP];
   for (int j = 0; j < count; ++j) {
     const sp24_gemm& g = gemms[j];
     const int st = check_spmm(g.A, g.vals, g.meta, g.T, g.N, g.K, g.out);
@@ -188,9 +187,27 @@ int sp24_spmm_group(const sp24_gemm* gemms, int count, void* workspace, void* st
     d[j] = {static_cast<const uint16_t*>(g.A), static_cast<const uint16_t*>(g.vals), g.meta,
             static_cast<uint16_t*>(g.out), g.T, g.N, g.K};
   }
+  return SP24_OK;
+}
+
+int sp24_spmm_group(const sp24_gemm* gemms, int count, void* workspace, void* stream) {
+  static_assert(SP24_MAX_GROUP <= 8, "the launcher's job table holds 8 products");
+  static_assert(SP24_GROUP_WORKSPACE_BYTES == 4 * sp24::kGroupScratchWords, "workspace size");
+  sp24::GemmDesc d[SP24_MAX_GROUP];
+  const int st = check_group(gemms, count, d);
+  if (st != SP24_OK) return st;
   if (workspace == nullptr) return SP24_ERR_NULL;
   if (!aligned16(workspace)) return SP24_ERR_ALIGN;
   return launch_status(sp24::launch_spmm_group(d, count, static_cast<unsigned int*>(workspace), as_stream(stream)));
+}
+
+int sp24_spmm_group_noalloc(const sp24_gemm* gemms, int count, void* stream) {
+  sp24::GemmDesc d[SP24_MAX_GROUP];
+  const int st = check_group(gemms, count, d);
+  if (st != SP24_OK) return st;
+  unsigned int* work = nullptr;
+  if (sp24::group_scratch(&work) != hipSuccess) return SP24_ERR_LAUNCH;
+  return launch_status(sp24::launch_spmm_group(d, count, work, as_stream(stream)));
 }
 
 int sp24_spmm_bwd_input(const void* dY, const void* vals_col, const uint16_t* meta_col, int64_t T, int64_t R,

@@ -87,5 +87,9 @@ struct GemmDesc {
 // K >= 192; the others run as single launches first).  work: 16 uint32 of
 // device memory, zero on entry; a completed launch leaves them zero.
 hipError_t launch_spmm_group(const GemmDesc* jobs, int count, unsigned int* work, hipStream_t s);
+// The device address, on the current device, of the library's own copy of
+// those 16 words (for the allocation-free entry point).
+constexpr int kGroupScratchWords = 16;
+hipError_t group_scratch(unsigned int** out);
 
 }  // namespace sp24

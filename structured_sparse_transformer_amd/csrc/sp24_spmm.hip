@@ -842,6 +842,30 @@ hipError_t launch_spmm_nt_geglu(const uint16_t* A, const uint16_t* vals, const u
   return launch_fast<256, 256, 128, 64, true>(A, vals, meta, T, N, K, out, N, s, gout, N / 2);
 }
 
+// The grouped launch's queue counters for callers that cannot allocate: 16
+// words of device memory in the library itself, one copy per GPU (zero when
+// the library is loaded, and left zero by every launch that completes).  Host
+// code must not pass the array's name to a kernel: it stands for a host-side
+// symbol.  Its device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current.
+static __device__ __align__(256) unsigned int scratch[kGroupScratchWords];
+
+hipError_t group_scratch(unsigned int** out) {
+  static std::atomic<unsigned int*> ptrs[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  unsigned int* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(reinterpret_cast<void**>(&p), HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 hipError_t launch_spmm_group(const GemmDesc* jobs, int count, unsigned int* work, hipStream_t s) {
   // jobs the fast kernel cannot take run as single launches first
   GroupArgs args{};

@@ -26,7 +26,8 @@ STATUS_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_
                 5: "ERR_UNSUPPORTED", 6: "ERR_TOO_LARGE"}
 EXPORTS = ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
            "sp24_flip_count", "sp24_weight_grad", "sp24_geglu_fwd", "sp24_geglu_bwd", "sp24_mvue",
-           "sp24_spmm_fwd", "sp24_spmm_fwd_geglu", "sp24_spmm_bwd_input", "sp24_spmm_group", "sp24_status_str",
+           "sp24_spmm_fwd", "sp24_spmm_fwd_geglu", "sp24_spmm_bwd_input", "sp24_spmm_group",
+           "sp24_spmm_group_noalloc", "sp24_status_str",
            "sp24_pattern_table", "sp24_abi_version")
 MAX_BATCH = 8
 MAX_GROUP = 8
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "sp24_spmm_fwd_geglu": [p, p, p, i64, i64, i64, p, p, p],
             "sp24_spmm_bwd_input": [p, p, p, i64, i64, i64, p, p],
             "sp24_spmm_group": [p, i32, p, p],
+            "sp24_spmm_group_noalloc": [p, i32, p],
             "sp24_status_str": [i32],
             "sp24_pattern_table": [p],
             "sp24_abi_version": [],
@@ -369,14 +371,7 @@ def group_workspace(device=None):
     return ws
 
 
-def sp24_spmm_group(gemms, workspace=None, stream=None):
-    """Several independent products out = A * S^T in one launch.
-
-    ``gemms`` is a list of (A, vals, meta, out) with A fp16 [T, K], (vals,
-    meta) the 2:4 row form of S [N, K] (fp16 [N, K/2], int16 [N, K/16]) and
-    out fp16 [T, N] or None (allocated).  The forward product of a layer is
-    (X, vals_row, meta_row, Y); its input gradient (dY, vals_col, meta_col,
-    dX).  Returns the outputs."""
+def _gemm_descs(gemms):
     if not 1 <= len(gemms) <= MAX_GROUP:
         raise ValueError(f"between 1 and {MAX_GROUP} products per group")
     descs, outs = (Gemm * len(gemms))(), []
@@ -392,6 +387,29 @@ def sp24_spmm_group(gemms, workspace=None, stream=None):
         outs.append(out)
         ptr = lambda t: _ptr(t).value if t is not None and t.numel() else None  # noqa: E731
         descs[k] = Gemm(ptr(A), ptr(vals), ptr(meta), ptr(out), T, N, K)
+    return descs, outs
+
+
+def sp24_spmm_group_noalloc(gemms, stream=None):
+    """sp24_spmm_group with the library's own per-GPU queue counters instead
+    of a workspace (the C entry point allocates nothing).  Calls that overlap
+    in time on one GPU race.  Output tensors given as None are allocated here
+    by torch; pass them all to keep the whole call allocation-free."""
+    descs, outs = _gemm_descs(gemms)
+    _check("sp24_spmm_group_noalloc", lib().sp24_spmm_group_noalloc(ctypes.cast(descs, ctypes.c_void_p), len(gemms),
+                                                                    _stream(stream)))
+    return outs
+
+
+def sp24_spmm_group(gemms, workspace=None, stream=None):
+    """Several independent products out = A * S^T in one launch.
+
+    ``gemms`` is a list of (A, vals, meta, out) with A fp16 [T, K], (vals,
+    meta) the 2:4 row form of S [N, K] (fp16 [N, K/2], int16 [N, K/16]) and
+    out fp16 [T, N] or None (allocated).  The forward product of a layer is
+    (X, vals_row, meta_row, Y); its input gradient (dY, vals_col, meta_col,
+    dX).  Returns the outputs."""
+    descs, outs = _gemm_descs(gemms)
     ws = group_workspace() if workspace is None else workspace
     if ws.numel() * ws.element_size() < GROUP_WORKSPACE_BYTES:
         raise ValueError(f"the workspace needs {GROUP_WORKSPACE_BYTES} bytes")

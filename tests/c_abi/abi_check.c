@@ -93,6 +93,9 @@ int main(void) {
     CHECK(sp24_spmm_group(g, 2, fake, NULL) == SP24_ERR_SHAPE);
     CHECK(sp24_spmm_group(g, 1, NULL, NULL) == SP24_ERR_NULL);
     CHECK(sp24_spmm_group(g, SP24_MAX_GROUP + 1, fake, NULL) == SP24_ERR_SHAPE);
+    CHECK(sp24_spmm_group_noalloc(g, SP24_MAX_GROUP + 1, NULL) == SP24_ERR_SHAPE);
+    CHECK(sp24_spmm_group_noalloc(g, 2, NULL) == SP24_ERR_SHAPE);
+    CHECK(sp24_spmm_group_noalloc(NULL, 1, NULL) == SP24_ERR_NULL);
     CHECK(SP24_GROUP_WORKSPACE_BYTES >= 64);
   }
   if (failures == 0) printf("ok\n");

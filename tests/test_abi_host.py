@@ -40,7 +40,8 @@ def test_header_declares_the_entry_points():
     for n in ("sp24_mask_search", "sp24_compress", "sp24_search_compress", "sp24_search_compress_batch",
               "sp24_flip_count", "sp24_weight_grad", "sp24_geglu_fwd", "sp24_geglu_bwd", "sp24_mvue",
               "sp24_spmm_fwd", "sp24_spmm_fwd_geglu",
-              "sp24_spmm_bwd_input", "sp24_spmm_group", "sp24_status_str", "sp24_pattern_table",
+              "sp24_spmm_bwd_input", "sp24_spmm_group", "sp24_spmm_group_noalloc", "sp24_status_str",
+              "sp24_pattern_table",
               "sp24_abi_version"):
         assert n in names
 
@@ -271,6 +272,12 @@ def test_spmm_group_validation(L):
     assert f(arr(ok, Gemm(0x1000, 0x1000, 0x1000, 0x1000, 1 << 31, 16, 16)), 2, FAKE, NUL) == 6
     # every product is checked before anything is launched; empty products need no buffers
     assert f(arr(Gemm(0, 0, 0, 0, 0, 256, 64), Gemm(0, 0, 0, 0, 16, 0, 64)), 2, FAKE, NUL) == 0
+    # the allocation-free variant checks the same way (and needs no workspace)
+    g = L.sp24_spmm_group_noalloc
+    assert g(None, 1, NUL) == 1
+    assert g(arr(*([ok] * 9)), 9, NUL) == 2
+    assert g(arr(ok, Gemm(0x1000, 0x1000, 0x1000, 0x1000, 300, 250, 1600)), 2, NUL) == 2
+    assert g(arr(ok, Gemm(0x1000, 0x1000, 0x1000, 0x1008, 300, 256, 64)), 2, NUL) == 3
 
 
 def test_ffn_layer_rejects_bad_shapes():
