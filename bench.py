@@ -39,7 +39,7 @@ from structured_sparse_transformer_amd import workloads as WL  # noqa: E402
 HBM_PEAK_GBPS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0      # dense fp16 matrix-core peak of MI355X
 SC_BYTES_PER_ELEM = 4.375           # read W 2 and previous idx 1/16; write idx 1/16, two 2:4 forms 2 x (1 + 1/8)
-COUNTERS = os.path.join(ROOT, "profiles", "spmm_nt_gpt2-1.5b_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "spmm_group_gpt2-1.5b_counters.json")
 DECAY = 2e-4                         # masked decay factor of the weight-gradient leg
 GEGLU_GROUP = 16                     # GEGLU column layout: blocks of 16 values, then their 16 gates
 TRIALS = 5                           # repeated timings behind each reported median

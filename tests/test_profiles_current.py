@@ -1,7 +1,8 @@
 """The committed rocprofv3 summaries describe the kernels as they are: each
 summary records the sha256 of the source file its kernels were built from,
 and that must be the current file's.  (bench.py applies the same rule to the
-GEMM's traffic counters, and reports no traffic when they are stale.)"""
+traffic counters of the GEMM and of search+compress, and reports no traffic
+when they are stale.)"""
 import hashlib
 import json
 import os
@@ -28,7 +29,9 @@ def test_every_kernel_summary_matches_its_source():
     assert seen >= 5
 
 
-def test_gemm_counters_match_the_source():
-    c = json.load(open(os.path.join(PROFILES, "spmm_nt_gpt2-1.5b_counters.json")))
-    assert c["source_sha256_16"] == sha16("structured_sparse_transformer_amd/csrc/sp24_spmm.hip")
-    assert c["hbm_bytes_per_launch"] > c["algorithmic_bytes_per_launch"] > 0
+def test_counter_summaries_match_their_sources():
+    for name, src in (("spmm_group_gpt2-1.5b_counters.json", "sp24_spmm.hip"),
+                      ("search_compress_gpt2-1.5b_counters.json", "sp24_search.hip")):
+        c = json.load(open(os.path.join(PROFILES, name)))
+        assert c["source_sha256_16"] == sha16("structured_sparse_transformer_amd/csrc/" + src), name
+        assert c["hbm_bytes_per_launch"] > 0 and c["algorithmic_bytes_per_launch"] > 0
