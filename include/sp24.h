@@ -31,7 +31,8 @@
  *   - W is the fp16 weight [R, C], row-major, PyTorch Linear layout [out, in].
  *   - Every pointer argument except `stream` is a DEVICE pointer owned by the
  *     caller.  The library allocates nothing, keeps no per-call state and never
- *     frees caller memory.  Buffers are contiguous and row-major.
+ *     frees caller memory.  Buffers are contiguous and row-major, except the
+ *     compressed 2:4 forms, which use the blocked order defined below.
  *   - Every device pointer must be 16-byte aligned (SP24_ERR_ALIGN otherwise).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls enqueue their kernels on that stream and return at once; nothing
@@ -64,6 +65,20 @@
  *                layout applied to the transpose of the pruned W (groups of 4
  *                along R).  It exists because the masks are transposable, so
  *                every column group keeps exactly two entries [Abstract].
+ * The bracketed shapes above give the logical matrices; in memory each is
+ * stored in BLOCKED ORDER (every vals and meta buffer of this library, in and
+ * out), a permutation of the same number of elements:
+ *   An n x m matrix (vals: m = C/2 halves per row, block width b = 32; meta:
+ *   m = C/16 words per row, b = 4) is cut into bands of 64 rows (the last
+ *   band has h = n - 64*(n/64) rows when n is not a multiple of 64).  Band k
+ *   occupies elements [64*k*m, 64*k*m + h_k*m) and holds its column blocks
+ *   of width b one after the other, each block row-major (h_k rows of its
+ *   width; the last block of a row is m - b*(m/b) wide when b does not
+ *   divide m).  So element (r, c) sits at
+ *     64*k*m + b*(c/b)*h_k + (r - 64*k)*w + c%b,   k = r/64,
+ *   with w = min(b, m - b*(c/b)).  One block holds the operands of 64
+ *   columns of W (64 of the reduction) for 64 output rows, so a sparse
+ *   product reads each of its stages as whole contiguous blocks.
  */
 #ifndef SP24_H
 #define SP24_H
@@ -387,12 +402,13 @@ int sp24_geglu_bwd(const void* U, const void* dout, int64_t T, int64_t h, int64_
  *               supplied by the caller
  *   rows, cols   >= 0, cols a multiple of 16
  *   vals   out  fp16 [rows, cols/2]    meta  out  uint16 [rows, cols/16]
- *               The library's 2:4 row form: the kept pair of group g in
- *               order, and its nibble i | k << 2.  The sparse GEMMs accept it
- *               as their sparse operand.
+ *               The library's 2:4 row form in blocked order: the kept pair
+ *               of group g in order, and its nibble i | k << 2.  The sparse
+ *               GEMMs accept it as their sparse operand.
  * Errors: NULL, SHAPE, ALIGN, LAUNCH; TOO_LARGE when a dimension reaches
- * 2^31, rows*cols reaches 2^40, or rows*cols/16 > 2^32 - 256 (one work-item
- * per meta word, the most one launch takes).
+ * 2^31, rows*cols reaches 2^40, or ceil(rows/64) * ceil(cols/128) > 2^24 - 1
+ * (one workgroup of 256 work-items per 64 x 128 panel; one launch takes at
+ * most 2^32 - 256 work-items).
  */
 int sp24_mvue(const void* M, const float* U, int64_t rows, int64_t cols, void* vals, uint16_t* meta,
               void* stream);
@@ -407,7 +423,7 @@ const char* sp24_status_str(int status);
  */
 int sp24_pattern_table(uint16_t* out);
 
-/* Host only: the library's ABI version (7 for this header). */
+/* Host only: the library's ABI version (8 for this header). */
 int sp24_abi_version(void);
 
 #ifdef __cplusplus

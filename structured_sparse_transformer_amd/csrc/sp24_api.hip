@@ -256,7 +256,8 @@ int sp24_mvue(const void* M, const float* U, int64_t rows, int64_t cols, void* v
   int st = check_dims(rows, cols, 1);
   if (st != SP24_OK) return st;
   if (cols % 16 != 0) return SP24_ERR_SHAPE;
-  if (rows != 0 && cols / 16 > kMaxLaunchItems / rows) return SP24_ERR_TOO_LARGE;   // one work-item per 16 entries
+  // one workgroup of 256 per two 64 x 64 blocks of a 64-row band
+  if (((rows + 63) / 64) * ((cols / 16 + 7) / 8) > kMaxLaunchItems / 256) return SP24_ERR_TOO_LARGE;
   if (rows == 0 || cols == 0) return SP24_OK;
   if (M == nullptr || U == nullptr || vals == nullptr || meta == nullptr) return SP24_ERR_NULL;
   if (!aligned16(M) || !aligned16(U) || !aligned16(vals) || !aligned16(meta)) return SP24_ERR_ALIGN;
@@ -283,6 +284,6 @@ int sp24_pattern_table(uint16_t* out) {
   return SP24_OK;
 }
 
-int sp24_abi_version(void) { return 7; }
+int sp24_abi_version(void) { return 8; }
 
 }  // extern "C"

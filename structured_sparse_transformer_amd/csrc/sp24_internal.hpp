@@ -5,6 +5,18 @@
 
 namespace sp24 {
 
+// Element offset of (r, c) in an n x m matrix stored in the compressed forms'
+// blocked order: bands of 64 rows, each band's column blocks of width b
+// (a power of two) stored one after the other, each block row-major; the
+// last band and each band's last block may be narrower.  vals use b = 32
+// halves (64 columns of W), meta b = 4 words.
+__host__ __device__ inline int64_t form_off(int64_t r, int64_t c, int64_t n, int64_t m, int64_t b) {
+  const int64_t r0 = r & ~(int64_t)63, c0 = c & ~(b - 1);
+  const int64_t h = n - r0 < 64 ? n - r0 : 64, w = m - c0 < b ? m - c0 : b;
+  return r0 * m + c0 * h + (r - r0) * w + (c - c0);
+}
+constexpr int64_t kValsBlock = 32, kMetaBlock = 4;
+
 // Mask search only: idx[R/4][C/4].  R, C multiples of 4.
 hipError_t launch_mask_search(const uint16_t* W, int64_t R, int64_t C, uint8_t* idx, hipStream_t s);
 
@@ -59,12 +71,14 @@ hipError_t launch_geglu_bwd(const uint16_t* U, const uint16_t* dout, int64_t T, 
                             uint16_t* dU, hipStream_t s);
 
 // MVUE 2:4 estimate of M [rows][cols] (cols a multiple of 16) with one
-// uniform U [rows][cols/4] per group, into the row form vals/meta.
+// uniform U [rows][cols/4] per group, into the row form vals/meta (blocked
+// order).
 hipError_t launch_mvue(const uint16_t* M, const float* U, int64_t rows, int64_t cols, uint16_t* vals, uint16_t* meta,
                        hipStream_t s);
 
 // out[T][N] = A[T][K] * S[N][K]^T with S in 2:4 row form along K:
-// vals [N][K/2] fp16, meta [N][K/16].  N, K multiples of 16.
+// vals [N][K/2] fp16, meta [N][K/16], both in blocked order.  N, K multiples
+// of 16.
 hipError_t launch_spmm_nt(const uint16_t* A, const uint16_t* vals, const uint16_t* meta, int64_t T,
                           int64_t N, int64_t K, uint16_t* out, hipStream_t s);
 

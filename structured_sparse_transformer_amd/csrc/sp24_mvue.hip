@@ -17,13 +17,18 @@
 // cumulative masses instead of dividing, the same decisions in exact
 // arithmetic.  Output: the
 // library's 2:4 row form (vals fp16 [rows][cols/2], meta [rows][cols/16], one
-// nibble i0 | i1 << 2 per group), which the sparse GEMM consumes directly.
+// nibble i0 | i1 << 2 per group) in the forms' blocked order, which the sparse
+// GEMM consumes directly.
 //
 // Bound by HBM: per entry it reads 2 bytes of the gradient and 1 of u (4 bytes
 // per group) and writes 1.125 bytes, against about 50 VALU operations per
-// group.  One lane handles 16 entries (one meta word) with 16-byte accesses;
-// splitting a lane's entries into two wave-contiguous halves, or giving each
-// lane 8, measured slower.
+// group.  One lane handles 16 entries (one meta word, 8 halves of vals) with
+// 16-byte accesses.  In the blocked order a 64-row band's column block of 64
+// entries is 4 KB of vals and 512 B of meta, contiguous; a workgroup of 256
+// lanes takes two neighbouring blocks of a band, one after the other, so its
+// lanes write whole contiguous blocks and read whole 128-byte lines of the
+// gradient (each row's 64 entries) and of u (the two blocks' 16 uniforms
+// each).
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -112,45 +117,57 @@ __device__ __forceinline__ Pick mvue_group(const float (&a)[4], float u) {
   return r;
 }
 
-template <typename Index>
+// Workgroup b: band b / pairs (rows 64 k ..), column blocks 2 (b % pairs) and
+// 2 (b % pairs) + 1 of that band (blocks of 4 meta words, 64 entries).  Lane t
+// of a block of h rows and w words takes row t / w, word t % w: its output is
+// the block's t-th element in blocked order.
 __global__ __launch_bounds__(kMvueThreads) void mvue_kernel(const uint16_t* __restrict__ M, const float* __restrict__ U,
-                                                            Index n, uint16_t* __restrict__ vals,
+                                                            int64_t rows, int64_t cols, int64_t pairs,
+                                                            uint16_t* __restrict__ vals,
                                                             uint16_t* __restrict__ meta) {
-  // lane i: entries 16i .. 16i+15 of the flattened matrix (rows are whole
-  // multiples of 16 entries, so a lane never straddles two rows)
-  const Index i = (Index)blockIdx.x * kMvueThreads + threadIdx.x;
-  if (i >= n) return;
-  const h8 lo = __builtin_bit_cast(h8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(M) + 2 * (int64_t)i));
-  const h8 hi =
-      __builtin_bit_cast(h8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(M) + 2 * (int64_t)i + 1));
-  const f32x4 us = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(U) + (int64_t)i);
-  h8 out;
-  uint32_t word = 0;
+  const int64_t b = blockIdx.x, band = b / pairs, pair = b - band * pairs;
+  const int64_t m = cols / 16;   // meta words (16-entry segments) per row
+  const int64_t r0 = 64 * band;
+  const int h = (int)min<int64_t>(64, rows - r0);
+  const int t = threadIdx.x;
+#pragma unroll 1
+  for (int q = 0; q < 2; ++q) {
+    const int64_t j = 2 * pair + q;
+    if (4 * j >= m) break;
+    const int w = (int)min<int64_t>(4, m - 4 * j);
+    const int rr = w == 4 ? t >> 2 : t / w, cc = w == 4 ? t & 3 : t - (t / w) * w;
+    if (rr >= h) continue;
+    const int64_t r = r0 + rr, seg = 4 * j + cc;
+    const int64_t out = r0 * m + 4 * j * h + t;   // blocked-order index of (r, seg)
+    const u32x4* src = reinterpret_cast<const u32x4*>(M + r * cols + 16 * seg);
+    const h8 lo = __builtin_bit_cast(h8, __builtin_nontemporal_load(src));
+    const h8 hi = __builtin_bit_cast(h8, __builtin_nontemporal_load(src + 1));
+    const f32x4 us = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(U + r * (cols / 4) + 4 * seg));
+    h8 o;
+    uint32_t word = 0;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float a[4];
+    for (int g = 0; g < 4; ++g) {
+      float a[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] = (float)(g < 2 ? lo[4 * g + e] : hi[4 * (g - 2) + e]);
-    const Pick pk = mvue_group(a, us[g]);
-    out[2 * g] = (_Float16)pk.vi;
-    out[2 * g + 1] = (_Float16)pk.vk;
-    word |= pk.nib << (4 * g);
+      for (int e = 0; e < 4; ++e) a[e] = (float)(g < 2 ? lo[4 * g + e] : hi[4 * (g - 2) + e]);
+      const Pick pk = mvue_group(a, us[g]);
+      o[2 * g] = (_Float16)pk.vi;
+      o[2 * g + 1] = (_Float16)pk.vk;
+      word |= pk.nib << (4 * g);
+    }
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, o), reinterpret_cast<u32x4*>(vals) + out);
+    meta[out] = (uint16_t)word;
   }
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, out), reinterpret_cast<u32x4*>(vals) + (int64_t)i);
-  meta[i] = (uint16_t)word;
 }
 
 }  // namespace
 
 hipError_t launch_mvue(const uint16_t* M, const float* U, int64_t rows, int64_t cols, uint16_t* vals, uint16_t* meta,
                        hipStream_t s) {
-  const int64_t n = rows * (cols / 16);
-  if (n == 0) return hipSuccess;
-  const dim3 grid((unsigned)((n + kMvueThreads - 1) / kMvueThreads));
-  if (n < ((int64_t)1 << 32) - kMvueThreads)
-    hipLaunchKernelGGL(mvue_kernel<uint32_t>, grid, dim3(kMvueThreads), 0, s, M, U, (uint32_t)n, vals, meta);
-  else
-    hipLaunchKernelGGL(mvue_kernel<uint64_t>, grid, dim3(kMvueThreads), 0, s, M, U, (uint64_t)n, vals, meta);
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const int64_t pairs = (cols / 16 + 7) / 8, bands = (rows + 63) / 64;
+  hipLaunchKernelGGL(mvue_kernel, dim3((unsigned)(bands * pairs)), dim3(kMvueThreads), 0, s, M, U, rows, cols, pairs,
+                     vals, meta);
   return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@
 // maximum in pattern order wins.  Two code paths compute exactly that:
 //
 //  * search_fast, for blocks whose sums are all exact in fp32.  With e the
-//    fp16 exponent field, a block is exact when emax - max(emin_nonzero, 1)
+//    fp16 exponent field, a block is exact when emax - max(em_innonzero, 1)
 //    <= 10: every entry is then an integer multiple of q = 2^(emin-25) below
 //    2^21 q, so every sum of up to 8 entries is an integer multiple of q below
 //    2^24 q and is exact in fp32 whatever the order of additions.  The sums are
@@ -41,7 +41,7 @@ typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b)));
 }
-__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+__device__ __forceinline__ uint32_t pk_m_inu16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b)));
 }
 __device__ __forceinline__ uint32_t pk_dec_u16(uint32_t a) {
@@ -64,18 +64,18 @@ struct BlockMag {
 
 // Exponent range of the block: returns true (fast path usable) and the scale
 // exponent emin' when all partial sums are exact in fp32.
-__device__ __forceinline__ bool exact_regime(const BlockMag& b, int& emin_out) {
+__device__ __forceinline__ bool exact_regime(const BlockMag& b, int& em_inout) {
   uint32_t mx = pk_max_u16(pk_max_u16(pk_max_u16(b.m[0][0], b.m[0][1]), pk_max_u16(b.m[1][0], b.m[1][1])),
                            pk_max_u16(pk_max_u16(b.m[2][0], b.m[2][1]), pk_max_u16(b.m[3][0], b.m[3][1])));
-  uint32_t mn = pk_min_u16(pk_min_u16(pk_min_u16(pk_dec_u16(b.m[0][0]), pk_dec_u16(b.m[0][1])),
-                                      pk_min_u16(pk_dec_u16(b.m[1][0]), pk_dec_u16(b.m[1][1]))),
-                           pk_min_u16(pk_min_u16(pk_dec_u16(b.m[2][0]), pk_dec_u16(b.m[2][1])),
-                                      pk_min_u16(pk_dec_u16(b.m[3][0]), pk_dec_u16(b.m[3][1]))));
+  uint32_t mn = pk_m_inu16(pk_m_inu16(pk_m_inu16(pk_dec_u16(b.m[0][0]), pk_dec_u16(b.m[0][1])),
+                                      pk_m_inu16(pk_dec_u16(b.m[1][0]), pk_dec_u16(b.m[1][1]))),
+                           pk_m_inu16(pk_m_inu16(pk_dec_u16(b.m[2][0]), pk_dec_u16(b.m[2][1])),
+                                      pk_m_inu16(pk_dec_u16(b.m[3][0]), pk_dec_u16(b.m[3][1]))));
   const uint32_t hmax = max(mx & 0xFFFFu, mx >> 16);
-  const uint32_t hmin_nz = min(mn & 0xFFFFu, mn >> 16) + 1u;  // 0x10000 when all entries are zero
+  const uint32_t hm_innz = min(mn & 0xFFFFu, mn >> 16) + 1u;  // 0x10000 when all entries are zero
   const int emax = (int)(hmax >> 10);
-  const int emin = max((int)(hmin_nz >> 10), 1);                 // 64 when all entries are zero
-  emin_out = emin;
+  const int emin = max((int)(hm_innz >> 10), 1);                 // 64 when all entries are zero
+  em_inout = emin;
   return emax < 31 && emax - emin <= 10;
 }
 
@@ -363,7 +363,10 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 // Stores of a whole 128 x 128 tile (every tile but those on a weight's ragged
 // edge).  Lane tid writes 16-byte segment tid % 8 of rows (and columns)
 // tid / 8 + 32 k, so its addresses are computed once and then advance by a
-// uniform stride: no per-segment division or 64-bit multiply.
+// uniform stride: no per-segment division or 64-bit multiply.  In the forms'
+// blocked order the tile covers two 64-row bands and two column blocks, all
+// full: pass k writes rows 32k .. 32k+31, in band k / 2 at row 32 (k % 2) of
+// the band, and each wave's 8 rows of a block are 512 contiguous bytes.
 __device__ __forceinline__ void write_full_tile(const TileRef& tr, int tid, const CompressSmem& sm) {
   const ScJob& jb = tr.jb;
   const int64_t R = jb.R, C = jb.C, r0 = tr.r0, c0 = tr.c0;
@@ -375,44 +378,54 @@ __device__ __forceinline__ void write_full_tile(const TileRef& tr, int tid, cons
                        (uint32_t)sm.idx[r][4 * g4 + 2] << 16 | (uint32_t)sm.idx[r][4 * g4 + 3] << 24;
     *reinterpret_cast<uint32_t*>(jb.idx_out + (r0 / 4 + r) * (C / 4) + c0 / 4 + 4 * g4) = v;
   }
+  // offsets within a band: column block g4 / 4, row r, segment (word) g4 % 4
+  const int vin = (g4 / 4) * 64 * (int)kValsBlock + r * (int)kValsBlock + 8 * (g4 % 4);
+  const int m_in = (g4 / 4) * 64 * (int)kMetaBlock + r * (int)kMetaBlock + (g4 % 4);
   if (jb.vals_row) {
-    uint16_t* vp = jb.vals_row + (r0 + r) * (C / 2) + c0 / 2 + 8 * g4;
-    uint16_t* mp = jb.meta_row + (r0 + r) * (C / 16) + c0 / 16 + g4;
-    const int64_t vstep = kStep * (C / 2), mstep = kStep * (C / 16);
+    // bands of 64 rows of C/2 halves (C/16 words); the tile's first column
+    // block starts at half c0/2 (word c0/16) of the band's columns
+    uint16_t* vp = jb.vals_row + r0 * (C / 2) + (c0 / 2) * 64 + vin;
+    uint16_t* mp = jb.meta_row + r0 * (C / 16) + (c0 / 16) * 64 + m_in;
+    const int64_t vband = 64 * (C / 2), mband = 64 * (C / 16);
     const int sh = 4 * (r & 3);   // the row within its block (kStep is a multiple of 4)
 #pragma unroll
     for (int k = 0; k < kTile / kStep; ++k) {
       const int rr = r + kStep * k;
-      *reinterpret_cast<uint4*>(vp + k * vstep) =
+      const int64_t vo = (k / 2) * vband + (k % 2) * kStep * kValsBlock;
+      const int64_t mo = (k / 2) * mband + (k % 2) * kStep * kMetaBlock;
+      *reinterpret_cast<uint4*>(vp + vo) =
           make_uint4(sm.vals_row[rr][4 * g4 + 0], sm.vals_row[rr][4 * g4 + 1], sm.vals_row[rr][4 * g4 + 2],
                      sm.vals_row[rr][4 * g4 + 3]);
       uint32_t word = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) word |= ((sm.bnibs[rr >> 2][4 * g4 + q] >> sh) & 0xFu) << (4 * q);
-      mp[k * mstep] = (uint16_t)word;
+      mp[mo] = (uint16_t)word;
     }
   }
   if (jb.vals_col) {
-    uint16_t* vp = jb.vals_col + (c0 + r) * (R / 2) + r0 / 2 + 8 * g4;
-    uint16_t* mp = jb.meta_col + (c0 + r) * (R / 16) + r0 / 16 + g4;
-    const int64_t vstep = kStep * (R / 2), mstep = kStep * (R / 16);
+    uint16_t* vp = jb.vals_col + c0 * (R / 2) + (r0 / 2) * 64 + vin;
+    uint16_t* mp = jb.meta_col + c0 * (R / 16) + (r0 / 16) * 64 + m_in;
+    const int64_t vband = 64 * (R / 2), mband = 64 * (R / 16);
     const int sh = 16 + 4 * (r & 3);
 #pragma unroll
     for (int k = 0; k < kTile / kStep; ++k) {
       const int c = r + kStep * k;
       const int cs = col_swz(kStep * k);   // equals col_swz(c), since r < kStep
-      *reinterpret_cast<uint4*>(vp + k * vstep) =
+      const int64_t vo = (k / 2) * vband + (k % 2) * kStep * kValsBlock;
+      const int64_t mo = (k / 2) * mband + (k % 2) * kStep * kMetaBlock;
+      *reinterpret_cast<uint4*>(vp + vo) =
           make_uint4(sm.vals_col[c][(4 * g4 + 0) ^ cs], sm.vals_col[c][(4 * g4 + 1) ^ cs],
                      sm.vals_col[c][(4 * g4 + 2) ^ cs], sm.vals_col[c][(4 * g4 + 3) ^ cs]);
       uint32_t word = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) word |= ((sm.bnibs[4 * g4 + q][c >> 2] >> sh) & 0xFu) << (4 * q);
-      mp[k * mstep] = (uint16_t)word;
+      mp[mo] = (uint16_t)word;
     }
   }
 }
 
-// Coalesced stores of a staged tile: 16-byte row and column segments.
+// Coalesced stores of a staged tile: 16-byte row and column segments, each
+// contiguous in the forms' blocked order (its columns stay in one block).
 __device__ __forceinline__ void write_tile(const TileRef& tr, int tid, const CompressSmem& sm) {
   if (tr.rows == kTile && tr.cols == kTile) {
     write_full_tile(tr, tid, sm);
@@ -435,13 +448,13 @@ __device__ __forceinline__ void write_tile(const TileRef& tr, int tid, const Com
       const int r = i / q4, g4 = i - r * q4;
       const uint4 v = make_uint4(sm.vals_row[r][4 * g4 + 0], sm.vals_row[r][4 * g4 + 1], sm.vals_row[r][4 * g4 + 2],
                                  sm.vals_row[r][4 * g4 + 3]);
-      *reinterpret_cast<uint4*>(jb.vals_row + (r0 + r) * (C / 2) + c0 / 2 + 8 * g4) = v;
+      *reinterpret_cast<uint4*>(jb.vals_row + form_off(r0 + r, c0 / 2 + 8 * g4, R, C / 2, kValsBlock)) = v;
       // row r's nibble in each of the four blocks (r/4, 4*g4 + q)
       const int sh = 4 * (r & 3);
       uint32_t word = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) word |= ((sm.bnibs[r >> 2][4 * g4 + q] >> sh) & 0xFu) << (4 * q);
-      jb.meta_row[(r0 + r) * (C / 16) + c0 / 16 + g4] = (uint16_t)word;
+      jb.meta_row[form_off(r0 + r, c0 / 16 + g4, R, C / 16, kMetaBlock)] = (uint16_t)word;
     }
   }
   if (jb.vals_col) {
@@ -450,13 +463,13 @@ __device__ __forceinline__ void write_tile(const TileRef& tr, int tid, const Com
       const int c = i / q4, g4 = i - c * q4, cs = col_swz(c);
       const uint4 v = make_uint4(sm.vals_col[c][(4 * g4 + 0) ^ cs], sm.vals_col[c][(4 * g4 + 1) ^ cs],
                                  sm.vals_col[c][(4 * g4 + 2) ^ cs], sm.vals_col[c][(4 * g4 + 3) ^ cs]);
-      *reinterpret_cast<uint4*>(jb.vals_col + (c0 + c) * (R / 2) + r0 / 2 + 8 * g4) = v;
+      *reinterpret_cast<uint4*>(jb.vals_col + form_off(c0 + c, r0 / 2 + 8 * g4, C, R / 2, kValsBlock)) = v;
       // column c's nibble in each of the four blocks (4*g4 + q, c/4)
       const int sh = 16 + 4 * (c & 3);
       uint32_t word = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) word |= ((sm.bnibs[4 * g4 + q][c >> 2] >> sh) & 0xFu) << (4 * q);
-      jb.meta_col[(c0 + c) * (R / 16) + r0 / 16 + g4] = (uint16_t)word;
+      jb.meta_col[form_off(c0 + c, r0 / 16 + g4, C, R / 16, kMetaBlock)] = (uint16_t)word;
     }
   }
 }

@@ -109,7 +109,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void spmm_nt_kernel(
       const int row = c / (BK / 16), part = c % (BK / 16);
       const int64_t gr = min<int64_t>(m0 + row, N - 1);
       const int64_t kc = k0 / 2 + part * 8;
-      s_reg[i] = kc < Kh ? *reinterpret_cast<const uint4*>(vals + gr * Kh + kc) : make_uint4(0, 0, 0, 0);
+      s_reg[i] = kc < Kh ? *reinterpret_cast<const uint4*>(vals + form_off(gr, kc, N, Kh, kValsBlock))
+                         : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < Cfg::B_PER_T; ++i) {
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void spmm_nt_kernel(
         const int row = c / 4, w = c % 4;
         const int64_t gr = min<int64_t>(m0 + row, N - 1);
         const int64_t kw = k0 / 16 + w;
-        m_reg[i] = kw < Km ? meta[gr * Km + kw] : (uint16_t)0;
+        m_reg[i] = kw < Km ? meta[form_off(gr, kw, N, Km, kMetaBlock)] : (uint16_t)0;
       }
     }
   };
@@ -302,22 +303,38 @@ __device__ __forceinline__ void spmm_fast_tile(unsigned char* __restrict__ smem,
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % Cfg::WAVES_M, wn = wave / Cfg::WAVES_M;
   const int l32 = lane & 31, g = lane >> 5;
-  const int Kh = (int)(K / 2), Km = (int)(K / 16);
   const int nk = (int)(K / 64);
 
   // buffer resources based at this tile's first row; bytes past the matrix
-  // end are out of range and load as zero
-  const i32x4 rs = make_rsrc(vals + m0 * Kh, (uint32_t)((N - m0) * Kh * 2));
+  // end are out of range and load as zero.  S and meta are in blocked order:
+  // a band of 64 rows starts every band_s (band_m) bytes, and stage kt of a
+  // band of h rows is its contiguous block at kt * h * 64 (kt * h * 8) bytes.
+  // Each load's rows (16 of S, 32 of meta) lie in one band, so its stage
+  // stride st_s (st_m) is uniform across the wave: 4096 (512) for a full
+  // band.  In the last band of an N % 64 != 0 operand, rows past N read bytes
+  // of other rows or of nothing (zero); both only feed outputs that are not
+  // stored.  Bands wholly past N start beyond the range.
+  const i32x4 rs = make_rsrc(vals + m0 * (K / 2), (uint32_t)((N - m0) * K));
   const i32x4 rb = make_rsrc(A + n0 * K, (uint32_t)((T - n0) * K * 2));
-  const i32x4 rm = make_rsrc(meta + m0 * Km, (uint32_t)((N - m0) * Km * 2));
+  const i32x4 rm = make_rsrc(meta + m0 * (K / 16), (uint32_t)((N - m0) * (K / 8)));
+  const int band_s = 64 * (int)K, band_m = 8 * (int)K;
+  auto band_rows = [&](int band) {
+    const int64_t left = N - m0 - 64 * band;
+    return (int)(left >= 64 ? 64 : left > 0 ? left : 0);
+  };
+  int st_s[Cfg::S_LOADS], st_m[Cfg::M_LOADS];
+#pragma unroll
+  for (int i = 0; i < Cfg::S_LOADS; ++i) st_s[i] = band_rows((wave * Cfg::S_LOADS + i) / 4) * 64;
+#pragma unroll
+  for (int i = 0; i < Cfg::M_LOADS; ++i) st_m[i] = band_rows((wave * Cfg::M_LOADS + i) / 2) * 8;
 
   // per-lane global byte offsets of this wave's direct loads (stage 0)
   int off_s[Cfg::S_LOADS], off_b[Cfg::B_LOADS], off_m[Cfg::M_LOADS];
 #pragma unroll
   for (int i = 0; i < Cfg::S_LOADS; ++i) {
-    const int q = wave * Cfg::S_LOADS + i;          // 1 KiB block: rows 16q .. 16q+15
+    const int q = wave * Cfg::S_LOADS + i;          // 1 KiB: rows 16q .. 16q+15, contiguous in their block
     const int r = 16 * q + lane / 4, p = lane % 4;
-    off_s[i] = r * Kh * 2 + ((p ^ swz_s(r)) * 16);
+    off_s[i] = (r / 64) * band_s + (r % 64) * 64 + ((p ^ swz_s(r)) * 16);
   }
 #pragma unroll
   for (int i = 0; i < Cfg::B_LOADS; ++i) {
@@ -329,32 +346,32 @@ __device__ __forceinline__ void spmm_fast_tile(unsigned char* __restrict__ smem,
   for (int i = 0; i < Cfg::M_LOADS; ++i) {
     const int q = wave * Cfg::M_LOADS + i;          // rows 32q .. 32q+31
     const int r = 32 * q + lane / 2;
-    off_m[i] = r * Km * 2 + (lane % 2) * 4;
+    off_m[i] = (r / 64) * band_m + (r % 64) * 8 + (lane % 2) * 4;
   }
 
   // one of this wave's LOADS direct loads of stage kt (j in [0, LOADS))
   auto issue_one = [&](int j, int kt, unsigned char* sb, unsigned char* bb, unsigned char* mb) {
     if (j < Cfg::S_LOADS) {
-      dma_b128(rs, lds_addr(sb) + (wave * Cfg::S_LOADS + j) * 1024, off_s[j] + kt * 64);
+      dma_b128(rs, lds_addr(sb) + (wave * Cfg::S_LOADS + j) * 1024, off_s[j] + kt * st_s[j]);
     } else if (j < Cfg::S_LOADS + Cfg::B_LOADS) {
       const int i = j - Cfg::S_LOADS;
       dma_b128(rb, lds_addr(bb) + (wave * Cfg::B_LOADS + i) * 1024, off_b[i] + kt * 128);
     } else {
       const int i = j - Cfg::S_LOADS - Cfg::B_LOADS;
-      dma_b32(rm, lds_addr(mb) + (wave * Cfg::M_LOADS + i) * 256, off_m[i] + kt * 8);
+      dma_b32(rm, lds_addr(mb) + (wave * Cfg::M_LOADS + i) * 256, off_m[i] + kt * st_m[i]);
     }
   };
   auto issue = [&](int kt, unsigned char* sb, unsigned char* bb, unsigned char* mb) {
-    const int ds = kt * 64, db = kt * 128, dm = kt * 8;
+    const int db = kt * 128;
 #pragma unroll
     for (int i = 0; i < Cfg::S_LOADS; ++i)
-      dma_b128(rs, lds_addr(sb) + (wave * Cfg::S_LOADS + i) * 1024, off_s[i] + ds);
+      dma_b128(rs, lds_addr(sb) + (wave * Cfg::S_LOADS + i) * 1024, off_s[i] + kt * st_s[i]);
 #pragma unroll
     for (int i = 0; i < Cfg::B_LOADS; ++i)
       dma_b128(rb, lds_addr(bb) + (wave * Cfg::B_LOADS + i) * 1024, off_b[i] + db);
 #pragma unroll
     for (int i = 0; i < Cfg::M_LOADS; ++i)
-      dma_b32(rm, lds_addr(mb) + (wave * Cfg::M_LOADS + i) * 256, off_m[i] + dm);
+      dma_b32(rm, lds_addr(mb) + (wave * Cfg::M_LOADS + i) * 256, off_m[i] + kt * st_m[i]);
   };
 
   // LDS read offsets of this lane (bytes), independent of the stage

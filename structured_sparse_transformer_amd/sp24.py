@@ -9,7 +9,10 @@ library every call raises.
 Shapes and layouts follow ``include/sp24.h``: W is fp16 [R, C]; idx uint8
 [R/4, C/4]; the row form is (vals_row fp16 [R, C/2], meta_row int16 [R, C/16])
 and the column form (vals_col fp16 [C, R/2], meta_col int16 [C, R/16]).  torch
-has no uint16, so meta words travel as int16 tensors with the same bits.
+has no uint16, so meta words travel as int16 tensors with the same bits.  The
+forms' tensors carry those logical shapes, but their elements are in the
+header's blocked order (64-row bands of contiguous column blocks), so a row
+of such a tensor is not a row of the form.
 """
 from __future__ import annotations
 

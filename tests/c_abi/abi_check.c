@@ -27,7 +27,7 @@ int main(void) {
   unsigned key[90];
   int p, ones, r, c;
 
-  CHECK(sp24_abi_version() == 7);
+  CHECK(sp24_abi_version() == 8);
   CHECK(sp24_pattern_table(NULL) == SP24_ERR_NULL);
   CHECK(sp24_pattern_table(table) == SP24_OK);
   /* every pattern keeps two entries in each row and each column */

@@ -61,7 +61,7 @@ def test_pattern_table_matches_oracle(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.sp24_abi_version() == 7
+    assert L.sp24_abi_version() == 8
     for s in range(7):
         assert L.sp24_status_str(s)
     assert L.sp24_status_str(99) == b"unknown status"
@@ -227,10 +227,11 @@ def test_mvue_validation(L):
     assert f(FAKE, FAKE, 4, 16, FAKE, NUL, NUL) == 1
     assert f(FAKE, MIS, 4, 16, FAKE, FAKE, NUL) == 3
     assert f(FAKE, FAKE, 1 << 31, 16, FAKE, FAKE, NUL) == 6
-    # one work-item per 16 entries, at most 2^32 - 256 per launch
-    assert f(FAKE, FAKE, (1 << 28) - 16, 256, MIS, FAKE, NUL) == 3   # exactly 2^32 - 256 items: allowed
-    assert f(FAKE, FAKE, (1 << 28) - 15, 256, FAKE, FAKE, NUL) == 6
-    assert f(FAKE, FAKE, 1 << 22, 1 << 14, FAKE, FAKE, NUL) == 6     # 2^32 items
+    # one workgroup of 256 work-items per 64 x 128 panel, at most 2^32 - 256 work-items per launch
+    assert f(FAKE, FAKE, (1 << 30) - 64, 128, MIS, FAKE, NUL) == 3   # 2^24 - 1 panels: allowed
+    assert f(FAKE, FAKE, (1 << 30) - 63, 128, FAKE, FAKE, NUL) == 6  # a 2^24-th (partial) band
+    assert f(FAKE, FAKE, 1 << 29, 256, FAKE, FAKE, NUL) == 6         # 2^23 bands of 2 panels
+    assert f(FAKE, FAKE, 1 << 29, 240, MIS, FAKE, NUL) == 6          # 240 columns still take 2 panels
     assert f(NUL, NUL, 0, 16, NUL, NUL, NUL) == 0
 
 

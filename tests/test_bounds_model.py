@@ -9,7 +9,10 @@ the HIP kernels are replayed here in numpy, and the test checks that:
   (the epilogues' lane -> element maps with their bounds checks);
 * every direct-load offset fits the 32-bit signed arithmetic the kernels form
   it in, and each buffer descriptor's base and byte range lie inside the
-  operand it reads (rows past the end then read as zero, by design).
+  operand it reads (rows past the end then read as zero, by design);
+* the compressed forms' addresses (the search's stores, the GEMMs' loads,
+  MVUE's stores) are where the header's blocked order puts each element,
+  taken from tests/forms_layout.py's construction of that order.
 
 The formulas are transcribed from the sources named in each function
 (structured_sparse_transformer_amd/csrc); a change to a kernel's indexing has
@@ -19,6 +22,8 @@ import numpy as np
 import pytest
 
 from structured_sparse_transformer_amd import workloads as WL
+
+from forms_layout import META_BLOCK, VALS_BLOCK, blocked_positions
 
 CUS = 256
 I32 = 2 ** 31
@@ -121,31 +126,82 @@ def check_fast_tile_pattern(BM, BN, WM, WN):
     return n, m
 
 
-def check_fast_loads(BM, BN, WM, WN, T, N, K, m0, n0):
-    """Direct-load offsets of one tile (int32 arithmetic) and its descriptors."""
+def fast_s_meta_offsets(BM, BN, WM, WN, N, K, m0):
+    """spmm_fast_tile's per-lane byte offsets of stage 0 for S and meta and
+    each load's stage stride, with the (row, 16-byte chunk) of S and (row,
+    dword) of meta each lane fetches: lists over (wave, load) of (row, chunk,
+    offset, stride)."""
     waves = (BM // WM) * (BN // WN)
-    Kh, Km, nk = K // 2, K // 16, K // 64
-    s_loads, b_loads, m_loads = BM * 64 // 1024 // waves, BN * 128 // 1024 // waves, BM * 8 // 256 // waves
+    s_loads, m_loads = BM * 64 // 1024 // waves, BM * 8 // 256 // waves
+    band_s, band_m = 64 * K, 8 * K
+
+    def band_rows(band):
+        return max(0, min(64, N - m0 - 64 * band))
+
     lane = np.arange(64)
-    worst = 0
+    s_out, m_out = [], []
     for wave in range(waves):
         for i in range(s_loads):
             r = 16 * (wave * s_loads + i) + lane // 4
-            off = r * Kh * 2 + ((lane % 4) ^ swz_s(r)) * 16
-            assert (off >= 0).all()
-            worst = max(worst, int(off.max()) + (nk - 1) * 64)
+            chunk = (lane % 4) ^ swz_s(r)
+            st = band_rows((wave * s_loads + i) // 4) * 64
+            assert (r // 64 == (wave * s_loads + i) // 4).all()
+            s_out.append((r, chunk, (r // 64) * band_s + (r % 64) * 64 + chunk * 16, st))
+        for i in range(m_loads):
+            r = 32 * (wave * m_loads + i) + lane // 2
+            st = band_rows((wave * m_loads + i) // 2) * 8
+            assert (r // 64 == (wave * m_loads + i) // 2).all()
+            m_out.append((r, lane % 2, (r // 64) * band_m + (r % 64) * 8 + (lane % 2) * 4, st))
+    return s_out, m_out
+
+
+def check_fast_loads(BM, BN, WM, WN, T, N, K, m0, n0):
+    """Direct-load offsets of one tile (int32 arithmetic) and its descriptors."""
+    waves = (BM // WM) * (BN // WN)
+    nk = K // 64
+    b_loads = BN * 128 // 1024 // waves
+    lane = np.arange(64)
+    s_out, m_out = fast_s_meta_offsets(BM, BN, WM, WN, N, K, m0)
+    worst = max(max(int(off.max()) + (nk - 1) * st for _, _, off, st in s_out),
+                max(int(off.max()) + (nk - 1) * st for _, _, off, st in m_out))
+    for wave in range(waves):
         for i in range(b_loads):
             r = 8 * (wave * b_loads + i) + lane // 8
             off = r * K * 2 + ((lane % 8) ^ swz_b(r)) * 16
             worst = max(worst, int(off.max()) + (nk - 1) * 128)
-        for i in range(m_loads):
-            r = 32 * (wave * m_loads + i) + lane // 2
-            worst = max(worst, int((r * Km * 2 + (lane % 2) * 4).max()) + (nk - 1) * 8)
     assert worst + 16 <= I32, "a direct-load offset overflows 32-bit arithmetic"
-    # descriptors: from this tile's first row to the operand's end
-    for base, rng, total in ((m0 * Kh * 2, (N - m0) * Kh * 2, N * Kh * 2), (n0 * K * 2, (T - n0) * K * 2, T * K * 2),
-                             (m0 * Km * 2, (N - m0) * Km * 2, N * Km * 2)):
+    # descriptors: from this tile's first row to the operand's end (S: N x K/2
+    # halves, meta: N x K/16 words, activations: T x K halves)
+    for base, rng, total in ((m0 * K, (N - m0) * K, N * K), (n0 * K * 2, (T - n0) * K * 2, T * K * 2),
+                             (m0 * K // 8, (N - m0) * K // 8, N * K // 8)):
         assert 0 <= base and base + rng == total and 0 < rng < U32
+
+
+def check_fast_form_loads(BM, BN, WM, WN, N_all, f0, N, K, m0):
+    """Each S and meta load of a tile at feature row m0 of a launch over rows
+    f0 .. f0+N of an N_all-row operand (a tail launch passes vals and meta
+    advanced by f0 rows) fetches, at every stage, the bytes the operand's
+    blocked order holds for its (row, chunk); rows past N start beyond the
+    descriptor's range (they load zeros)."""
+    nk = K // 64
+    ps, pm = blocked_positions(N_all, K // 2, VALS_BLOCK), blocked_positions(N_all, K // 16, META_BLOCK)
+    s_out, m_out = fast_s_meta_offsets(BM, BN, WM, WN, N, K, m0)
+    for kt in sorted({0, nk // 2, nk - 1}):
+        for r, chunk, off, st in s_out:
+            inside = m0 + r < N
+            want = ps[f0 + m0 + r[inside], 32 * kt + 8 * chunk[inside]] * 2
+            at = off + kt * st
+            assert (f0 * K + m0 * K + at[inside] == want).all(), "S load off its block"
+            # rows past N: whole 16-byte reads inside the operand, or past its end
+            past = at[~inside]
+            assert ((past + 16 <= (N - m0) * K) | (past >= (N - m0) * K)).all()
+        for r, dw, off, st in m_out:
+            inside = m0 + r < N
+            want = pm[f0 + m0 + r[inside], 4 * kt + 2 * dw[inside]] * 2
+            at = off + kt * st
+            assert ((f0 + m0) * K // 8 + at[inside] == want).all(), "meta load off its block"
+            past = at[~inside]
+            assert ((past + 4 <= (N - m0) * K // 8) | (past >= (N - m0) * K // 8)).all()
 
 
 def check_spmm(T, N, K):
@@ -158,6 +214,8 @@ def check_spmm(T, N, K):
             tiles_m, tiles_n = cdiv(nf, BM), cdiv(T, BN)
             tm, tn = check_tile_map(tiles_m, tiles_n)
             n_rel, m_rel = check_fast_tile_pattern(BM, BN, WM, WN)
+            for a in range(tiles_m):
+                check_fast_form_loads(BM, BN, WM, WN, N, f0, nf, K, a * BM)
             for a, b in zip(tm, tn):
                 m0, n0 = a * BM, b * BN
                 check_fast_loads(BM, BN, WM, WN, T, nf, K, m0, n0)
@@ -272,6 +330,23 @@ def check_weight_grad(T, R, C):
 TILE, THREADS, TILES_PER_WG = 128, 256, 1
 
 
+def form_off(r, c, n, m, b):
+    """sp24_internal.hpp's form_off: the offset of (r, c) of an n x m form
+    matrix in blocked order (bands of 64 rows, column blocks of width b)."""
+    r0, c0 = r & ~63, c & ~(b - 1)
+    h, w = np.minimum(64, n - r0), np.minimum(b, m - c0)
+    return r0 * m + c0 * h + (r - r0) * w + (c - c0)
+
+
+def full_tile_form_offsets(n, m, b, r0, c0s, r, g4, kk):
+    """write_full_tile's offset of row r0 + r + 32 kk, segment g4 of a form
+    matrix n x m (vals: segments of 8 halves, b = 32, c0s = c0 / 2; meta:
+    words, b = 4, c0s = c0 / 16)."""
+    seg = 8 if b == VALS_BLOCK else 1
+    inner = (g4 // 4) * 64 * b + r * b + seg * (g4 % 4)
+    return r0 * m + c0s * 64 + inner + (kk // 2) * 64 * m + (kk % 2) * 32 * b
+
+
 def check_search_compress(shapes):
     """One batched launch over `shapes`: tiles map onto jobs once, and the
     index, both values and both meta outputs of every job are written once."""
@@ -301,11 +376,22 @@ def check_search_compress(shapes):
         cv = cov[k]
         tid = np.arange(THREADS)
         if rows == TILE and cols == TILE:
-            # write_full_tile: segment tid % 8 of rows (columns) tid / 8 + 32 k
+            # write_full_tile: segment tid % 8 of rows (columns) tid / 8 + 32 k,
+            # at offsets that must be the blocked order's
             g4, r = tid % 8, tid // 8
             np.add.at(cv["idx"], (r0 // 4 + r, c0 // 16 + g4), 1)
+            pv_r, pm_r = blocked_positions(R, C // 2, VALS_BLOCK), blocked_positions(R, C // 16, META_BLOCK)
+            pv_c, pm_c = blocked_positions(C, R // 2, VALS_BLOCK), blocked_positions(C, R // 16, META_BLOCK)
             for kk in range(TILE // 32):
                 rr = r + 32 * kk
+                assert (full_tile_form_offsets(R, C // 2, VALS_BLOCK, r0, c0 // 2, r, g4, kk)
+                        == pv_r[r0 + rr, c0 // 2 + 8 * g4]).all()
+                assert (full_tile_form_offsets(R, C // 16, META_BLOCK, r0, c0 // 16, r, g4, kk)
+                        == pm_r[r0 + rr, c0 // 16 + g4]).all()
+                assert (full_tile_form_offsets(C, R // 2, VALS_BLOCK, c0, r0 // 2, r, g4, kk)
+                        == pv_c[c0 + rr, r0 // 2 + 8 * g4]).all()
+                assert (full_tile_form_offsets(C, R // 16, META_BLOCK, c0, r0 // 16, r, g4, kk)
+                        == pm_c[c0 + rr, r0 // 16 + g4]).all()
                 np.add.at(cv["vr"], (r0 + rr, c0 // 16 + g4), 1)
                 np.add.at(cv["mr"], (r0 + rr, c0 // 16 + g4), 1)
                 np.add.at(cv["vc"], (c0 + rr, r0 // 16 + g4), 1)
@@ -327,6 +413,40 @@ def check_search_compress(shapes):
 
 
 # ----------------------------------------------------------------------------
+# MVUE (sp24_mvue.hip): one workgroup of 256 lanes per two column blocks of a
+# 64-row band
+
+def check_mvue(rows, cols):
+    """Every meta word (and its 8 halves of vals) written once, at its
+    blocked-order position, and every lane's 16 entries inside the input."""
+    m = cols // 16
+    if rows == 0 or m == 0:
+        return
+    pairs, bands = cdiv(m, 8), cdiv(rows, 64)
+    pos = blocked_positions(rows, m, META_BLOCK)   # vals segments share meta's order
+    assert (blocked_positions(rows, cols // 2, VALS_BLOCK)[:, ::8] == pos * 8).all()
+    seen = np.zeros(rows * m, np.int8)
+    t = np.arange(256)
+    for b in range(bands * pairs):
+        band, pair = b // pairs, b % pairs
+        r0 = 64 * band
+        h = min(64, rows - r0)
+        for q in range(2):
+            j = 2 * pair + q
+            if 4 * j >= m:
+                break
+            w = min(4, m - 4 * j)
+            rr, cc = t // w, t % w
+            ok = rr < h
+            r, seg = r0 + rr[ok], 4 * j + cc[ok]
+            out = r0 * m + 4 * j * h + t[ok]
+            assert (out == pos[r, seg]).all()
+            assert (r * cols + 16 * seg + 16 <= rows * cols).all()
+            np.add.at(seen, out, 1)
+    assert (seen == 1).all()
+
+
+# ----------------------------------------------------------------------------
 # the shapes of the GPU tests and the benchmark
 
 FFN = [WL.GPT2_355M, WL.GPT2_774M, WL.GPT2_1P5B]
@@ -334,7 +454,8 @@ GEMMS = sorted({(T, N, K) for cfg in [WL.TINY] + FFN for _, T, N, K in cfg.gemm_
     (1, 16, 16), (7, 48, 80), (100, 272, 144), (129, 256, 512), (300, 528, 336), (256, 64, 4112), (300, 320, 192),
     (16347, 1152, 128), (16347, 1280, 128), (16347, 6400, 128), (16347, 128, 1152), (16347, 128, 1280),
     (16347, 128, 6400), (16384, 256, 65472), (16401, 256, 65472), (300, 272, 192), (37, 48, 80), (513, 528, 256),
-    (1000, 1040, 448), (96, 160, 192), (96, 192, 160)})
+    (1000, 1040, 448), (96, 160, 192), (96, 192, 160), (1, 32, 64), (100, 96, 128), (300, 544, 320),
+    (257, 256, 1024), (300, 32, 64)})
 
 
 @pytest.mark.parametrize("T,N,K", GEMMS)
@@ -373,3 +494,16 @@ def test_weight_grad_writes_and_loads(T, R, C):
                          ids=lambda s: "+".join(f"{r}x{c}" for r, c in s))
 def test_search_compress_writes(shapes):
     check_search_compress(shapes)
+
+
+@pytest.mark.parametrize("n,m,b", [(1, 1, 4), (3, 5, 4), (64, 32, 32), (65, 33, 32), (130, 40, 32), (200, 7, 4),
+                                   (6400, 800, 32), (1600, 400, 4), (16, 2, 4), (272, 72, 32)])
+def test_form_off_is_the_blocked_order(n, m, b):
+    r, c = np.meshgrid(np.arange(n), np.arange(m), indexing="ij")
+    assert (form_off(r, c, n, m, b) == blocked_positions(n, m, b)).all()
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 16), (7, 48), (33, 256), (64, 1024), (256, 512), (100, 144), (65, 80),
+                                       (16384, 6400), (2048, 1600)])
+def test_mvue_writes(rows, cols):
+    check_mvue(rows, cols)

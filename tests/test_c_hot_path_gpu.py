@@ -18,6 +18,8 @@ import pytest
 from oracle import sp24_oracle as O
 from structured_sparse_transformer_amd import workloads as WL
 
+from forms_layout import block_width, from_blocked
+
 pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -68,7 +70,7 @@ def test_plain_c_client_runs_the_hot_path(tmp_path, R, C, T):
     want = O.compress(W, idx)
     for k, dtype in (("vals_row", np.uint16), ("meta_row", np.uint16), ("vals_col", np.uint16),
                      ("meta_col", np.uint16)):
-        got = read(k, dtype, want[k].shape)
+        got = from_blocked(read(k, dtype, want[k].shape), block_width(k))
         assert (got == want[k].view(np.uint16)).all(), k
     if T == 0:
         return

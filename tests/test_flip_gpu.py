@@ -11,6 +11,7 @@ import pytest
 
 from oracle import sp24_oracle as O
 from structured_sparse_transformer_amd import workloads as WL
+from forms_layout import META_BLOCK, from_blocked
 
 pytestmark = pytest.mark.gpu
 
@@ -98,8 +99,8 @@ def test_fused_flips_in_place(sp):
     assert int(f.item()) == O.flip_count(i0, i1)
     assert (buf.cpu().numpy() == i1).all()
     c = O.compress(w1, i1)
-    assert (o["meta_row"].cpu().numpy().view(np.uint16) == c["meta_row"]).all()
-    assert (o["meta_col"].cpu().numpy().view(np.uint16) == c["meta_col"]).all()
+    assert (from_blocked(o["meta_row"].cpu().numpy().view(np.uint16), META_BLOCK) == c["meta_row"]).all()
+    assert (from_blocked(o["meta_col"].cpu().numpy().view(np.uint16), META_BLOCK) == c["meta_col"]).all()
 
 
 def test_fused_flips_shared_counter_and_bad_prev(sp):

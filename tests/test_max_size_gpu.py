@@ -15,6 +15,7 @@ import pytest
 from oracle import sp24_oracle as O
 from structured_sparse_transformer_amd import workloads as WL
 
+from forms_layout import forms_to_blocked
 from gpu_checks import Guarded, gemm_full
 
 pytestmark = pytest.mark.gpu
@@ -47,7 +48,8 @@ def forms():
     """The oracle's row form of a [256, 65472] weight, on the host and the GPU."""
     W = WL.normal_f16(SEED, 2, (N, K_BIG), 0.02)
     c = O.compress(W, O.mask_search(W))
-    return c, (torch.from_numpy(c["vals_row"]).cuda(), torch.from_numpy(c["meta_row"].view(np.int16)).cuda())
+    b = forms_to_blocked(c)   # the library's order
+    return c, (torch.from_numpy(b["vals_row"]).cuda(), torch.from_numpy(b["meta_row"].view(np.int16)).cuda())
 
 
 @pytest.mark.parametrize("T", [T_FAST, T_GENERIC])

@@ -1,7 +1,7 @@
 """GPU parity of the HIP path against the CPU oracle (needs an MI355X).
 
 Masks, indices, compressed values and metadata must match the oracle bit for
-bit.  GEMM outputs (fp16 in, fp32 accumulation, fp16 out) must be within a
+bit (the library's forms are taken out of their blocked order first).  GEMM outputs (fp16 in, fp32 accumulation, fp16 out) must be within a
 normwise max relative error of 1e-2 and a mean absolute error of 1e-3 of the
 oracle's float64 product.  Full-size GEMMs are checked element by element
 (the oracle runs over chunks of token rows), with the column-sum identity as
@@ -16,6 +16,7 @@ import pytest
 from oracle import sp24_oracle as O
 from structured_sparse_transformer_amd import workloads as WL
 
+from forms_layout import block_width, from_blocked
 from gpu_checks import Guarded, check_all, gemm_full, guarded_forms
 
 pytestmark = pytest.mark.gpu
@@ -54,7 +55,7 @@ def assert_forms_equal(got: dict, want: dict):
     for k in ("vals_row", "meta_row", "vals_col", "meta_col"):
         if k not in got:
             continue
-        g = host(got[k], np.uint16 if k.startswith("meta") else None)
+        g = from_blocked(host(got[k], np.uint16 if k.startswith("meta") else None), block_width(k))
         w = want[k]
         assert g.shape == w.shape, k
         bad = np.argwhere(bits(g) != bits(w))

@@ -14,6 +14,7 @@ import pytest
 from oracle import sp24_oracle as O
 from structured_sparse_transformer_amd import workloads as WL
 
+from forms_layout import META_BLOCK, VALS_BLOCK, from_blocked
 from gpu_checks import Guarded, gemm_full
 
 pytestmark = pytest.mark.gpu
@@ -83,8 +84,8 @@ def test_group_gpt2_1p5b_against_the_oracle(sp):
     outs = sp.sp24_spmm_group([(dev(A), v, m, None) for _, A, v, m, _, _, _ in prods])
     for (name, A, v, m, R, C, fwd), out in zip(prods, outs):
         print(f"group {name}", flush=True)
-        vals = v.cpu().numpy()
-        meta = m.cpu().numpy().view(np.uint16)
+        vals = from_blocked(v.cpu().numpy(), VALS_BLOCK)
+        meta = from_blocked(m.cpu().numpy().view(np.uint16), META_BLOCK)
         gemm_full(out, A, vals, meta, R, C, fwd)
 
 
