@@ -406,8 +406,8 @@ int sp24_geglu_bwd(const void* U, const void* dout, int64_t T, int64_t h, int64_
  *               of group g in order, and its nibble i | k << 2.  The sparse
  *               GEMMs accept it as their sparse operand.
  * Errors: NULL, SHAPE, ALIGN, LAUNCH; TOO_LARGE when a dimension reaches
- * 2^31, rows*cols reaches 2^40, or ceil(rows/64) * ceil(cols/128) > 2^24 - 1
- * (one workgroup of 256 work-items per 64 x 128 panel; one launch takes at
+ * 2^31, rows*cols reaches 2^40, or ceil(rows/64) * ceil(cols/256) > 2^24 - 1
+ * (one workgroup of 256 work-items per 64 x 256 panel; one launch takes at
  * most 2^32 - 256 work-items).
  */
 int sp24_mvue(const void* M, const float* U, int64_t rows, int64_t cols, void* vals, uint16_t* meta,

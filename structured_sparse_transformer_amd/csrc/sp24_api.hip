@@ -256,8 +256,8 @@ int sp24_mvue(const void* M, const float* U, int64_t rows, int64_t cols, void* v
   int st = check_dims(rows, cols, 1);
   if (st != SP24_OK) return st;
   if (cols % 16 != 0) return SP24_ERR_SHAPE;
-  // one workgroup of 256 per two 64 x 64 blocks of a 64-row band
-  if (((rows + 63) / 64) * ((cols / 16 + 7) / 8) > kMaxLaunchItems / 256) return SP24_ERR_TOO_LARGE;
+  // one workgroup of 256 per 64 x 256 region (four column blocks of a 64-row band)
+  if (((rows + 63) / 64) * ((cols / 16 + 15) / 16) > kMaxLaunchItems / 256) return SP24_ERR_TOO_LARGE;
   if (rows == 0 || cols == 0) return SP24_OK;
   if (M == nullptr || U == nullptr || vals == nullptr || meta == nullptr) return SP24_ERR_NULL;
   if (!aligned16(M) || !aligned16(U) || !aligned16(vals) || !aligned16(meta)) return SP24_ERR_ALIGN;

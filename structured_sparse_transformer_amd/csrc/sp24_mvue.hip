@@ -24,11 +24,11 @@
 // per group) and writes 1.125 bytes, against about 50 VALU operations per
 // group.  One lane handles 16 entries (one meta word, 8 halves of vals) with
 // 16-byte accesses.  In the blocked order a 64-row band's column block of 64
-// entries is 4 KB of vals and 512 B of meta, contiguous; a workgroup of 256
-// lanes takes two neighbouring blocks of a band, one after the other, so its
-// lanes write whole contiguous blocks and read whole 128-byte lines of the
-// gradient (each row's 64 entries) and of u (the two blocks' 16 uniforms
-// each).
+// entries is 4 KB of vals and 512 B of meta, contiguous, so the lanes are laid
+// out to keep both the gradient's reads and the forms' writes in long runs
+// (mvue_kernel).  The row-major output of the same kernel design ran about 6%
+// faster (69-71 against 72-78 us at 16384 x 6400): the price of handing the
+// sparse GEMM its operand order.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -117,32 +117,40 @@ __device__ __forceinline__ Pick mvue_group(const float (&a)[4], float u) {
   return r;
 }
 
-// Workgroup b: band b / pairs (rows 64 k ..), column blocks 2 (b % pairs) and
-// 2 (b % pairs) + 1 of that band (blocks of 4 meta words, 64 entries).  Lane t
-// of a block of h rows and w words takes row t / w, word t % w: its output is
-// the block's t-th element in blocked order.
+// Workgroup b: band b / regions (rows 64 k ..) and words 16 (b % regions) ..
+// + 15 of each of its rows, i.e. four column blocks, whose outputs are one
+// 16 KB run of vals.  Lane l of wave v takes word l % 16 of rows
+// 4 v + l / 16 + 16 i: each wave instruction reads 512 contiguous bytes of
+// the gradient from each of 4 rows and writes 256 contiguous bytes (4 rows)
+// into each of the 4 blocks.  (One block per workgroup, 16 rows x 128 B per
+// wave instruction, ran 10-15% slower; 2 rows x 1 KB, which writes 128-byte
+// runs, and one row of 2 KB, which writes 64-byte runs, slower still.)
+constexpr int kMvueWords = 16;   // words of a row per region
 __global__ __launch_bounds__(kMvueThreads) void mvue_kernel(const uint16_t* __restrict__ M, const float* __restrict__ U,
-                                                            int64_t rows, int64_t cols, int64_t pairs,
+                                                            int64_t rows, int64_t cols, uint32_t regions,
                                                             uint16_t* __restrict__ vals,
                                                             uint16_t* __restrict__ meta) {
-  const int64_t b = blockIdx.x, band = b / pairs, pair = b - band * pairs;
+  constexpr int kRowsPerWave = 64 / kMvueWords, kRowsPerPass = kRowsPerWave * (kMvueThreads / 64);
+  const uint32_t b = blockIdx.x, band = b / regions, reg = b - band * regions;
   const int64_t m = cols / 16;   // meta words (16-entry segments) per row
-  const int64_t r0 = 64 * band;
+  const int64_t r0 = 64 * (int64_t)band;
   const int h = (int)min<int64_t>(64, rows - r0);
-  const int t = threadIdx.x;
-#pragma unroll 1
-  for (int q = 0; q < 2; ++q) {
-    const int64_t j = 2 * pair + q;
-    if (4 * j >= m) break;
-    const int w = (int)min<int64_t>(4, m - 4 * j);
-    const int rr = w == 4 ? t >> 2 : t / w, cc = w == 4 ? t & 3 : t - (t / w) * w;
-    if (rr >= h) continue;
-    const int64_t r = r0 + rr, seg = 4 * j + cc;
-    const int64_t out = r0 * m + 4 * j * h + t;   // blocked-order index of (r, seg)
+  const int lane = (int)(threadIdx.x & 63), wave = (int)(threadIdx.x >> 6);
+  const int64_t seg = (int64_t)kMvueWords * reg + lane % kMvueWords;
+  if (seg >= m) return;
+  // the segment's column block j (4 words, w of them in a row's last block)
+  // and the blocked-order index of its row 0 in the band
+  const int64_t j = seg >> 2;
+  const int w = (int)min<int64_t>(4, m - 4 * j);
+  const int64_t blk = r0 * m + 4 * j * h + (seg & 3);
+#pragma unroll 2
+  for (int rr = wave * kRowsPerWave + lane / kMvueWords; rr < h; rr += kRowsPerPass) {
+    const int64_t r = r0 + rr;
+    const int64_t out = blk + (int64_t)rr * w;
     const u32x4* src = reinterpret_cast<const u32x4*>(M + r * cols + 16 * seg);
     const h8 lo = __builtin_bit_cast(h8, __builtin_nontemporal_load(src));
     const h8 hi = __builtin_bit_cast(h8, __builtin_nontemporal_load(src + 1));
-    const f32x4 us = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(U + r * (cols / 4) + 4 * seg));
+    const f32x4 us = *reinterpret_cast<const f32x4*>(U + r * (cols / 4) + 4 * seg);
     h8 o;
     uint32_t word = 0;
 #pragma unroll
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(kMvueThreads) void mvue_kernel(const uint16_t* __re
       o[2 * g + 1] = (_Float16)pk.vk;
       word |= pk.nib << (4 * g);
     }
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, o), reinterpret_cast<u32x4*>(vals) + out);
+    *(reinterpret_cast<u32x4*>(vals) + out) = __builtin_bit_cast(u32x4, o);
     meta[out] = (uint16_t)word;
   }
 }
@@ -165,9 +173,9 @@ __global__ __launch_bounds__(kMvueThreads) void mvue_kernel(const uint16_t* __re
 hipError_t launch_mvue(const uint16_t* M, const float* U, int64_t rows, int64_t cols, uint16_t* vals, uint16_t* meta,
                        hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
-  const int64_t pairs = (cols / 16 + 7) / 8, bands = (rows + 63) / 64;
-  hipLaunchKernelGGL(mvue_kernel, dim3((unsigned)(bands * pairs)), dim3(kMvueThreads), 0, s, M, U, rows, cols, pairs,
-                     vals, meta);
+  const int64_t regions = (cols / 16 + kMvueWords - 1) / kMvueWords, bands = (rows + 63) / 64;
+  hipLaunchKernelGGL(mvue_kernel, dim3((unsigned)(bands * regions)), dim3(kMvueThreads), 0, s, M, U, rows, cols,
+                     (uint32_t)regions, vals, meta);
   return hipGetLastError();
 }
 

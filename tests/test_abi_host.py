@@ -227,11 +227,12 @@ def test_mvue_validation(L):
     assert f(FAKE, FAKE, 4, 16, FAKE, NUL, NUL) == 1
     assert f(FAKE, MIS, 4, 16, FAKE, FAKE, NUL) == 3
     assert f(FAKE, FAKE, 1 << 31, 16, FAKE, FAKE, NUL) == 6
-    # one workgroup of 256 work-items per 64 x 128 panel, at most 2^32 - 256 work-items per launch
-    assert f(FAKE, FAKE, (1 << 30) - 64, 128, MIS, FAKE, NUL) == 3   # 2^24 - 1 panels: allowed
-    assert f(FAKE, FAKE, (1 << 30) - 63, 128, FAKE, FAKE, NUL) == 6  # a 2^24-th (partial) band
-    assert f(FAKE, FAKE, 1 << 29, 256, FAKE, FAKE, NUL) == 6         # 2^23 bands of 2 panels
-    assert f(FAKE, FAKE, 1 << 29, 240, MIS, FAKE, NUL) == 6          # 240 columns still take 2 panels
+    # one workgroup of 256 work-items per 64 x 256 panel, at most 2^32 - 256 work-items per launch
+    assert f(FAKE, FAKE, (1 << 30) - 64, 256, MIS, FAKE, NUL) == 3   # 2^24 - 1 panels: allowed
+    assert f(FAKE, FAKE, (1 << 30) - 63, 256, FAKE, FAKE, NUL) == 6  # a 2^24-th (partial) band
+    assert f(FAKE, FAKE, 1 << 29, 512, FAKE, FAKE, NUL) == 6         # 2^23 bands of 2 panels
+    assert f(FAKE, FAKE, 1 << 29, 272, MIS, FAKE, NUL) == 6          # 272 columns take 2 panels
+    assert f(FAKE, FAKE, (1 << 29) - 64, 512, MIS, FAKE, NUL) == 3   # 2^23 - 1 bands of 2 panels
     assert f(NUL, NUL, 0, 16, NUL, NUL, NUL) == 0
 
 

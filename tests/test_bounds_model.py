@@ -413,8 +413,8 @@ def check_search_compress(shapes):
 
 
 # ----------------------------------------------------------------------------
-# MVUE (sp24_mvue.hip): one workgroup of 256 lanes per two column blocks of a
-# 64-row band
+# MVUE (sp24_mvue.hip): one workgroup of 256 lanes per 16 words (four column
+# blocks) of a 64-row band
 
 def check_mvue(rows, cols):
     """Every meta word (and its 8 halves of vals) written once, at its
@@ -422,27 +422,31 @@ def check_mvue(rows, cols):
     m = cols // 16
     if rows == 0 or m == 0:
         return
-    pairs, bands = cdiv(m, 8), cdiv(rows, 64)
+    regions, bands = cdiv(m, 16), cdiv(rows, 64)
     pos = blocked_positions(rows, m, META_BLOCK)   # vals segments share meta's order
     assert (blocked_positions(rows, cols // 2, VALS_BLOCK)[:, ::8] == pos * 8).all()
     seen = np.zeros(rows * m, np.int8)
-    t = np.arange(256)
-    for b in range(bands * pairs):
-        band, pair = b // pairs, b % pairs
+    lane, wave = np.arange(256) % 64, np.arange(256) // 64
+    for b in range(bands * regions):
+        band, reg = b // regions, b % regions
         r0 = 64 * band
         h = min(64, rows - r0)
-        for q in range(2):
-            j = 2 * pair + q
-            if 4 * j >= m:
+        seg = 16 * reg + lane % 16
+        live = seg < m
+        j = seg >> 2
+        w = np.minimum(4, m - 4 * j)
+        blk = r0 * m + 4 * j * h + (seg & 3)
+        rr = wave * 4 + lane // 16
+        while True:
+            ok = live & (rr < h)
+            if not ok.any():
                 break
-            w = min(4, m - 4 * j)
-            rr, cc = t // w, t % w
-            ok = rr < h
-            r, seg = r0 + rr[ok], 4 * j + cc[ok]
-            out = r0 * m + 4 * j * h + t[ok]
-            assert (out == pos[r, seg]).all()
-            assert (r * cols + 16 * seg + 16 <= rows * cols).all()
+            r = r0 + rr[ok]
+            out = blk[ok] + rr[ok] * w[ok]
+            assert (out == pos[r, seg[ok]]).all()
+            assert (r * cols + 16 * seg[ok] + 16 <= rows * cols).all()
             np.add.at(seen, out, 1)
+            rr = rr + 16
     assert (seen == 1).all()
 
 
