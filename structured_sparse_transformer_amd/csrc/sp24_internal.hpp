@@ -40,6 +40,7 @@ struct ScJobs {
   ScJob j[kMaxScJobs];
   int count;
   int64_t total_tiles;
+  int cus;   // filled in by the launcher: the device's CU count
 };
 // Search (all jobs without idx_in) or compress with given masks (all jobs
 // with idx_in); R, C multiples of 16.

@@ -30,6 +30,7 @@
 #include <algorithm>
 #include <cstdint>
 
+#include "sp24_device.hpp"
 #include "sp24_internal.hpp"
 #include "sp24_patterns.hpp"
 
@@ -502,6 +503,17 @@ __global__ __launch_bounds__(kCompressThreads) void search_compress_kernel(ScJob
   const int64_t per_xcd = (ngroups + 7) / 8;
   const int64_t grp = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (grp >= ngroups) return;
+  // The first four workgroups of each CU (ids below 4 x CUs: the dispatcher
+  // fills one slot of every CU before the next) would otherwise all load,
+  // then all search, then all store in step, leaving HBM idle while the
+  // VALUs work and the reverse.  Starting slot k about k x 2 us late
+  // (4096 clocks each) interleaves those phases: 27.8 against 29.9 us for
+  // both 1.5B weights (kernel trace, median); 1 or 3 us per slot gave 28.0
+  // and 28.4 us.
+  if ((int64_t)blockIdx.x < 4 * (int64_t)jobs.cus) {
+    const int slot = (int)(blockIdx.x / (unsigned)jobs.cus);
+    for (int i = 0; i < slot; ++i) __builtin_amdgcn_s_sleep(64);
+  }
 
   TileRef tr[kTilesPerWg];
   TileData td[kTilesPerWg];
@@ -626,6 +638,7 @@ hipError_t launch_search_compress_jobs(ScJobs jobs, bool search, hipStream_t s) 
     total += ((jb.R + kTile - 1) / kTile) * jb.tiles_c;
   }
   jobs.total_tiles = total;
+  jobs.cus = (int)device_cu_count();
   if (total == 0) return hipSuccess;
   const int64_t groups = (total + kTilesPerWg - 1) / kTilesPerWg;
   const int64_t grid = ((groups + 7) / 8) * 8;
