@@ -333,10 +333,16 @@ int sp24_spmm_group_noalloc(const sp24_gemm* gemms, int count, void* stream);
  *   T, R, C        T >= 0; R, C >= 0, multiples of 16; T*R and T*C < 2^30
  *   dW        out  fp32 [R, C] (written, not accumulated).  T == 0 gives the
  *                  decay term alone (zeros without W).
- * Results are deterministic: every output element is reduced by one
- * workgroup in a fixed order.
+ * Results are deterministic.  Every output element is reduced in a fixed
+ * order by one workgroup, or, when the weight has too few tiles to fill the
+ * GPU (a GPT-2-1.5B FFN weight), by two: each sums one half of the tokens in
+ * a fixed order, and the second half's sum, stored in dW and announced by a
+ * flag, is added to the first half's (fp32 addition of two terms does not
+ * depend on their order).  The flags are library memory on each GPU (64
+ * sets, taken in turn by the calls that split, each left clear); up to 64
+ * such calls may overlap in time on one GPU.
  * Errors: NULL (also exactly one of W and idx given), SHAPE, ALIGN,
- * TOO_LARGE, LAUNCH.
+ * TOO_LARGE, LAUNCH (also when the flags' address cannot be had).
  */
 int sp24_weight_grad(const void* dY, const void* X, const void* W, const uint8_t* idx, float decay,
                      int64_t T, int64_t R, int64_t C, float* dW, void* stream);

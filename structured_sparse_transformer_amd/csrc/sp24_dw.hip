@@ -31,7 +31,20 @@
 // (one per SIMD) of WM x WN, K (tokens) in stages of 32 through a 3-stage
 // LDS ring filled two stages ahead.  Rows of dY/X past T read as zero (buffer
 // bounds); columns past R or C feed only outputs that are not stored.
+//
+// Token split: when a weight has too few tiles to fill the GPU (256 x 320
+// tiles of a GPT-2-1.5B FFN weight: 125 on 256 CUs), each tile runs as two
+// workgroups, one per half of the tokens.  The second half's workgroup (the
+// producer) stores its partial product into dW and raises the tile's flag;
+// the first half's (the consumer) waits for the flag, adds the stored partial
+// to its own and adds the decay term.  Two fp32 partials sum to the same
+// value in either order, so the result does not depend on timing.  Producer
+// and consumer of a tile are dealt to the same XCD, the producer with the
+// lower workgroup id: workgroups reach an XCD's CUs in id order, so a
+// consumer only starts once its producer has, and the wait always ends.  The
+// consumer's wait is bounded all the same (about 0.1 s).
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <cstdint>
 
 #include "sp24_device.hpp"
@@ -95,7 +108,8 @@ constexpr bool windows_disjoint(int row_bytes) {
     }
   return true;
 }
-static_assert(windows_disjoint(512) && windows_disjoint(320) && windows_disjoint(256), "bank-disjoint windows");
+static_assert(windows_disjoint(512) && windows_disjoint(320) && windows_disjoint(256) && windows_disjoint(640),
+              "bank-disjoint windows");
 
 // vmcnt wait (expcnt and lgkmcnt not waited for)
 template <int N>
@@ -103,22 +117,33 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Token-split roles
+enum : int { kWhole = 0, kConsumer = 1, kProducer = 2 };
+
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void weight_grad_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     const uint8_t* __restrict__ idx, float decay, int64_t T, int64_t R, int64_t C, float* __restrict__ dW,
-    int tiles_m, int tiles_n) {
+    int tiles_m, int tiles_n, int split, unsigned int* __restrict__ flags) {
   using Cfg = DwCfg<BM, BN, WM, WN>;
   __shared__ __align__(1024) unsigned char smem[Cfg::SMEM];
   MaskTable* masks = reinterpret_cast<MaskTable*>(smem + 3 * Cfg::STAGE);
 
   // tile order: groups of 8 row tiles, column tiles within a group; each XCD
-  // (workgroups are dealt round-robin to 8 XCDs) takes a contiguous run
+  // (workgroups are dealt round-robin to 8 XCDs) takes a contiguous run.
+  // Split: an XCD's first per_xcd workgroups are the producers of its run,
+  // the next per_xcd the consumers of the same tiles.
   constexpr int kGroupM = 8;
   const int ntiles = tiles_m * tiles_n;
   const int per_xcd = (ntiles + 7) / 8;
-  const int lin = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (lin >= ntiles) return;
+  const int xcd = (int)(blockIdx.x % 8), in_xcd = (int)(blockIdx.x / 8);
+  int role = kWhole, slot = in_xcd;
+  if (split) {
+    role = in_xcd < per_xcd ? kProducer : kConsumer;
+    slot = in_xcd < per_xcd ? in_xcd : in_xcd - per_xcd;
+  }
+  const int lin = xcd * per_xcd + slot;
+  if (slot >= per_xcd || lin >= ntiles) return;
   const int group = lin / (kGroupM * tiles_n);
   const int gm0 = group * kGroupM;
   const int gsize = min(kGroupM, tiles_m - gm0);
@@ -130,15 +155,19 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void weight_grad_ker
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % Cfg::WAVES_M, wn = wave / Cfg::WAVES_M;
-  const int nk = (int)((T + kBK - 1) / kBK);
+  // stages of 32 tokens: the consumer takes the first half, the producer the rest
+  const int nk_all = (int)((T + kBK - 1) / kBK);
+  const int k_lo = role == kProducer ? nk_all / 2 : 0;
+  const int nk = role == kWhole ? nk_all : role == kConsumer ? nk_all / 2 : nk_all - nk_all / 2;
+  const int64_t t0 = (int64_t)k_lo * kBK;
 
   if (tid < (int)(sizeof(MaskTable) / 4))
     reinterpret_cast<uint32_t*>(masks)[tid] = reinterpret_cast<const uint32_t*>(&g_masks)[tid];
 
-  // buffer descriptors from this tile's first column to the matrix end;
-  // bytes past it (token rows beyond T) load as zero
-  const i32x4 ra = make_rsrc(dY + m0, (uint32_t)((T * R - m0) * 2));
-  const i32x4 rb = make_rsrc(X + n0, (uint32_t)((T * C - n0) * 2));
+  // buffer descriptors from this tile's first column (at token t0) to the
+  // matrix end; bytes past it (token rows beyond T) load as zero
+  const i32x4 ra = make_rsrc(dY + t0 * R + m0, (uint32_t)(((T - t0) * R - m0) * 2));
+  const i32x4 rb = make_rsrc(X + t0 * C + n0, (uint32_t)(((T - t0) * C - n0) * 2));
 
   // This wave's direct loads: loads w, w + WAVES, ... of a stage.  Load j
   // fills LDS slots 64j .. 64j+63 (16 bytes each) of the stage, A rows first;
@@ -202,6 +231,12 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void weight_grad_ker
     b_off[nt] = Cfg::A_BYTES + krow * (2 * BN) + ((q + rot_slots(2 * BN, j4)) % n) * 16 + (c4 & 1) * 8;
   }
 
+  // With five row or column blocks (waves of 128 x 160 or 160 x 128) the 20
+  // accumulator tiles exceed the 256 accumulation registers: the fifth block
+  // runs as an asm MFMA with its accumulators in ordinary VGPRs (the compiler
+  // gives every MFMA builtin of a function the same register form).
+  constexpr bool kAsmN = Cfg::TN == 5, kAsmM = Cfg::TM == 5;
+  static_assert(Cfg::TM * Cfg::TN <= 16 || kAsmN || kAsmM, "accumulators beyond the AGPRs");
   f16v acc[Cfg::TM][Cfg::TN];
 #pragma unroll
   for (int i = 0; i < Cfg::TM; ++i)
@@ -240,7 +275,14 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void weight_grad_ker
     for (int mt = 0; mt < Cfg::TM; ++mt)
 #pragma unroll
       for (int nt = 0; nt < Cfg::TN; ++nt) {
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mt], f.b[nt], acc[mt][nt], 0, 0, 0);
+        if ((kAsmN && nt == 4) || (kAsmM && mt == 4)) {
+          // s_nop 1: wait states after a VALU write of the operands
+          asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
+                       : "+v"(acc[mt][nt])
+                       : "v"(f.a[mt]), "v"(f.b[nt]));
+        } else {
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a[mt], f.b[nt], acc[mt][nt], 0, 0, 0);
+        }
         const int u = mt * Cfg::TN + nt;
         if (u < Cfg::LOADS_HI && kt_load >= 0 && u < nl) issue_one(u, kt_load, slot_ring);
         __builtin_amdgcn_sched_barrier(0);
@@ -284,34 +326,114 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void weight_grad_ker
     }
   }
   __syncthreads();   // the mask table is visible (and the ring idle)
+  // the asm MFMAs' results are read by VALU below: 18 or more wait states
+  // after the last one
+  if constexpr (kAsmN || kAsmM) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // Epilogue: each group of four accumulators is rows r4 .. r4+3 (one mask
   // block row) of column c; add the decay term to the pruned entries.
   const int l32 = lane & 31, g = lane >> 5;
   const bool with_decay = W != nullptr;
+  unsigned int* const flag = split ? flags + lin : nullptr;
+  if (role == kProducer) {
+    // the raw partial of the second half of the tokens
+#pragma unroll
+    for (int mt = 0; mt < Cfg::TM; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < Cfg::TN; ++nt) {
+        const int64_t c = n0 + wn * WN + nt * 32 + l32;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int64_t r4 = m0 + wm * WM + mt * 32 + 8 * i4 + 4 * g;
+          if (r4 >= R || c >= C) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dW[(r4 + e) * C + c] = acc[mt][nt][4 * i4 + e];
+        }
+      }
+    // every wave's stores are done, then they are made visible device-wide
+    // before the flag goes up
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    __syncthreads();
+    if (tid == 0) {
+      __atomic_thread_fence(__ATOMIC_RELEASE);
+      // the L2 write-back the fence issues has completed before the flag is stored
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+      __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  if (role == kConsumer) {
+    if (tid == 0) {
+      // bounded: 25000 sleeps of about 8000 clocks
+      for (int spin = 0; spin < 25000; ++spin) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) break;
+        __builtin_amdgcn_s_sleep(127);
+      }
+      __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next launch
+    }
+    __syncthreads();
+    __atomic_thread_fence(__ATOMIC_ACQUIRE);
+  }
+  // The epilogue goes through the tile a 32-row block and two of its column
+  // blocks at a time: every load of such a group (the producer's partial, the
+  // block indices and W for the decay term) is issued before its first store,
+  // so they are in flight together.  Loaded one element group at a time, the
+  // consumer's epilogue took 170 us of a 480 us launch (its partial and W come
+  // from memory after the acquire).  Addresses are clamped into the matrix;
+  // values of elements outside it are loaded and never used.
+  constexpr int kHalf = 2;   // column blocks per group
 #pragma unroll
   for (int mt = 0; mt < Cfg::TM; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < Cfg::TN; ++nt) {
-      const int64_t c = n0 + wn * WN + nt * 32 + l32;
+    for (int part = 0; part < (Cfg::TN + kHalf - 1) / kHalf; ++part) {
+      float prev[kHalf][16];
+      uint32_t pat[kHalf][4];
+      uint16_t wv[kHalf][16];
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int64_t r4 = m0 + wm * WM + mt * 32 + 8 * i4 + 4 * g;
-        if (r4 >= R || c >= C) continue;
-        float v[4] = {acc[mt][nt][4 * i4], acc[mt][nt][4 * i4 + 1], acc[mt][nt][4 * i4 + 2], acc[mt][nt][4 * i4 + 3]};
-        if (with_decay) {
-          uint32_t p = idx[(r4 / 4) * (C / 4) + c / 4];
-          p = p < (uint32_t)kNumPatterns ? p : 0u;
-          const uint32_t kept = (uint32_t)masks->mask[p] >> (c & 3);
+      for (int h = 0; h < kHalf; ++h) {
+        const int nt = part * kHalf + h;
+        if (nt >= Cfg::TN) continue;
+        const int64_t c = min<int64_t>(n0 + wn * WN + nt * 32 + l32, C - 1);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (!((kept >> (4 * e)) & 1u)) {
-              const float w = (float)__builtin_bit_cast(_Float16, W[(r4 + e) * C + c]);
-              v[e] = v[e] + decay * w;
-            }
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int64_t r4 = min<int64_t>(m0 + wm * WM + mt * 32 + 8 * i4 + 4 * g, R - 4);
+          if (role == kConsumer) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) prev[h][4 * i4 + e] = dW[(r4 + e) * C + c];   // the producer's partial
+          }
+          if (with_decay) {
+            pat[h][i4] = idx[(r4 / 4) * (C / 4) + c / 4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[h][4 * i4 + e] = W[(r4 + e) * C + c];
+          }
         }
+      }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dW[(r4 + e) * C + c] = v[e];
+      for (int h = 0; h < kHalf; ++h) {
+        const int nt = part * kHalf + h;
+        if (nt >= Cfg::TN) continue;
+        const int64_t c = n0 + wn * WN + nt * 32 + l32;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int64_t r4 = m0 + wm * WM + mt * 32 + 8 * i4 + 4 * g;
+          if (r4 >= R || c >= C) continue;
+          float v[4] = {acc[mt][nt][4 * i4], acc[mt][nt][4 * i4 + 1], acc[mt][nt][4 * i4 + 2],
+                        acc[mt][nt][4 * i4 + 3]};
+          if (role == kConsumer) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += prev[h][4 * i4 + e];
+          }
+          if (with_decay) {
+            uint32_t p = pat[h][i4];
+            p = p < (uint32_t)kNumPatterns ? p : 0u;
+            const uint32_t kept = (uint32_t)masks->mask[p] >> (c & 3);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (!((kept >> (4 * e)) & 1u)) v[e] = v[e] + decay * (float)__builtin_bit_cast(_Float16, wv[h][4 * i4 + e]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dW[(r4 + e) * C + c] = v[e];
+        }
       }
     }
 }
@@ -322,13 +444,41 @@ struct DwShape {
 
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_dw(const uint16_t* dY, const uint16_t* X, const uint16_t* W, const uint8_t* idx, float decay,
-                     int64_t T, int64_t R, int64_t C, float* dW, hipStream_t s) {
+                     int64_t T, int64_t R, int64_t C, float* dW, hipStream_t s, unsigned int* flags = nullptr) {
   using Cfg = DwCfg<BM, BN, WM, WN>;
   const int tiles_m = (int)((R + BM - 1) / BM), tiles_n = (int)((C + BN - 1) / BN);
-  const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
+  const int per_xcd = (tiles_m * tiles_n + 7) / 8;
+  const int split = flags != nullptr ? 1 : 0;
+  const int grid = 8 * per_xcd * (split ? 2 : 1);
   hipLaunchKernelGGL((weight_grad_kernel<BM, BN, WM, WN>), dim3(grid), dim3(Cfg::THREADS), 0, s, dY, X, W, idx, decay,
-                     T, R, C, dW, tiles_m, tiles_n);
+                     T, R, C, dW, tiles_m, tiles_n, split, flags);
   return hipGetLastError();
+}
+
+// Tile flags of the token split: 64 sets of kDwFlagTiles words in the library,
+// one copy per GPU (zero when the library is loaded; each consumer clears its
+// tile's flag).  Launches take the sets in turn, so launches that run at the
+// same time on one GPU (from different streams) use different sets unless 64
+// of them overlap.  The device address comes from hipGetSymbolAddress, looked
+// up once per device with that device current.
+constexpr int kDwFlagSets = 64, kDwFlagTiles = 256;
+__device__ __align__(256) unsigned int dw_flags[kDwFlagSets * kDwFlagTiles];
+
+hipError_t dw_flag_set(unsigned int** out) {
+  static std::atomic<unsigned int*> ptrs[64];
+  static std::atomic<unsigned int> next{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  unsigned int* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(reinterpret_cast<void**>(&p), HIP_SYMBOL(dw_flags));
+    if (e != hipSuccess) return e;
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  *out = p + (size_t)(next.fetch_add(1, std::memory_order_relaxed) % kDwFlagSets) * kDwFlagTiles;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -338,28 +488,49 @@ hipError_t launch_weight_grad(const uint16_t* dY, const uint16_t* X, const uint1
   if (R == 0 || C == 0) return hipSuccess;
   // Tile shape: each candidate's time is modelled as (rounds of one tile per
   // CU) x (tile area / relative speed of the shape); the cheapest wins.  The
-  // 256 x 160 shapes fill 256 CUs with a GPT-2-1.5B FFN weight (6400 x 1600)
-  // in one round, which a 256 x 256 tile leaves 32 % idle.
+  // 256 x 320 and 320 x 256 tiles (waves of 128 x 160 or 160 x 128, the fewest
+  // LDS bytes per MFMA) may split the tokens in two when twice their tiles
+  // still fit on the CUs: a GPT-2-1.5B FFN weight (6400 x 1600 or 1600 x 6400)
+  // is 125 such tiles, 250 workgroups on 256 CUs.
   struct Cand {
     int bm, bn;
     double speed;
+    bool splittable;
   };
-  const Cand cands[] = {{256, 256, 1.0}, {256, 160, 0.9}, {160, 256, 0.9}, {128, 128, 0.75}};
+  const Cand cands[] = {{256, 256, 1.0, false}, {256, 320, 0.97, true}, {320, 256, 0.97, true},
+                        {256, 160, 0.9, false}, {160, 256, 0.9, false}, {128, 128, 0.75, false}};
+  constexpr int kCands = sizeof(cands) / sizeof(cands[0]);
   const int64_t cus = device_cu_count();
+  const int64_t stages = (T + kBK - 1) / kBK;
   int best = 0;
+  bool best_split = false;
   double best_t = 0.0;
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kCands; ++k) {
     const int64_t tiles = ((R + cands[k].bm - 1) / cands[k].bm) * ((C + cands[k].bn - 1) / cands[k].bn);
-    const double t = (double)((tiles + cus - 1) / cus) * cands[k].bm * cands[k].bn / cands[k].speed;
+    const double area = (double)cands[k].bm * cands[k].bn / cands[k].speed;
+    double t = (double)((tiles + cus - 1) / cus) * area;
+    bool split = false;
+    if (cands[k].splittable && 2 * tiles <= cus && tiles <= kDwFlagTiles && stages >= 2 && area / 2 < t) {
+      t = area / 2;
+      split = true;
+    }
     if (k == 0 || t < best_t) {
       best = k;
       best_t = t;
+      best_split = split;
     }
+  }
+  unsigned int* flags = nullptr;
+  if (best_split) {
+    const hipError_t e = dw_flag_set(&flags);
+    if (e != hipSuccess) return e;
   }
   switch (best) {
     case 0: return launch_dw<256, 256, 128, 128>(dY, X, W, idx, decay, T, R, C, dW, s);
-    case 1: return launch_dw<256, 160, 64, 160>(dY, X, W, idx, decay, T, R, C, dW, s);
-    case 2: return launch_dw<160, 256, 160, 64>(dY, X, W, idx, decay, T, R, C, dW, s);
+    case 1: return launch_dw<256, 320, 128, 160>(dY, X, W, idx, decay, T, R, C, dW, s, flags);
+    case 2: return launch_dw<320, 256, 160, 128>(dY, X, W, idx, decay, T, R, C, dW, s, flags);
+    case 3: return launch_dw<256, 160, 64, 160>(dY, X, W, idx, decay, T, R, C, dW, s);
+    case 4: return launch_dw<160, 256, 160, 64>(dY, X, W, idx, decay, T, R, C, dW, s);
     default: return launch_dw<128, 128, 64, 64>(dY, X, W, idx, decay, T, R, C, dW, s);
   }
 }

@@ -274,22 +274,63 @@ def group_queues(jobs):
 # ----------------------------------------------------------------------------
 # weight gradient (sp24_dw.hip)
 
-DW_SHAPES = [(256, 256, 128, 128, 1.0), (256, 160, 64, 160, 0.9), (160, 256, 160, 64, 0.9), (128, 128, 64, 64, 0.75)]
+# (BM, BN, WM, WN, relative speed, may split the tokens)
+DW_SHAPES = [(256, 256, 128, 128, 1.0, False), (256, 320, 128, 160, 0.97, True), (320, 256, 160, 128, 0.97, True),
+             (256, 160, 64, 160, 0.9, False), (160, 256, 160, 64, 0.9, False), (128, 128, 64, 64, 0.75, False)]
+DW_FLAG_TILES = 256
 
 
-def dw_shape(R, C):
-    best, best_t = None, 0.0
-    for k, (bm, bn, wm, wn, speed) in enumerate(DW_SHAPES):
-        t = cdiv(cdiv(R, bm) * cdiv(C, bn), CUS) * bm * bn / speed
+def dw_shape(T, R, C):
+    """launch_weight_grad's choice: (BM, BN, WM, WN, split)."""
+    best, best_t, best_split = None, 0.0, False
+    stages = cdiv(T, 32)
+    for k, (bm, bn, wm, wn, speed, splittable) in enumerate(DW_SHAPES):
+        tiles = cdiv(R, bm) * cdiv(C, bn)
+        area = bm * bn / speed
+        t = cdiv(tiles, CUS) * area
+        split = False
+        if splittable and 2 * tiles <= CUS and tiles <= DW_FLAG_TILES and stages >= 2 and area / 2 < t:
+            t, split = area / 2, True
         if best is None or t < best_t:
-            best, best_t = k, t
-    return DW_SHAPES[best][:4]
+            best, best_t, best_split = k, t, split
+    return DW_SHAPES[best][:4] + (best_split,)
+
+
+def dw_roles(tiles_m, tiles_n, split):
+    """weight_grad_kernel's workgroup -> (tile, role) map: role 0 whole, 1 the
+    first half of the tokens (consumer), 2 the second half (producer)."""
+    ntiles = tiles_m * tiles_n
+    per_xcd = cdiv(ntiles, 8)
+    grid = 8 * per_xcd * (2 if split else 1)
+    out = []
+    for b in range(grid):
+        xcd, in_xcd = b % 8, b // 8
+        role, slot = 0, in_xcd
+        if split:
+            role, slot = (2, in_xcd) if in_xcd < per_xcd else (1, in_xcd - per_xcd)
+        lin = xcd * per_xcd + slot
+        if slot < per_xcd and lin < ntiles:
+            out.append((b, lin, role))
+    return out
 
 
 def check_weight_grad(T, R, C):
-    BM, BN, WM, WN = dw_shape(R, C)
+    BM, BN, WM, WN, split = dw_shape(T, R, C)
     tiles_m, tiles_n = cdiv(R, BM), cdiv(C, BN)
     tm, tn = check_tile_map(tiles_m, tiles_n)
+    roles = dw_roles(tiles_m, tiles_n, split)
+    # every tile once (whole), or once as producer and once as consumer, with
+    # the producer on the same XCD and a lower workgroup id
+    per_tile = {}
+    for b, lin, role in roles:
+        per_tile.setdefault(lin, []).append((role, b))
+    assert sorted(per_tile) == list(range(tiles_m * tiles_n))
+    for lin, rs in per_tile.items():
+        if split:
+            (r1, b1), (r2, b2) = sorted(rs)
+            assert (r1, r2) == (1, 2) and b2 < b1 and b1 % 8 == b2 % 8
+        else:
+            assert [r for r, _ in rs] == [0]
     waves = (BM // WM) * (BN // WN)
     lane = np.arange(64)
     l32, g = lane & 31, lane >> 5
@@ -306,22 +347,32 @@ def check_weight_grad(T, R, C):
     np.add.at(quad, (rel_r // 4, rel_c), 1)
     assert (quad == 1).all(), "the weight-gradient epilogue does not cover its tile once"
     cover = np.zeros((R // 4, C), np.int8)
-    nk = cdiv(T, 32)
-    for a, b in zip(tm, tn):
+    nk_all = cdiv(T, 32)
+    lm, ln = group_order(np.arange(tiles_m * tiles_n), tiles_m, tiles_n)   # the kernel's lin -> tile
+    for lin in range(tiles_m * tiles_n):
+        a, b = int(lm[lin]), int(ln[lin])
         m0, n0 = a * BM, b * BN
         r4, c = m0 + rel_r, n0 + rel_c
         ok = (r4 < R) & (c < C)
         assert (r4[ok] + 4 <= R).all()
-        np.add.at(cover, (r4[ok] // 4, c[ok]), 1)
-        # direct loads: 32 token rows per stage, rows of the tile's columns;
+        np.add.at(cover, (r4[ok] // 4, c[ok]), 1)   # the final store (whole or consumer)
+        # direct loads of each role: 32 token rows per stage from token t0 on,
         # offsets row*R*2 + slot*16 + kt*32*R*2 in 32-bit arithmetic
-        if T:
+        ranges = [(0, nk_all)] if not split else [(0, nk_all // 2), (nk_all // 2, nk_all - nk_all // 2)]
+        assert sum(n for _, n in ranges) == nk_all
+        for k_lo, nk in ranges:
+            if T == 0 or nk == 0:
+                continue
+            t0 = k_lo * 32
             worst_a = 31 * R * 2 + (BM // 8 - 1) * 16 + (nk - 1) * 32 * R * 2
             worst_b = 31 * C * 2 + (BN // 8 - 1) * 16 + (nk - 1) * 32 * C * 2
             assert max(worst_a, worst_b) + 16 <= I32
-            for base, rng, total in ((m0 * 2, (T * R - m0) * 2, T * R * 2), (n0 * 2, (T * C - n0) * 2, T * C * 2)):
+            for base, rng, total in (((t0 * R + m0) * 2, ((T - t0) * R - m0) * 2, T * R * 2),
+                                     ((t0 * C + n0) * 2, ((T - t0) * C - n0) * 2, T * C * 2)):
                 assert base + rng == total and 0 < rng < U32
     assert (cover == 1).all()
+    if split:
+        assert tiles_m * tiles_n <= DW_FLAG_TILES
 
 
 # ----------------------------------------------------------------------------
@@ -487,9 +538,16 @@ def test_grouped_queues_cover_every_tile_once(cfg):
 @pytest.mark.parametrize("T,R,C", sorted({(T, R, C) for cfg in FFN for (T, R, C) in
                                           ((cfg.tokens, cfg.dff, cfg.d), (cfg.tokens, cfg.d, cfg.dff))} | {
     (1, 16, 16), (33, 272, 144), (100, 528, 336), (700, 256, 160), (64, 1040, 656), (2048, 4096, 4096),
-    (16384, 65520, 16), (0, 272, 400), (16384, 1600, 3200)}))
+    (16384, 65520, 16), (0, 272, 400), (16384, 1600, 3200), (16384, 4096, 5120), (1000, 6400, 1600),
+    (33, 1600, 6400), (32, 6400, 1600)}))
 def test_weight_grad_writes_and_loads(T, R, C):
     check_weight_grad(T, R, C)
+
+
+def test_weight_grad_splits_the_gpt2_1p5b_weights():
+    assert dw_shape(16384, 6400, 1600) == (256, 320, 128, 160, True)
+    assert dw_shape(16384, 1600, 6400) == (320, 256, 160, 128, True)
+    assert dw_shape(32, 6400, 1600)[4] is False   # one stage of tokens: nothing to split
 
 
 @pytest.mark.parametrize("shapes", [[(64, 64)], [(4096, 4096)], [(6400, 1600), (1600, 6400)],

@@ -9,6 +9,8 @@ error of 1e-4 (a dropped token, sign or operand shows up far above it) and a
 mean absolute error of 1e-5 of the mean magnitude.  The decay term alone
 (T = 0) must match to one fp32 rounding.  Full-size outputs are checked in
 full against the oracle, inside guard bands, plus a column-sum identity.
+With the two-way token split the two halves' fp32 sums are added once more;
+the error model above covers that rounding.
 """
 import numpy as np
 import pytest
@@ -105,6 +107,45 @@ def test_weight_grad_deterministic(sp):
     b = sp.sp24_weight_grad(dev(dY), dev(X), dev(W), dev(idx), 0.1)
     assert torch.equal(a, b)
     check(a.cpu().numpy(), O.weight_grad(dY, X, W, idx, 0.1))
+
+
+@pytest.mark.parametrize("T,R,C", [(976, 2048, 2560), (40, 2048, 2560), (1000, 2560, 2048)])
+def test_weight_grad_token_split(sp, T, R, C):
+    """Shapes whose 256 x 320 tiles take the two-way token split: an odd
+    number of 32-token stages (31: the first half gets 15, the second 16),
+    two stages, and ragged column tiles (2048 = 6 x 320 + 128).  Every
+    element against the oracle inside guard bands, and the same bits on a
+    second call (the halves meet through a flag; their sum does not depend on
+    which finishes first)."""
+    dY, X, W = inputs(T + R + C, T, R, C, 0.02)
+    idx = O.mask_search(W)
+    g = Guarded((R, C), torch.float32)
+    sp.sp24_weight_grad(dev(dY), dev(X), dev(W), dev(idx), 0.05, dW=g.t)
+    g.check("dW")
+    got = g.t.cpu().numpy()
+    check(got, O.weight_grad(dY, X, W, idx, 0.05))
+    again = sp.sp24_weight_grad(dev(dY), dev(X), dev(W), dev(idx), 0.05)
+    assert torch.equal(again, g.t)
+
+
+def test_weight_grad_token_split_on_two_streams(sp):
+    """Split launches of two weights in flight together on two streams (they
+    take different sets of tile flags), then again in the other order."""
+    T, R, C = 976, 2048, 2560
+    cases = [inputs(70 + k, T, R, C, 0.02) for k in range(2)]
+    idxs = [O.mask_search(W) for _, _, W in cases]
+    devs = [(dev(dY), dev(X), dev(W), dev(i)) for (dY, X, W), i in zip(cases, idxs)]
+    wants = [O.weight_grad(dY, X, W, i, 0.05) for (dY, X, W), i in zip(cases, idxs)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for order in ((0, 1), (1, 0)):
+        outs = [torch.empty(R, C, dtype=torch.float32, device="cuda") for _ in range(2)]
+        torch.cuda.synchronize()
+        for k in order:
+            with torch.cuda.stream(streams[k]):
+                sp.sp24_weight_grad(*devs[k][:3], devs[k][3], 0.05, dW=outs[k])
+        torch.cuda.synchronize()
+        for k in range(2):
+            check(outs[k].cpu().numpy(), wants[k])
 
 
 def _column_sums(got, dY, X, W, idx, decay):
