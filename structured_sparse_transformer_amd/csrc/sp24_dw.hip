@@ -510,7 +510,12 @@ hipError_t launch_weight_grad(const uint16_t* dY, const uint16_t* X, const uint1
     const double area = (double)cands[k].bm * cands[k].bn / cands[k].speed;
     double t = (double)((tiles + cus - 1) / cus) * area;
     bool split = false;
-    if (cands[k].splittable && 2 * tiles <= cus && tiles <= kDwFlagTiles && stages >= 2 && area / 2 < t) {
+    // split only whole tiles that fill at least three quarters of the CUs
+    // with their halves: a 1600 x 3200 weight (70 ragged 256 x 320 tiles, 140
+    // workgroups) took 310 us split against 274 us as 325 128 x 128 tiles
+    const bool whole = R % cands[k].bm == 0 && C % cands[k].bn == 0;
+    if (cands[k].splittable && whole && 2 * tiles <= cus && 8 * tiles >= 3 * cus && tiles <= kDwFlagTiles &&
+        stages >= 2 && area / 2 < t) {
       t = area / 2;
       split = true;
     }

@@ -289,7 +289,9 @@ def dw_shape(T, R, C):
         area = bm * bn / speed
         t = cdiv(tiles, CUS) * area
         split = False
-        if splittable and 2 * tiles <= CUS and tiles <= DW_FLAG_TILES and stages >= 2 and area / 2 < t:
+        whole = R % bm == 0 and C % bn == 0
+        if (splittable and whole and 2 * tiles <= CUS and 8 * tiles >= 3 * CUS and tiles <= DW_FLAG_TILES
+                and stages >= 2 and area / 2 < t):
             t, split = area / 2, True
         if best is None or t < best_t:
             best, best_t, best_split = k, t, split
@@ -539,7 +541,7 @@ def test_grouped_queues_cover_every_tile_once(cfg):
                                           ((cfg.tokens, cfg.dff, cfg.d), (cfg.tokens, cfg.d, cfg.dff))} | {
     (1, 16, 16), (33, 272, 144), (100, 528, 336), (700, 256, 160), (64, 1040, 656), (2048, 4096, 4096),
     (16384, 65520, 16), (0, 272, 400), (16384, 1600, 3200), (16384, 4096, 5120), (1000, 6400, 1600),
-    (33, 1600, 6400), (32, 6400, 1600)}))
+    (33, 1600, 6400), (32, 6400, 1600), (976, 3072, 2560), (40, 3072, 2560), (976, 2560, 3072)}))
 def test_weight_grad_writes_and_loads(T, R, C):
     check_weight_grad(T, R, C)
 
@@ -548,6 +550,8 @@ def test_weight_grad_splits_the_gpt2_1p5b_weights():
     assert dw_shape(16384, 6400, 1600) == (256, 320, 128, 160, True)
     assert dw_shape(16384, 1600, 6400) == (320, 256, 160, 128, True)
     assert dw_shape(32, 6400, 1600)[4] is False   # one stage of tokens: nothing to split
+    assert dw_shape(16384, 1600, 3200)[4] is False   # ragged 256 x 320 tiles: not split
+    assert dw_shape(16384, 4096, 5120) == (256, 320, 128, 160, False)   # one full round unsplit
 
 
 @pytest.mark.parametrize("shapes", [[(64, 64)], [(4096, 4096)], [(6400, 1600), (1600, 6400)],

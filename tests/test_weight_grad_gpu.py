@@ -109,14 +109,14 @@ def test_weight_grad_deterministic(sp):
     check(a.cpu().numpy(), O.weight_grad(dY, X, W, idx, 0.1))
 
 
-@pytest.mark.parametrize("T,R,C", [(976, 2048, 2560), (40, 2048, 2560), (1000, 2560, 2048)])
+@pytest.mark.parametrize("T,R,C", [(976, 3072, 2560), (40, 3072, 2560), (976, 2560, 3072)])
 def test_weight_grad_token_split(sp, T, R, C):
-    """Shapes whose 256 x 320 tiles take the two-way token split: an odd
-    number of 32-token stages (31: the first half gets 15, the second 16),
-    two stages, and ragged column tiles (2048 = 6 x 320 + 128).  Every
-    element against the oracle inside guard bands, and the same bits on a
-    second call (the halves meet through a flag; their sum does not depend on
-    which finishes first)."""
+    """Shapes whose tiles take the two-way token split (96 whole 256 x 320 or
+    320 x 256 tiles, 192 workgroups): an odd number of 32-token stages (31:
+    the first half gets 15, the second 16) and two stages.  Every element
+    against the oracle inside guard bands, and the same bits on a second call
+    (the halves meet through a flag; their sum does not depend on which
+    finishes first)."""
     dY, X, W = inputs(T + R + C, T, R, C, 0.02)
     idx = O.mask_search(W)
     g = Guarded((R, C), torch.float32)
@@ -131,7 +131,7 @@ def test_weight_grad_token_split(sp, T, R, C):
 def test_weight_grad_token_split_on_two_streams(sp):
     """Split launches of two weights in flight together on two streams (they
     take different sets of tile flags), then again in the other order."""
-    T, R, C = 976, 2048, 2560
+    T, R, C = 976, 3072, 2560
     cases = [inputs(70 + k, T, R, C, 0.02) for k in range(2)]
     idxs = [O.mask_search(W) for _, _, W in cases]
     devs = [(dev(dY), dev(X), dev(W), dev(i)) for (dY, X, W), i in zip(cases, idxs)]
