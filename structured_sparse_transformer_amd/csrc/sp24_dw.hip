@@ -38,11 +38,14 @@
 // producer) stores its partial product into dW and raises the tile's flag;
 // the first half's (the consumer) waits for the flag, adds the stored partial
 // to its own and adds the decay term.  Two fp32 partials sum to the same
-// value in either order, so the result does not depend on timing.  Producer
-// and consumer of a tile are dealt to the same XCD, the producer with the
-// lower workgroup id: workgroups reach an XCD's CUs in id order, so a
-// consumer only starts once its producer has, and the wait always ends.  The
-// consumer's wait is bounded all the same (about 0.1 s).
+// value in either order, so the result does not depend on timing.  Producers
+// never wait; they run on XCDs 0-3 and the consumers on XCDs 4-7 (workgroup
+// id modulo 8), so a waiting consumer never holds a CU its producer needs,
+// and the wait always ends.  Were all workgroups to reach a single queue, a
+// producer's id is still the lower (by 4), and workgroups start in id order.  An XCD then computes twice the
+// tiles over half the tokens, whose operand strips are fewer bytes than those
+// of half the tiles over all of them.  The consumer's wait is bounded all the
+// same (about 0.1 s).
 #include <hip/hip_runtime.h>
 #include <atomic>
 #include <cstdint>
@@ -129,27 +132,41 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), 1) void weight_grad_ker
   __shared__ __align__(1024) unsigned char smem[Cfg::SMEM];
   MaskTable* masks = reinterpret_cast<MaskTable*>(smem + 3 * Cfg::STAGE);
 
-  // tile order: groups of 8 row tiles, column tiles within a group; each XCD
-  // (workgroups are dealt round-robin to 8 XCDs) takes a contiguous run.
-  // Split: an XCD's first per_xcd workgroups are the producers of its run,
-  // the next per_xcd the consumers of the same tiles.
-  constexpr int kGroupM = 8;
+  // Workgroups are dealt round-robin to the 8 XCDs; each XCD takes a
+  // contiguous run of tiles.  Whole tiles: runs of ceil(tiles/8) in groups of
+  // 8 row tiles, column tiles within a group.  Split: XCD x < 4 runs the
+  // producers of run x (ceil(tiles/4) tiles), XCD x + 4 their consumers, both
+  // over half the tokens, with the tiles taken across the grid's shorter side
+  // first, so that each XCD's L2 fetches the operand strips of a compact block.
   const int ntiles = tiles_m * tiles_n;
-  const int per_xcd = (ntiles + 7) / 8;
   const int xcd = (int)(blockIdx.x % 8), in_xcd = (int)(blockIdx.x / 8);
-  int role = kWhole, slot = in_xcd;
+  int role = kWhole, lin, tm, tn;
   if (split) {
-    role = in_xcd < per_xcd ? kProducer : kConsumer;
-    slot = in_xcd < per_xcd ? in_xcd : in_xcd - per_xcd;
+    const int per_run = (ntiles + 3) / 4;
+    role = xcd < 4 ? kProducer : kConsumer;
+    lin = (xcd % 4) * per_run + in_xcd;
+    if (in_xcd >= per_run || lin >= ntiles) return;
+    if (tiles_n <= tiles_m) {
+      tm = lin / tiles_n;
+      tn = lin % tiles_n;
+    } else {
+      tn = lin / tiles_m;
+      tm = lin % tiles_m;
+    }
+  } else {
+    constexpr int kGroupM = 8;
+    const int per_xcd = (ntiles + 7) / 8;
+    lin = xcd * per_xcd + in_xcd;
+    if (in_xcd >= per_xcd || lin >= ntiles) return;
+    const int group = lin / (kGroupM * tiles_n);
+    const int gm0 = group * kGroupM;
+    const int gsize = min(kGroupM, tiles_m - gm0);
+    const int in_group = lin - group * kGroupM * tiles_n;
+    tn = in_group / gsize;
+    tm = gm0 + in_group % gsize;
   }
-  const int lin = xcd * per_xcd + slot;
-  if (slot >= per_xcd || lin >= ntiles) return;
-  const int group = lin / (kGroupM * tiles_n);
-  const int gm0 = group * kGroupM;
-  const int gsize = min(kGroupM, tiles_m - gm0);
-  const int in_group = lin - group * kGroupM * tiles_n;
-  const int tn = __builtin_amdgcn_readfirstlane(in_group / gsize);
-  const int tm = __builtin_amdgcn_readfirstlane(gm0 + in_group % gsize);
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tn = __builtin_amdgcn_readfirstlane(tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
   const int tid = threadIdx.x;
@@ -447,9 +464,8 @@ hipError_t launch_dw(const uint16_t* dY, const uint16_t* X, const uint16_t* W, c
                      int64_t T, int64_t R, int64_t C, float* dW, hipStream_t s, unsigned int* flags = nullptr) {
   using Cfg = DwCfg<BM, BN, WM, WN>;
   const int tiles_m = (int)((R + BM - 1) / BM), tiles_n = (int)((C + BN - 1) / BN);
-  const int per_xcd = (tiles_m * tiles_n + 7) / 8;
   const int split = flags != nullptr ? 1 : 0;
-  const int grid = 8 * per_xcd * (split ? 2 : 1);
+  const int grid = 8 * (split ? (tiles_m * tiles_n + 3) / 4 : (tiles_m * tiles_n + 7) / 8);
   hipLaunchKernelGGL((weight_grad_kernel<BM, BN, WM, WN>), dim3(grid), dim3(Cfg::THREADS), 0, s, dY, X, W, idx, decay,
                      T, R, C, dW, tiles_m, tiles_n, split, flags);
   return hipGetLastError();

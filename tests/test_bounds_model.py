@@ -302,27 +302,47 @@ def dw_roles(tiles_m, tiles_n, split):
     """weight_grad_kernel's workgroup -> (tile, role) map: role 0 whole, 1 the
     first half of the tokens (consumer), 2 the second half (producer)."""
     ntiles = tiles_m * tiles_n
-    per_xcd = cdiv(ntiles, 8)
-    grid = 8 * per_xcd * (2 if split else 1)
+    per_run = cdiv(ntiles, 4 if split else 8)
     out = []
-    for b in range(grid):
+    for b in range(8 * per_run):
         xcd, in_xcd = b % 8, b // 8
-        role, slot = 0, in_xcd
-        if split:
-            role, slot = (2, in_xcd) if in_xcd < per_xcd else (1, in_xcd - per_xcd)
-        lin = xcd * per_xcd + slot
-        if slot < per_xcd and lin < ntiles:
+        role = 0 if not split else (2 if xcd < 4 else 1)
+        lin = (xcd % 4 if split else xcd) * per_run + in_xcd
+        if in_xcd < per_run and lin < ntiles:
             out.append((b, lin, role))
     return out
+
+
+def dw_tile(lin, tiles_m, tiles_n, split):
+    """weight_grad_kernel's tile of run position lin: groups of 8 row tiles
+    (whole), or across the grid's shorter side first (split)."""
+    if not split:
+        lm, ln = group_order(np.array([lin]), tiles_m, tiles_n)
+        return int(lm[0]), int(ln[0])
+    return (lin // tiles_n, lin % tiles_n) if tiles_n <= tiles_m else (lin % tiles_m, lin // tiles_m)
+
+
+def dw_l2_fill_bytes(T, R, C, bm, bn, split):
+    """Bytes of dY and X that the XCDs' L2s fetch, each XCD its tiles' operand
+    strips once over its token range (the model behind the split's tile map)."""
+    tiles_m, tiles_n = cdiv(R, bm), cdiv(C, bn)
+    rows, cols = [set() for _ in range(8)], [set() for _ in range(8)]
+    for b, lin, _ in dw_roles(tiles_m, tiles_n, split):
+        a, c = dw_tile(lin, tiles_m, tiles_n, split)
+        rows[b % 8].add(a)
+        cols[b % 8].add(c)
+    tokens = T // 2 if split else T
+    return sum((len(r) * bm + len(c) * bn) * tokens * 2 for r, c in zip(rows, cols))
 
 
 def check_weight_grad(T, R, C):
     BM, BN, WM, WN, split = dw_shape(T, R, C)
     tiles_m, tiles_n = cdiv(R, BM), cdiv(C, BN)
-    tm, tn = check_tile_map(tiles_m, tiles_n)
+    if not split:
+        check_tile_map(tiles_m, tiles_n)
     roles = dw_roles(tiles_m, tiles_n, split)
-    # every tile once (whole), or once as producer and once as consumer, with
-    # the producer on the same XCD and a lower workgroup id
+    # every tile once (whole), or once as producer (XCDs 0-3) and once as
+    # consumer (XCDs 4-7), the producer with the lower workgroup id
     per_tile = {}
     for b, lin, role in roles:
         per_tile.setdefault(lin, []).append((role, b))
@@ -330,7 +350,7 @@ def check_weight_grad(T, R, C):
     for lin, rs in per_tile.items():
         if split:
             (r1, b1), (r2, b2) = sorted(rs)
-            assert (r1, r2) == (1, 2) and b2 < b1 and b1 % 8 == b2 % 8
+            assert (r1, r2) == (1, 2) and b2 < b1 and b2 % 8 < 4 and b1 % 8 == b2 % 8 + 4
         else:
             assert [r for r, _ in rs] == [0]
     waves = (BM // WM) * (BN // WN)
@@ -350,9 +370,10 @@ def check_weight_grad(T, R, C):
     assert (quad == 1).all(), "the weight-gradient epilogue does not cover its tile once"
     cover = np.zeros((R // 4, C), np.int8)
     nk_all = cdiv(T, 32)
-    lm, ln = group_order(np.arange(tiles_m * tiles_n), tiles_m, tiles_n)   # the kernel's lin -> tile
+    tiles_seen = np.zeros((tiles_m, tiles_n), np.int64)
     for lin in range(tiles_m * tiles_n):
-        a, b = int(lm[lin]), int(ln[lin])
+        a, b = dw_tile(lin, tiles_m, tiles_n, split)   # the kernel's lin -> tile
+        tiles_seen[a, b] += 1
         m0, n0 = a * BM, b * BN
         r4, c = m0 + rel_r, n0 + rel_c
         ok = (r4 < R) & (c < C)
@@ -372,7 +393,7 @@ def check_weight_grad(T, R, C):
             for base, rng, total in (((t0 * R + m0) * 2, ((T - t0) * R - m0) * 2, T * R * 2),
                                      ((t0 * C + n0) * 2, ((T - t0) * C - n0) * 2, T * C * 2)):
                 assert base + rng == total and 0 < rng < U32
-    assert (cover == 1).all()
+    assert (cover == 1).all() and (tiles_seen == 1).all()
     if split:
         assert tiles_m * tiles_n <= DW_FLAG_TILES
 
@@ -552,6 +573,19 @@ def test_weight_grad_splits_the_gpt2_1p5b_weights():
     assert dw_shape(32, 6400, 1600)[4] is False   # one stage of tokens: nothing to split
     assert dw_shape(16384, 1600, 3200)[4] is False   # ragged 256 x 320 tiles: not split
     assert dw_shape(16384, 4096, 5120) == (256, 320, 128, 160, False)   # one full round unsplit
+
+
+@pytest.mark.parametrize("R,C,bm,bn,bound", [(6400, 1600, 256, 320, 1.75), (1600, 6400, 320, 256, 1.75),
+                                              (3072, 2560, 256, 320, 2.4)])
+def test_weight_grad_split_fetches_less(R, C, bm, bn, bound):
+    """The split's XCD pairs fetch fewer operand bytes than the same tiles run
+    whole on 8 XCDs (and than the split's earlier same-XCD pairing, which had
+    each XCD fetch the strips of the whole-tile runs over all the tokens)."""
+    T = 16384
+    split = dw_l2_fill_bytes(T, R, C, bm, bn, True)
+    whole = dw_l2_fill_bytes(T, R, C, bm, bn, False)
+    assert split < 0.7 * whole
+    assert split < bound * (R + C) * T * 2   # the operands themselves, (R + C) T fp16
 
 
 @pytest.mark.parametrize("shapes", [[(64, 64)], [(4096, 4096)], [(6400, 1600), (1600, 6400)],
