@@ -448,11 +448,12 @@ def main():
     fl_us = e0.elapsed_time(e1) * 1e3 / fl_calls
     fl_bytes = 2 * F1["idx"].numel()
 
-    def timed_ms(fn, reps):
+    def timed_ms(fn, reps, warm=1):
         """Average ms per call over `reps` back-to-back calls between two events.
-        One untimed call goes first, so the GPU is busy while the timed calls
+        `warm` untimed calls go first, so the GPU is busy while the timed calls
         are enqueued and host launch latency stays outside the events."""
-        fn()
+        for _ in range(warm):
+            fn()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
         for _ in range(reps):
@@ -492,11 +493,18 @@ def main():
     del Um, mv_out
 
     # next row: the weight gradients of both linears with the masked decay
-    # term (dense fp16 MFMA, fp32 out), timed back to back after the step
+    # term (dense fp16 MFMA, fp32 out), timed back to back after the step.
+    # After the memory-bound kernels above, the first 20 ms or so of these
+    # launches run slower (a dW launch fell from about 410 to 345 us over
+    # them), so 40 untimed calls (about 15 ms) of both go first
     dW1 = torch.empty(f, d, dtype=torch.float32, device=dev)
     dW2 = torch.empty(d, f, dtype=torch.float32, device=dev)
-    wg_ms = np.array([timed_ms(lambda: sp24.sp24_weight_grad(dY1, X, W1s[-1], F1["idx"], DECAY, dW=dW1), 5),
-                      timed_ms(lambda: sp24.sp24_weight_grad(dY2, H, W2s[-1], F2["idx"], DECAY, dW=dW2), 5)])
+    wg_calls = [lambda: sp24.sp24_weight_grad(dY1, X, W1s[-1], F1["idx"], DECAY, dW=dW1),
+                lambda: sp24.sp24_weight_grad(dY2, H, W2s[-1], F2["idx"], DECAY, dW=dW2)]
+    for _ in range(20):
+        for fn in wg_calls:
+            fn()
+    wg_ms = np.array([timed_ms(fn, 20) for fn in wg_calls])
     wg_flops = 2 * T * f * d
     wg_tflops = [wg_flops / (ms * 1e-3) / 1e12 for ms in wg_ms]
     wg_achieved = wg_flops / (float(np.mean(wg_ms)) * 1e-3) / 1e12
