@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <cstdint>
+#include <utility>
 
 #include "sp24_device.hpp"
 #include "sp24_internal.hpp"
@@ -80,8 +81,66 @@ __device__ __forceinline__ bool exact_regime(const BlockMag& b, int& em_inout) {
   return emax < 31 && emax - emin <= 10;
 }
 
+// Tie-break offsets of the keys, moved between the two halves of a class.
+// A top key carries 122 - top_base and a bottom key 5 - bot_rank, whose sum
+// over a class's top and bottom is 127 - index.  Taking K_c from every top
+// constant of class c and giving it to every bottom constant of that class
+// leaves each sum unchanged, and brings the constants into 0..64: operands
+// that a three-input add takes inline, where larger ones cost a second
+// instruction.  None is negative, so a key of a zero score cannot wrap.
+struct KeyOffsets {
+  uint32_t top[36], bot[36];
+};
+constexpr KeyOffsets build_key_offsets() {
+  KeyOffsets o{};
+  int shift[kNumClasses] = {};
+  for (int c = 0; c < kNumClasses; ++c) {
+    int lo = 1 << 20, hi = -1;
+    for (int p = 0; p < 36; ++p)
+      if (kTables.pair_class[p] == c) {
+        const int ct = 122 - kTables.top_base[p];
+        lo = ct < lo ? ct : lo;
+        hi = ct > hi ? ct : hi;
+      }
+    int k = hi - 64 > 0 ? hi - 64 : 0;   // every top constant at most 64 ...
+    k = k < lo ? k : lo;                  // ... unless that needs one below 0
+    shift[c] = k < 59 ? k : 59;           // bottom constants (at most 5 + k) at most 64
+  }
+  for (int p = 0; p < 36; ++p) {
+    o.top[p] = (uint32_t)(122 - kTables.top_base[p] - shift[kTables.pair_class[p]]);
+    o.bot[p] = (uint32_t)(5 - kTables.bot_rank[p] + shift[kTables.bot_class[p]]);
+  }
+  return o;
+}
+constexpr KeyOffsets kKeyOff = build_key_offsets();
+constexpr bool key_offsets_ok() {
+  bool ok = true;
+  for (int p = 0; p < 36; ++p) ok = ok && (int)kKeyOff.top[p] >= 0 && kKeyOff.top[p] < 128 && kKeyOff.bot[p] <= 64;
+  // every pattern's two offsets still sum to 127 - index
+  for (int i = 0; i < kNumPatterns; ++i) {
+    const int tp = 6 * kTables.code[i][0] + kTables.code[i][1];
+    const int bp = 6 * kTables.code[i][2] + kTables.code[i][3];
+    ok = ok && kKeyOff.top[tp] + kKeyOff.bot[bp] == (uint32_t)(127 - i);
+  }
+  return ok;
+}
+static_assert(key_offsets_ok(), "key offsets");
+
+// a + b + C as one instruction when C is an inline constant (0..64); the
+// compiler would share a + C between keys that have the same C, at three
+// instructions for two keys
+template <uint32_t C>
+__device__ __forceinline__ uint32_t add3_const(uint32_t a, uint32_t b) {
+  if constexpr (C <= 64) {
+    uint32_t r;
+    asm("v_add3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "n"(C));
+    return r;
+  } else {
+    return a + b + C;
+  }
+}
+
 __device__ __forceinline__ int search_fast(const BlockMag& b, int emin) {
-  constexpr const PatternTables& T = kTables;
   // scale 2^(25 - emin): entries become integers below 2^21.  fma(x, s, 2^23)
   // is exact and its bit pattern is 0x4B000000 + integer.
   const float scale = __uint_as_float((uint32_t)(25 - emin + 127) << 23);
@@ -95,25 +154,30 @@ __device__ __forceinline__ int search_fast(const BlockMag& b, int emin) {
   }
   // Pair sums shifted left by 7.  The two 0x4B000000 offsets sum to
   // 0x96000000, which vanishes modulo 2^32 after the shift.
+  // The shift is opaque to the compiler: knowing the low 7 bits zero, it
+  // turns the key offset additions below into ORs, which a three-input add
+  // cannot absorb.
   uint32_t P[4][6];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int k = 0; k < 6; ++k) P[r][k] = (q[r][kPairLo[k]] + q[r][kPairHi[k]]) << 7;
+    for (int k = 0; k < 6; ++k)
+      asm("v_add_lshl_u32 %0, %1, %2, 7" : "=v"(P[r][k]) : "v"(q[r][kPairLo[k]]), "v"(q[r][kPairHi[k]]));
   // best top and bottom key per deficit class
   uint32_t top[kNumClasses], bot[kNumClasses];
   bool top_set[kNumClasses] = {}, bot_set[kNumClasses] = {};
-#pragma unroll
-  for (int p = 0; p < 36; ++p) {
-    const int x = p / 6, y = p % 6;
-    const uint32_t tk = P[0][x] + P[1][y] + (uint32_t)(122 - T.top_base[p]);
-    const uint32_t bk = P[2][x] + P[3][y] + (uint32_t)(5 - T.bot_rank[p]);
-    const int tc = T.pair_class[p], bc = T.bot_class[p];
-    top[tc] = top_set[tc] ? max(top[tc], tk) : tk;
-    top_set[tc] = true;
-    bot[bc] = bot_set[bc] ? max(bot[bc], bk) : bk;
-    bot_set[bc] = true;
-  }
+  [&]<int... ps>(std::integer_sequence<int, ps...>) {
+    ([&] {
+      constexpr int p = ps, x = p / 6, y = p % 6;
+      const uint32_t tk = add3_const<kKeyOff.top[p]>(P[0][x], P[1][y]);
+      const uint32_t bk = add3_const<kKeyOff.bot[p]>(P[2][x], P[3][y]);
+      constexpr int tc = kTables.pair_class[p], bc = kTables.bot_class[p];
+      top[tc] = top_set[tc] ? max(top[tc], tk) : tk;
+      top_set[tc] = true;
+      bot[bc] = bot_set[bc] ? max(bot[bc], bk) : bk;
+      bot_set[bc] = true;
+    }(), ...);
+  }(std::make_integer_sequence<int, 36>{});
   uint32_t best = top[0] + bot[0];
 #pragma unroll
   for (int k = 1; k < kNumClasses; ++k) best = max(best, top[k] + bot[k]);
