@@ -51,6 +51,7 @@ class SparseGegluFFN:
         self.W1, self.W2, self.decay = W1, W2, float(decay)
         self.forms = None
         self.flips = torch.zeros(2, dtype=torch.int64, device=W1.device)
+        self._side = None
 
     def refresh(self) -> None:
         if self.forms is None:
@@ -73,11 +74,22 @@ class SparseGegluFFN:
         return Y, Saved(X, U, Hg)
 
     def backward(self, dY: torch.Tensor, saved: Saved):
+        """dW2 runs on a second stream beside dHg, the GEGLU backward and dX,
+        which do not need it: its last round of tiles leaves most CUs to
+        them.  The caller's stream waits for it before this returns, and
+        every output is allocated on the caller's stream."""
         f1, f2 = self._current_forms()
         two_h, d = self.W1.shape
+        main = torch.cuda.current_stream()
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=main.device)
+        side = self._side
+        dW2 = torch.empty(d, two_h // 2, dtype=torch.float32, device=dY.device)
         dHg = sp24.sp24_spmm_bwd_input(dY, f2["vals_col"], f2["meta_col"], d, two_h // 2)
-        dW2 = sp24.sp24_weight_grad(dY, saved.Hg, self.W2, f2["idx"], self.decay)
+        side.wait_stream(main)
+        sp24.sp24_weight_grad(dY, saved.Hg, self.W2, f2["idx"], self.decay, dW=dW2, stream=side)
         dU = sp24.sp24_geglu_bwd(saved.U, dHg, GROUP)
         dX = sp24.sp24_spmm_bwd_input(dU, f1["vals_col"], f1["meta_col"], two_h, d)
         dW1 = sp24.sp24_weight_grad(dU, saved.X, self.W1, f1["idx"], self.decay)
+        main.wait_stream(side)
         return dX, dW1, dW2
