@@ -42,10 +42,10 @@
 // never wait; they run on XCDs 0-3 and the consumers on XCDs 4-7 (workgroup
 // id modulo 8), so a waiting consumer never holds a CU its producer needs,
 // and the wait always ends.  Were all workgroups to reach a single queue, a
-// producer's id is still the lower (by 4), and workgroups start in id order.  An XCD then computes twice the
-// tiles over half the tokens, whose operand strips are fewer bytes than those
-// of half the tiles over all of them.  The consumer's wait is bounded all the
-// same (about 0.1 s).
+// producer's id is still the lower (by 4), and workgroups start in id order.
+// An XCD then computes twice the tiles over half the tokens, whose operand
+// strips are fewer bytes than those of half the tiles over all of them.  The
+// consumer's wait is bounded all the same (about 0.1 s).
 #include <hip/hip_runtime.h>
 #include <atomic>
 #include <cstdint>

@@ -12,7 +12,7 @@
 // maximum in pattern order wins.  Two code paths compute exactly that:
 //
 //  * search_fast, for blocks whose sums are all exact in fp32.  With e the
-//    fp16 exponent field, a block is exact when emax - max(em_innonzero, 1)
+//    fp16 exponent field, a block is exact when emax - max(emin_nonzero, 1)
 //    <= 10: every entry is then an integer multiple of q = 2^(emin-25) below
 //    2^21 q, so every sum of up to 8 entries is an integer multiple of q below
 //    2^24 q and is exact in fp32 whatever the order of additions.  The sums are
